@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN decode hot path on one MI355X.
+
+One step = one gdn_decode_layer call (conv update, gates, delta-rule state update and
+readout, gated RMSNorm) over the whole batch, inputs resident in HBM. The workload is
+the Qwen3.5-style layer (H_k = 16, H_v = 32, d_k = d_v = 128, K = 4, bf16 activations,
+fp32 state) at B = 512: its 1 GiB of state exceeds the 256 MB Infinity Cache, so the
+bandwidth figure is a cold-HBM one. 32 distinct steps of inputs are drawn and reused
+cyclically; the state keeps evolving. B = 1 and B = 64 are reported in "sweep", the
+B = 8 x T = 4096 multi-token call in "sequence".
+
+Prints one JSON line. `value` = sequences x steps / second (seq-layer steps/s).
+The roofline figure uses algorithmic bytes (state read once and written once, every
+input read once, output written once) over the kernel's average duration, timed
+with HIP events on the stream the kernel is launched on.
+
+    python bench.py [--steps K] [--warmup W]
+    python bench.py --copy-calibration     # plain copy of known size (PMC scaling)
+    python bench.py --summarize DIR        # summarise rocprofv3 CSV output in DIR
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN decode steps/s (seq·layer) at B=1/64/512 + achieved HBM GB/s vs peak"
+UNIT = "seq·layer steps/s"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_linear_causal_amd", "csrc", "gdn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdn_decode_B512_traffic.json")
+
+
+def algorithmic_bytes(cfg, T=1) -> int:
+    """Bytes one call must move: per sequence the fp32 state read and written once,
+    the conv state read and rolled, qkv / z / a / b of each token read, the output
+    written (fp32); plus the shared conv taps, A_log, dt_bias and norm weight."""
+    ea = 2 if cfg.act_dtype == "bf16" else 4
+    Hv, dk, dv, K, C = cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim, cfg.conv_kernel, cfg.channels
+    per_seq = 2 * Hv * dk * dv * 4 + 2 * (K - 1) * C * ea
+    per_tok = C * ea + Hv * dv * ea + 2 * Hv * ea + Hv * dv * 4
+    shared = C * K * ea + 2 * Hv * 4 + dv * 4
+    return cfg.batch * (per_seq + T * per_tok) + shared
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from committed PMC counters, only if they were taken on
+    the current kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def build_inputs(cfg, steps, torch):
+    import numpy as np
+    from gated_deltanet_linear_causal_amd import inputs as I
+    data = I.generate(cfg, steps=steps)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    d = {k: dev(v) for k, v in data.items()}
+    return data, d
+
+
+def time_decode(cfg, d, steps, warmup, torch, gdn):
+    """Average seconds per gdn_decode_layer launch over `steps` timed launches."""
+    s = gdn.make_shape(cfg.batch, cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim,
+                       cfg.conv_kernel, cfg.l2_eps, cfg.rms_eps, cfg.act_dtype, "f32")
+    nin = d["qkv"].shape[0]
+    out = torch.empty((cfg.batch, cfg.z_dim), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        j = i % nin
+        gdn.gdn_decode_layer(s, d["conv_state"], d["state"], d["qkv"][j], d["conv_w"], d["a"][j], d["b"][j],
+                             d["z"][j], d["A_log"], d["dt_bias"], d["norm_w"], out, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / steps
+
+
+def time_sequence(cfg, d, reps, torch, gdn):
+    s = gdn.make_shape(cfg.batch, cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim,
+                       cfg.conv_kernel, cfg.l2_eps, cfg.rms_eps, cfg.act_dtype, "f32")
+    out = torch.empty((cfg.batch, cfg.steps, cfg.z_dim), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ws_bytes = gdn.gdn_sequence_workspace_bytes(s, cfg.steps)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+
+    def run():
+        gdn.gdn_sequence(s, cfg.steps, d["conv_state"], d["state"], d["qkv"], d["conv_w"], d["a"], d["b"], d["z"],
+                         d["A_log"], d["dt_bias"], d["norm_w"], out, workspace=ws, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def cpu_baseline(cfg, data, target_s=15.0):
+    """The fp64 oracle, as it is, on a bounded sample of the same workload: the first
+    n sequences over the 32 drawn steps, n doubled until the run takes >= ~target_s/4."""
+    import numpy as np
+    from gated_deltanet_linear_causal_amd import inputs as I
+    from oracle import oracle as O
+    threads = O.threads(0)
+    S = data["qkv"].shape[0]
+    n = 8
+    while True:
+        idx = np.arange(min(n, cfg.batch))
+        s = O.shape_of(cfg, batch=len(idx))
+        cs = I.widen(data["conv_state"][idx], cfg.act_dtype).astype(np.float64)
+        st = data["state"][idx].astype(np.float64)
+        sw = lambda k: np.ascontiguousarray(np.swapaxes(I.widen(data[k][:, idx], cfg.act_dtype), 0, 1))
+        args = (sw("qkv"), I.widen(data["conv_w"], cfg.act_dtype), sw("a"), sw("b"), sw("z"))
+        t0 = time.perf_counter()
+        O.sequence(s, S, cs, st, args[0], args[1], args[2], args[3], args[4], data["A_log"], data["dt_bias"],
+                   data["norm_w"])
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or len(idx) >= cfg.batch:
+            break
+        n = min(cfg.batch, int(n * max(2.0, min(8.0, target_s / 4 / max(dt, 1e-3)))))
+    return {"value": len(idx) * S / dt, "unit": UNIT, "cores": threads, "kind": "oracle",
+            "sample": "first %d of the %d sequences x %d decode steps of the same inputs, fp64 C oracle "
+                      "(OpenMP over sequence x k-head units), %.1f s" % (len(idx), cfg.batch, S, dt)}
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=3):
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
+                      "reps": reps}))
+
+
+def summarize(path):
+    """Per-kernel summary of rocprofv3 CSV output found under `path`."""
+    stats = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+    for f in stats:
+        print("==", os.path.relpath(f, path))
+        for row in csv.DictReader(open(f)):
+            print("%-70.70s calls %6s  avg %10.1f us  min %10.1f us  max %10.1f us  %5.1f%%" % (
+                row["Name"], row["Calls"], float(row["AverageNs"]) / 1e3, float(row["MinNs"]) / 1e3,
+                float(row["MaxNs"]) / 1e3, float(row["Percentage"])))
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        print("==", os.path.relpath(f, path))
+        acc = {}
+        for row in csv.DictReader(open(f)):
+            key = (row.get("Kernel_Name", row.get("Kernel-Name", "?"))[:70], row["Counter_Name"])
+            acc.setdefault(key, []).append(float(row["Counter_Value"]))
+        for (k, c), v in sorted(acc.items()):
+            print("%-70.70s %-12s dispatches %5d  mean %14.1f" % (k, c, len(v), sum(v) / len(v)))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the B=1 / B=64 / sequence figures")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize)
+        return 0
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the GDN core shards "
+              "by sequence and k-head with no exchange; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from gated_deltanet_linear_causal_amd import gdn
+    from gated_deltanet_linear_causal_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    gdn.library()  # fail loudly if the HIP library is missing
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return 0
+
+    cfg = I.config(3)  # B = 512
+    data, d = build_inputs(cfg, 32, torch)
+    sec = time_decode(cfg, d, args.steps, args.warmup, torch, gdn)
+    nbytes = algorithmic_bytes(cfg)
+    gbs = nbytes / sec / 1e9
+    value = cfg.batch / sec
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded; recipe in inputs.py)",
+        "config": {"workload": "GDN decode, Qwen3.5-style layer, B=512", "batch": cfg.batch,
+                   "num_k_heads": cfg.num_k_heads, "num_v_heads": cfg.num_v_heads, "head_k_dim": cfg.head_k_dim,
+                   "head_v_dim": cfg.head_v_dim, "conv_kernel": cfg.conv_kernel,
+                   "activations": "bf16", "state": "fp32", "output": "fp32", "distinct_step_inputs": 32},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
+                     "kernel": "gdn_step_fast<128, 2, fused, bf16, K=4>", "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(sec * 1e6, 2)},
+    }
+    del d
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        sweep = {}
+        for i in (1, 2):
+            c = I.config(i)
+            _, dd = build_inputs(c, 32, torch)
+            ssec = time_decode(c, dd, max(args.steps, 200), args.warmup, torch, gdn)
+            b = algorithmic_bytes(c)
+            sweep["B%d" % c.batch] = {"steps_per_s": round(c.batch / ssec, 1), "us_per_step": round(ssec * 1e6, 2),
+                                      "GB_s": round(b / ssec / 1e9, 1), "frac": round(b / ssec / 1e9 / HBM_PEAK_GBS, 4)}
+            del dd
+        result["sweep"] = sweep
+        c = I.config(4)
+        _, dd = build_inputs(c, c.steps, torch)
+        ssec = time_sequence(c, dd, 2, torch, gdn)
+        b = algorithmic_bytes(c, T=c.steps)
+        result["sequence"] = {"workload": "B=8 x T=4096 gdn_sequence", "ms": round(ssec * 1e3, 3),
+                              "tokens_per_s": round(c.batch * c.steps / ssec, 1),
+                              "GB_s": round(b / ssec / 1e9, 1), "hbm_frac": round(b / ssec / 1e9 / HBM_PEAK_GBS, 4)}
+        del dd
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, data)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,295 @@
+// Host side of libgdn.so: argument validation and kernel dispatch for the entry
+// points declared in include/gdn.h. Every check runs before anything is enqueued, so
+// an error return leaves every buffer untouched. No memory is allocated here.
+
+#include "gdn.h"
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "gdn_internal.h"
+
+namespace {
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+  bool written;
+  size_t align;
+};
+
+size_t elt(int32_t dtype) { return dtype == GDN_BF16 ? 2 : 4; }
+
+bool valid_dtype(int32_t d) { return d == GDN_F32 || d == GDN_BF16; }
+
+// Shape checks shared by all entry points. `need_heads` is false only for queries.
+gdn_status_t check_shape(const gdn_shape_t* s) {
+  if (!s) return GDN_ERR_NULL;
+  if (s->batch < 0 || s->num_k_heads < 1 || s->num_v_heads < 1 || s->head_k_dim < 1 || s->head_v_dim < 1)
+    return GDN_ERR_SHAPE;
+  if (s->num_v_heads % s->num_k_heads != 0) return GDN_ERR_SHAPE;
+  if (s->conv_kernel < 2 || s->conv_kernel > gdn::kMaxConvTaps) return GDN_ERR_SHAPE;
+  if (!(std::isfinite(s->l2_eps) && s->l2_eps >= 0.0f) || !(std::isfinite(s->rms_eps) && s->rms_eps >= 0.0f))
+    return GDN_ERR_SHAPE;
+  if (!valid_dtype(s->act_dtype) || !valid_dtype(s->out_dtype)) return GDN_ERR_DTYPE;
+  // grid = B * H_k workgroups; channel and state offsets are computed in 64 bits
+  if (static_cast<int64_t>(s->batch) * s->num_k_heads > std::numeric_limits<int32_t>::max()) return GDN_ERR_SHAPE;
+  const int64_t C = 2LL * s->num_k_heads * s->head_k_dim + static_cast<int64_t>(s->num_v_heads) * s->head_v_dim;
+  if (C > std::numeric_limits<int32_t>::max()) return GDN_ERR_SHAPE;
+  if (s->head_k_dim != s->head_v_dim) return GDN_ERR_UNSUPPORTED;
+  const int d = s->head_k_dim;
+  if (d != 32 && d != 64 && d != 128) return GDN_ERR_UNSUPPORTED;
+  if (s->num_v_heads / s->num_k_heads > 64) return GDN_ERR_UNSUPPORTED;  // LDS holds G*d values
+  return GDN_OK;
+}
+
+int heads_per_pass(const gdn_shape_t* s) { return (s->num_v_heads / s->num_k_heads) % 2 == 0 ? 2 : 1; }
+
+// Null, alignment and overlap checks. Buffers with bytes == 0 are skipped.
+gdn_status_t check_buffers(const Buf* bufs, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (bufs[i].bytes == 0) continue;
+    if (!bufs[i].p) return GDN_ERR_NULL;
+  }
+  for (int i = 0; i < n; ++i) {
+    if (bufs[i].bytes == 0) continue;
+    if (reinterpret_cast<uintptr_t>(bufs[i].p) % bufs[i].align != 0) return GDN_ERR_ALIGN;
+  }
+  for (int i = 0; i < n; ++i) {
+    if (bufs[i].bytes == 0) continue;
+    for (int j = i + 1; j < n; ++j) {
+      if (bufs[j].bytes == 0) continue;
+      if (!bufs[i].written && !bufs[j].written) continue;  // read-only pairs may share memory
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(bufs[i].p), a1 = a0 + bufs[i].bytes;
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(bufs[j].p), b1 = b0 + bufs[j].bytes;
+      if (a0 < b1 && b0 < a1) return GDN_ERR_ALIAS;
+    }
+  }
+  return GDN_OK;
+}
+
+struct Sizes {
+  size_t B, Hk, Hv, d, K, C, ea, eo;
+  explicit Sizes(const gdn_shape_t* s)
+      : B(s->batch), Hk(s->num_k_heads), Hv(s->num_v_heads), d(s->head_k_dim), K(s->conv_kernel),
+        C(2 * Hk * d + Hv * d), ea(elt(s->act_dtype)), eo(elt(s->out_dtype)) {}
+  size_t conv_state() const { return B * (K - 1) * C * ea; }
+  size_t state() const { return B * Hv * d * d * 4; }
+  size_t conv_w() const { return C * K * ea; }
+};
+
+gdn::KernelArgs base_args(const gdn_shape_t* s) {
+  gdn::KernelArgs a{};
+  a.B = s->batch;
+  a.Hk = s->num_k_heads;
+  a.Hv = s->num_v_heads;
+  a.G = s->num_v_heads / s->num_k_heads;
+  a.K = s->conv_kernel;
+  a.C = 2 * s->num_k_heads * s->head_k_dim + s->num_v_heads * s->head_v_dim;
+  a.T = 1;
+  a.l2_eps = s->l2_eps;
+  a.rms_eps = s->rms_eps;
+  a.act_bf16 = s->act_dtype == GDN_BF16;
+  a.out_bf16 = s->out_dtype == GDN_BF16;
+  return a;
+}
+
+gdn_status_t launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdn_abi_version(void) { return (1 << 16) | 0; }
+
+const char* gdn_status_string(int32_t st) {
+  switch (st) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "invalid shape or size";
+    case GDN_ERR_DTYPE: return "invalid dtype";
+    case GDN_ERR_ALIGN: return "misaligned buffer";
+    case GDN_ERR_ALIAS: return "a written buffer overlaps another buffer";
+    case GDN_ERR_WORKSPACE: return "workspace too small";
+    case GDN_ERR_UNSUPPORTED: return "shape has no compiled kernel (supported: d_k == d_v in {32, 64, 128})";
+    case GDN_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+gdn_status_t gdn_conv_update(const gdn_shape_t* shape, void* conv1d_state, const void* qkv,
+                             const void* conv1d_weight, float* qkv_act, void* stream) {
+  gdn_status_t st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  const Sizes z(shape);
+  if (z.B == 0) return GDN_OK;
+  const Buf bufs[] = {
+      {conv1d_state, z.conv_state(), true, 16},
+      {qkv, z.B * z.C * z.ea, false, 16},
+      {conv1d_weight, z.conv_w(), false, 16},
+      {qkv_act, z.B * z.C * 4, true, 16},
+  };
+  if ((st = check_buffers(bufs, 4)) != GDN_OK) return st;
+  gdn::KernelArgs a = base_args(shape);
+  a.conv_state = conv1d_state;
+  a.qkv = qkv;
+  a.qkv_bs = static_cast<long>(z.C);
+  a.conv_w = conv1d_weight;
+  a.qkv_act_out = qkv_act;
+  (void)hipGetLastError();
+  return launched(gdn::launch_step(gdn::kModeConv, shape->head_k_dim, heads_per_pass(shape), a,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_recurrent_step(const gdn_shape_t* shape, float* state, const float* qkv_act,
+                                const void* dt_raw, const void* b_raw, const float* A_log,
+                                const float* dt_bias, void* y, void* stream) {
+  gdn_status_t st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  const Sizes z(shape);
+  if (z.B == 0) return GDN_OK;
+  const Buf bufs[] = {
+      {state, z.state(), true, 16},
+      {qkv_act, z.B * z.C * 4, false, 16},
+      {dt_raw, z.B * z.Hv * z.ea, false, z.ea},
+      {b_raw, z.B * z.Hv * z.ea, false, z.ea},
+      {A_log, z.Hv * 4, false, 4},
+      {dt_bias, z.Hv * 4, false, 4},
+      {y, z.B * z.Hv * z.d * z.eo, true, 16},
+  };
+  if ((st = check_buffers(bufs, 7)) != GDN_OK) return st;
+  gdn::KernelArgs a = base_args(shape);
+  a.state = state;
+  a.qkv_act_in = qkv_act;
+  a.dt_raw = dt_raw;
+  a.b_raw = b_raw;
+  a.ab_bs = static_cast<long>(z.Hv);
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.out = y;
+  a.out_bs = static_cast<long>(z.Hv * z.d);
+  (void)hipGetLastError();
+  return launched(gdn::launch_step(gdn::kModeRec, shape->head_k_dim, heads_per_pass(shape), a,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_decode_layer(const gdn_shape_t* shape, void* conv1d_state, float* state,
+                              const void* qkv, const void* conv1d_weight, const void* dt_raw,
+                              const void* b_raw, const void* z_in, const float* A_log,
+                              const float* dt_bias, const float* norm_weight, void* out,
+                              void* stream) {
+  gdn_status_t st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  const Sizes z(shape);
+  if (z.B == 0) return GDN_OK;
+  const Buf bufs[] = {
+      {conv1d_state, z.conv_state(), true, 16},
+      {state, z.state(), true, 16},
+      {qkv, z.B * z.C * z.ea, false, 16},
+      {conv1d_weight, z.conv_w(), false, 16},
+      {dt_raw, z.B * z.Hv * z.ea, false, z.ea},
+      {b_raw, z.B * z.Hv * z.ea, false, z.ea},
+      {z_in, z.B * z.Hv * z.d * z.ea, false, 16},
+      {A_log, z.Hv * 4, false, 4},
+      {dt_bias, z.Hv * 4, false, 4},
+      {norm_weight, z.d * 4, false, 16},
+      {out, z.B * z.Hv * z.d * z.eo, true, 16},
+  };
+  if ((st = check_buffers(bufs, 11)) != GDN_OK) return st;
+  gdn::KernelArgs a = base_args(shape);
+  a.conv_state = conv1d_state;
+  a.state = state;
+  a.qkv = qkv;
+  a.qkv_bs = static_cast<long>(z.C);
+  a.conv_w = conv1d_weight;
+  a.dt_raw = dt_raw;
+  a.b_raw = b_raw;
+  a.ab_bs = static_cast<long>(z.Hv);
+  a.z = z_in;
+  a.z_bs = static_cast<long>(z.Hv * z.d);
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.norm_w = norm_weight;
+  a.out = out;
+  a.out_bs = static_cast<long>(z.Hv * z.d);
+  (void)hipGetLastError();
+  return launched(gdn::launch_step(gdn::kModeFused, shape->head_k_dim, heads_per_pass(shape), a,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_sequence_workspace_bytes(const gdn_shape_t* shape, int32_t T) {
+  if (check_shape(shape) != GDN_OK || T < 0) return SIZE_MAX;
+  return 0;
+}
+
+gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_state, float* state,
+                          const void* qkv, const void* conv1d_weight, const void* dt_raw,
+                          const void* b_raw, const void* z_in, const float* A_log,
+                          const float* dt_bias, const float* norm_weight, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  gdn_status_t st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (T < 0) return GDN_ERR_SHAPE;
+  const Sizes z(shape);
+  if (z.B == 0 || T == 0) return GDN_OK;
+  const size_t need = gdn_sequence_workspace_bytes(shape, T);
+  if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  const size_t Tz = static_cast<size_t>(T);
+  const Buf bufs[] = {
+      {conv1d_state, z.conv_state(), true, 16},
+      {state, z.state(), true, 16},
+      {qkv, z.B * Tz * z.C * z.ea, false, 16},
+      {conv1d_weight, z.conv_w(), false, 16},
+      {dt_raw, z.B * Tz * z.Hv * z.ea, false, z.ea},
+      {b_raw, z.B * Tz * z.Hv * z.ea, false, z.ea},
+      {z_in, z.B * Tz * z.Hv * z.d * z.ea, false, 16},
+      {A_log, z.Hv * 4, false, 4},
+      {dt_bias, z.Hv * 4, false, 4},
+      {norm_weight, z.d * 4, false, 16},
+      {out, z.B * Tz * z.Hv * z.d * z.eo, true, 16},
+      {workspace, need, true, 256},
+  };
+  if ((st = check_buffers(bufs, 12)) != GDN_OK) return st;
+  gdn::KernelArgs a = base_args(shape);
+  a.T = T;
+  a.conv_state = conv1d_state;
+  a.state = state;
+  a.qkv = qkv;
+  a.qkv_bs = static_cast<long>(Tz * z.C);
+  a.qkv_ts = static_cast<long>(z.C);
+  a.conv_w = conv1d_weight;
+  a.dt_raw = dt_raw;
+  a.b_raw = b_raw;
+  a.ab_bs = static_cast<long>(Tz * z.Hv);
+  a.ab_ts = static_cast<long>(z.Hv);
+  a.z = z_in;
+  a.z_bs = static_cast<long>(Tz * z.Hv * z.d);
+  a.z_ts = static_cast<long>(z.Hv * z.d);
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.norm_w = norm_weight;
+  a.out = out;
+  a.out_bs = static_cast<long>(Tz * z.Hv * z.d);
+  a.out_ts = static_cast<long>(z.Hv * z.d);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = shape->head_k_dim, G = a.G;
+  (void)hipGetLastError();
+  if (G <= 2 && a.K == 4) return launched(gdn::launch_sequence(d, G, a, s));
+  // Shapes whose state or taps do not stay resident: one fused step launch per token.
+  const size_t ea = z.ea, eo = z.eo;
+  for (int32_t t = 0; t < T; ++t) {
+    gdn::KernelArgs at = a;
+    at.T = 1;
+    at.qkv = static_cast<const char*>(qkv) + t * z.C * ea;
+    at.dt_raw = static_cast<const char*>(dt_raw) + t * z.Hv * ea;
+    at.b_raw = static_cast<const char*>(b_raw) + t * z.Hv * ea;
+    at.z = static_cast<const char*>(z_in) + t * z.Hv * z.d * ea;
+    at.out = static_cast<char*>(out) + t * z.Hv * z.d * eo;
+    st = launched(gdn::launch_step(gdn::kModeFused, d, heads_per_pass(shape), at, s));
+    if (st != GDN_OK) return st;
+  }
+  return GDN_OK;
+}
+
+}  // extern "C"

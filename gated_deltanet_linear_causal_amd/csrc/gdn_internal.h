@@ -1,0 +1,48 @@
+// Internal interface between the host side (validation, dispatch) and the HIP
+// kernels of libgdn.so. Not installed; the public ABI is include/gdn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kMaxConvTaps = 8;
+
+// Everything a kernel launch needs. Element strides are in elements of the buffer's
+// own dtype. "bs" = stride between sequences, "ts" = stride between tokens.
+struct KernelArgs {
+  int B, Hk, Hv, G, K, C, T;
+  float l2_eps, rms_eps;
+  int act_bf16, out_bf16;
+  void* conv_state;        // [B][K-1][C] act dtype, in place
+  float* state;            // [B][Hv][D][D] fp32, in place
+  const void* qkv;         // act dtype
+  const void* conv_w;      // [C][K] act dtype
+  const float* qkv_act_in; // [B][C] fp32 (recurrence-only mode)
+  float* qkv_act_out;      // [B][C] fp32 (conv-only mode)
+  const void* dt_raw;      // act dtype
+  const void* b_raw;       // act dtype
+  const void* z;           // act dtype
+  const float* A_log;      // [Hv]
+  const float* dt_bias;    // [Hv]
+  const float* norm_w;     // [D]
+  void* out;               // y (recurrence-only) or gated output, out dtype
+  long qkv_bs, qkv_ts;
+  long ab_bs, ab_ts;
+  long z_bs, z_ts;
+  long out_bs, out_ts;
+};
+
+enum Mode : int { kModeConv = 0, kModeRec = 1, kModeFused = 2 };
+
+// Launchers (gdn_kernels.hip). Return the hipError_t of the launch.
+// d: head dim (d_k == d_v); p: v-heads per pass (1 or 2). Grid = B * Hk workgroups.
+bool step_supported(int d, int p);
+hipError_t launch_step(int mode, int d, int p, const KernelArgs& a, hipStream_t stream);
+// Multi-token kernel that keeps the state on chip for all T tokens; needs G == p
+// and K == 4.
+hipError_t launch_sequence(int d, int p, const KernelArgs& a, hipStream_t stream);
+
+}  // namespace gdn

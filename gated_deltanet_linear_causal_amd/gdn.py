@@ -1,0 +1,194 @@
+"""Python binding of libgdn.so (include/gdn.h), by ctypes.
+
+Argument marshalling only: tensors become device pointers, the current torch stream
+becomes the hipStream_t, and a nonzero status raises GdnError. Every step of the
+computation runs in the library's HIP kernels; there is no other code path, and a
+missing library raises at first use.
+
+Before passing pointers, each tensor is checked to be a contiguous tensor on the GPU
+with the dtype and at least the number of elements the shape implies, so that the
+library never reads or writes past a tensor it was given.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "GDN_F32", "GDN_BF16", "GdnError", "GdnShape", "make_shape", "library", "library_path",
+    "gdn_conv_update", "gdn_recurrent_step", "gdn_decode_layer", "gdn_sequence",
+    "gdn_sequence_workspace_bytes", "gdn_status_string", "gdn_abi_version", "STATUS",
+]
+
+GDN_F32 = 0
+GDN_BF16 = 1
+
+STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE",
+          -4: "GDN_ERR_ALIGN", -5: "GDN_ERR_ALIAS", -6: "GDN_ERR_WORKSPACE",
+          -7: "GDN_ERR_UNSUPPORTED", -8: "GDN_ERR_HIP"}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libgdn.so")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (where, STATUS.get(status, status), gdn_status_string(status)))
+
+
+class GdnShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_k_heads", ctypes.c_int32),
+                ("num_v_heads", ctypes.c_int32), ("head_k_dim", ctypes.c_int32),
+                ("head_v_dim", ctypes.c_int32), ("conv_kernel", ctypes.c_int32),
+                ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("act_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+    @property
+    def channels(self) -> int:
+        return 2 * self.num_k_heads * self.head_k_dim + self.num_v_heads * self.head_v_dim
+
+
+def make_shape(batch, num_k_heads, num_v_heads, head_k_dim, head_v_dim, conv_kernel=4,
+               l2_eps=1e-6, rms_eps=1e-6, act_dtype="bf16", out_dtype="f32") -> GdnShape:
+    code = {"f32": GDN_F32, "bf16": GDN_BF16, GDN_F32: GDN_F32, GDN_BF16: GDN_BF16}
+    return GdnShape(int(batch), int(num_k_heads), int(num_v_heads), int(head_k_dim), int(head_v_dim),
+                    int(conv_kernel), float(l2_eps), float(rms_eps),
+                    code.get(act_dtype, act_dtype), code.get(out_dtype, out_dtype))
+
+
+_lib = None
+
+
+def library():
+    """The loaded libgdn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError("libgdn.so is not built (%s); run "
+                               "`python -m gated_deltanet_linear_causal_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        P, S, I32 = ctypes.c_void_p, ctypes.POINTER(GdnShape), ctypes.c_int32
+        lib.gdn_conv_update.argtypes = [S, P, P, P, P, P]
+        lib.gdn_recurrent_step.argtypes = [S, P, P, P, P, P, P, P, P]
+        lib.gdn_decode_layer.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.gdn_sequence.argtypes = [S, I32] + [P] * 12 + [ctypes.c_size_t, P]
+        for f in (lib.gdn_conv_update, lib.gdn_recurrent_step, lib.gdn_decode_layer, lib.gdn_sequence):
+            f.restype = I32
+        lib.gdn_sequence_workspace_bytes.argtypes = [S, I32]
+        lib.gdn_sequence_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdn_status_string.argtypes = [I32]
+        lib.gdn_status_string.restype = ctypes.c_char_p
+        lib.gdn_abi_version.argtypes = []
+        lib.gdn_abi_version.restype = I32
+        _lib = lib
+    return _lib
+
+
+def gdn_status_string(status: int) -> str:
+    return library().gdn_status_string(int(status)).decode()
+
+
+def gdn_abi_version() -> int:
+    return library().gdn_abi_version()
+
+
+def gdn_sequence_workspace_bytes(shape: GdnShape, T: int) -> int:
+    return library().gdn_sequence_workspace_bytes(ctypes.byref(shape), int(T))
+
+
+_ACT = {GDN_F32: torch.float32, GDN_BF16: torch.bfloat16}
+
+
+def _p(t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] = None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s has %d elements, the shape needs %d" % (name, t.numel(), numel))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _done(st: int, where: str, check: bool) -> int:
+    if check and st != 0:
+        raise GdnError(st, where)
+    return st
+
+
+def gdn_conv_update(shape: GdnShape, conv1d_state, qkv, conv1d_weight, qkv_act, stream=None, check=True) -> int:
+    s = shape
+    act = _ACT.get(s.act_dtype)
+    B, C, K = s.batch, s.channels, s.conv_kernel
+    st = library().gdn_conv_update(
+        ctypes.byref(s), _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C), _p(qkv, "qkv", act, B * C),
+        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(qkv_act, "qkv_act", torch.float32, B * C), _stream(stream))
+    return _done(st, "gdn_conv_update", check)
+
+
+def gdn_recurrent_step(shape: GdnShape, state, qkv_act, dt_raw, b_raw, A_log, dt_bias, y, stream=None,
+                       check=True) -> int:
+    s = shape
+    act, out = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
+    B, C, Hv, dk, dv = s.batch, s.channels, s.num_v_heads, s.head_k_dim, s.head_v_dim
+    st = library().gdn_recurrent_step(
+        ctypes.byref(s), _p(state, "state", torch.float32, B * Hv * dk * dv),
+        _p(qkv_act, "qkv_act", torch.float32, B * C), _p(dt_raw, "dt_raw", act, B * Hv),
+        _p(b_raw, "b_raw", act, B * Hv), _p(A_log, "A_log", torch.float32, Hv),
+        _p(dt_bias, "dt_bias", torch.float32, Hv), _p(y, "y", out, B * Hv * dv), _stream(stream))
+    return _done(st, "gdn_recurrent_step", check)
+
+
+def gdn_decode_layer(shape: GdnShape, conv1d_state, state, qkv, conv1d_weight, dt_raw, b_raw, z, A_log,
+                     dt_bias, norm_weight, out, stream=None, check=True) -> int:
+    s = shape
+    act, od = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
+    B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
+    st = library().gdn_decode_layer(
+        ctypes.byref(s), _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
+        _p(state, "state", torch.float32, B * Hv * dk * dv), _p(qkv, "qkv", act, B * C),
+        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(dt_raw, "dt_raw", act, B * Hv),
+        _p(b_raw, "b_raw", act, B * Hv), _p(z, "z", act, B * Hv * dv), _p(A_log, "A_log", torch.float32, Hv),
+        _p(dt_bias, "dt_bias", torch.float32, Hv), _p(norm_weight, "norm_weight", torch.float32, dv),
+        _p(out, "out", od, B * Hv * dv), _stream(stream))
+    return _done(st, "gdn_decode_layer", check)
+
+
+def gdn_sequence(shape: GdnShape, T: int, conv1d_state, state, qkv, conv1d_weight, dt_raw, b_raw, z, A_log,
+                 dt_bias, norm_weight, out, workspace=None, stream=None, check=True) -> int:
+    s = shape
+    act, od = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
+    B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
+    T = int(T)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().gdn_sequence(
+        ctypes.byref(s), T, _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
+        _p(state, "state", torch.float32, B * Hv * dk * dv), _p(qkv, "qkv", act, B * T * C),
+        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(dt_raw, "dt_raw", act, B * T * Hv),
+        _p(b_raw, "b_raw", act, B * T * Hv), _p(z, "z", act, B * T * Hv * dv),
+        _p(A_log, "A_log", torch.float32, Hv), _p(dt_bias, "dt_bias", torch.float32, Hv),
+        _p(norm_weight, "norm_weight", torch.float32, dv), _p(out, "out", od, B * T * Hv * dv),
+        _p(workspace, "workspace"), ctypes.c_size_t(ws_bytes), _stream(stream))
+    return _done(st, "gdn_sequence", check)

@@ -1,0 +1,148 @@
+/*
+ * gdn.h - C ABI of libgdn.so, the MI355X (gfx950) Gated DeltaNet decode path.
+ *
+ * The operations are the GDN (linear-attention) layer steps of the page
+ * "linear_attention.rs" (spark_model/forward/qwen3_5, forward_linear_attention):
+ *   step 3    fused causal_conv1d_update + SiLU + per-head L2 norm of Q and K
+ *   steps 4-5 gate alpha = exp(softplus(dt + dt_bias) * -exp(A_log)), beta = sigmoid(b)
+ *   step 6    qkv split into Q | K | V
+ *   step 7    gated_delta_rule_decode: per v-head state update and readout
+ *   step 8    per-head RMSNorm of the readout with one norm_weight vector of d_v
+ *   steps 9-11  silu(z) (.) y_norm, the gated input of out_proj (out_proj itself is
+ *             not part of this library)
+ * The delta rule of step 7 is the published gated delta rule (Gated DeltaNet):
+ *   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t / sqrt(d_k).
+ * The conv state is rolled in place, the convention the page "ple.rs" documents for
+ * ple_conv, so one call serves decode (T = 1) and multi-token input (T > 1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: every buffer pointer is a DEVICE pointer (HIP device memory of the current
+ *   device), owned by the caller; the library allocates no memory and keeps no state
+ *   between calls. The shape struct is a HOST pointer, read during the call only.
+ * Stream: `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *   work and return; results are ready when the stream is synchronised.
+ * Layouts (row-major, C order; B = batch, C = 2*H_k*d_k + H_v*d_v channels):
+ *   conv1d_state  [B][K-1][C]   act dtype; row 0 = oldest token; read and rolled in place
+ *   state         [B][H_v][d_k][d_v] fp32, d_v contiguous: H[i][j] with S = H^T, so the
+ *                 readout is o_j = sum_i H[i][j] q_i / sqrt(d_k); updated in place
+ *   qkv           [B][C] act dtype: Q of k-head g at g*d_k, K at H_k*d_k + g*d_k, V of
+ *                 v-head h at 2*H_k*d_k + h*d_v (step 6)
+ *   conv1d_weight [C][K] act dtype: tap K-1 multiplies the current token; no bias
+ *   dt_raw, b_raw [B][H_v] act dtype (one per v-head, steps 4-5)
+ *   z             [B][H_v*d_v] act dtype
+ *   A_log, dt_bias [H_v] fp32; norm_weight [d_v] fp32
+ *   v-head h reads the Q/K of k-head h / G, G = H_v / H_k (consecutive v-heads share).
+ * Validation: every argument is checked on the host before anything is enqueued; on any
+ *   error the call returns a negative gdn_status_t and writes nothing.
+ *   - NULL buffer pointers -> GDN_ERR_NULL (allowed only when batch, or T, is 0)
+ *   - batch < 0, heads < 1, H_v % H_k != 0, K outside [2, 8], eps < 0 or not finite,
+ *     T < 0, grid too large -> GDN_ERR_SHAPE
+ *   - act_dtype / out_dtype not a gdn_dtype_t -> GDN_ERR_DTYPE
+ *   - qkv, conv1d_state, state, conv1d_weight, z, qkv_act, y, out not 16-byte aligned,
+ *     or another buffer not aligned to its element size -> GDN_ERR_ALIGN
+ *   - a buffer the call writes overlaps any other buffer of the call -> GDN_ERR_ALIAS
+ *   - head dims without a compiled kernel (supported: d_k == d_v in {32, 64, 128})
+ *     -> GDN_ERR_UNSUPPORTED
+ *   - the HIP runtime rejects the launch -> GDN_ERR_HIP (kernels may already be queued
+ *     for an earlier part of the call only in gdn_sequence's multi-launch path).
+ *   Faults inside a kernel surface asynchronously at the caller's next synchronisation.
+ * Concurrency: calls on one stream are ordered; two calls that touch the same state
+ *   buffers on different streams race. Within one call every conv-state channel and
+ *   every state element is read and written by exactly one workgroup.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = -1,
+  GDN_ERR_SHAPE = -2,
+  GDN_ERR_DTYPE = -3,
+  GDN_ERR_ALIGN = -4,
+  GDN_ERR_ALIAS = -5,
+  GDN_ERR_WORKSPACE = -6,
+  GDN_ERR_UNSUPPORTED = -7,
+  GDN_ERR_HIP = -8
+} gdn_status_t;
+
+/* Layer shape and precision, named after the config fields of the page
+ * "linear_attention.rs" (k_head_dim_lin, v_head_dim_lin, num_k_heads_lin,
+ * num_v_heads_lin, conv_kernel_size, rms_eps) plus the step-3 l2_eps. */
+typedef struct {
+  int32_t batch;       /* B: independent sequences (>= 0; 0 is a no-op) */
+  int32_t num_k_heads; /* H_k */
+  int32_t num_v_heads; /* H_v, a multiple of H_k */
+  int32_t head_k_dim;  /* d_k */
+  int32_t head_v_dim;  /* d_v */
+  int32_t conv_kernel; /* K taps, 2..8 */
+  float l2_eps;        /* epsilon of the Q/K L2 norm: q / sqrt(sum q^2 + l2_eps); 1e-6 on the page */
+  float rms_eps;       /* epsilon of the per-head RMSNorm: o / sqrt(mean o^2 + rms_eps) */
+  int32_t act_dtype;   /* gdn_dtype_t of qkv, z, dt_raw, b_raw, conv1d_weight, conv1d_state */
+  int32_t out_dtype;   /* gdn_dtype_t of y / out (GDN_F32 keeps full precision) */
+} gdn_shape_t;
+
+/* Step 3 alone ("linear_attention.rs", step 3: fused causal_conv1d_update_l2norm).
+ * For every sequence and channel c: u = sum_j conv1d_weight[c][j] * w_j over the window
+ * w = (conv1d_state rows 0..K-2, qkv[c]), a = silu(u); Q and K segments of each k-head
+ * are then divided by sqrt(sum a^2 + l2_eps); V keeps silu(u). The conv state is rolled
+ * in place (rows shift up one, row K-2 <- qkv, bit-exact copy).
+ * Writes qkv_act [B][C] fp32 (device). */
+gdn_status_t gdn_conv_update(const gdn_shape_t* shape, void* conv1d_state, const void* qkv,
+                             const void* conv1d_weight, float* qkv_act, void* stream);
+
+/* Steps 4, 5 and 7 ("linear_attention.rs", steps 4-7: gdn_gate, sigmoid,
+ * gated_delta_rule_decode). Reads qkv_act [B][C] fp32 as written by gdn_conv_update
+ * (Q and K already unit-normalised). Per (b, v-head h): alpha, beta from dt_raw, b_raw,
+ * A_log, dt_bias; m = H^T k; H <- alpha H + k (beta (v - alpha m))^T (in place);
+ * y = H^T q / sqrt(d_k) with the updated H, written as y [B][H_v][d_v] in out_dtype. */
+gdn_status_t gdn_recurrent_step(const gdn_shape_t* shape, float* state, const float* qkv_act,
+                                const void* dt_raw, const void* b_raw, const float* A_log,
+                                const float* dt_bias, void* y, void* stream);
+
+/* One fused decode step, steps 3-11 of "linear_attention.rs" up to (excluding) the
+ * out_proj GEMV: conv update, gates, delta-rule update and readout, then
+ * out = y / sqrt(mean_j y_j^2 + rms_eps) * norm_weight * silu(z) per v-head.
+ * conv1d_state and state are updated in place; out is [B][H_v*d_v] in out_dtype.
+ * Each state element is read once and written once. */
+gdn_status_t gdn_decode_layer(const gdn_shape_t* shape, void* conv1d_state, float* state,
+                              const void* qkv, const void* conv1d_weight, const void* dt_raw,
+                              const void* b_raw, const void* z, const float* A_log,
+                              const float* dt_bias, const float* norm_weight, void* out,
+                              void* stream);
+
+/* T consecutive tokens of gdn_decode_layer per sequence, with both states carried
+ * from token to token (the rolled conv state of "ple.rs" serves prefill and decode
+ * alike). Inputs are [B][T][...]: qkv [B][T][C], dt_raw and b_raw [B][T][H_v],
+ * z [B][T][H_v*d_v]; out is [B][T][H_v*d_v]. Equal, up to rounding, to T calls of
+ * gdn_decode_layer. `workspace` (device, may be NULL when the query returns 0) must
+ * hold gdn_sequence_workspace_bytes(shape, T) bytes -> else GDN_ERR_WORKSPACE. */
+gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_state, float* state,
+                          const void* qkv, const void* conv1d_weight, const void* dt_raw,
+                          const void* b_raw, const void* z, const float* A_log,
+                          const float* dt_bias, const float* norm_weight, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes gdn_sequence needs for this shape and T (0 if none; SIZE_MAX if the
+ * shape is invalid). Host-only, no HIP call. */
+size_t gdn_sequence_workspace_bytes(const gdn_shape_t* shape, int32_t T);
+
+/* Static, NUL-terminated description of a status code. Host-only. */
+const char* gdn_status_string(int32_t status);
+
+/* ABI version of this header: (major << 16) | minor. Host-only. */
+int32_t gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

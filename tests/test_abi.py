@@ -1,0 +1,181 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/gdn.h
+declares, and its host-side validation returns the documented status for each kind
+of bad argument before anything reaches the GPU (these calls never launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_linear_causal_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, WORKSPACE, UNSUPPORTED, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+NO_GPU = _no_gpu()
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gdn.library_path()), reason="libgdn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) >= {"gdn_conv_update", "gdn_recurrent_step", "gdn_decode_layer", "gdn_sequence",
+                          "gdn_sequence_workspace_bytes", "gdn_status_string", "gdn_abi_version"}
+    lib = ctypes.CDLL(gdn.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    for code in gdn.STATUS:
+        assert gdn.gdn_status_string(code)
+    assert gdn.gdn_status_string(12345) == "unknown status"
+    assert gdn.gdn_abi_version() >> 16 == 1
+
+
+def qwen(batch=4, **kw):
+    args = dict(batch=batch, num_k_heads=16, num_v_heads=32, head_k_dim=128, head_v_dim=128)
+    args.update(kw)
+    return gdn.make_shape(**args)
+
+
+class Fake:
+    """Distinct, aligned, non-overlapping fake device addresses (never dereferenced)."""
+
+    next = 1 << 40  # shared by all instances: addresses never repeat within a run
+
+    def __call__(self, nbytes=1 << 32):
+        p = Fake.next
+        Fake.next += (nbytes + 4095) // 4096 * 4096 + (1 << 30)
+        return ctypes.c_void_p(p)
+
+
+def decode_args(shape, **override):
+    f = Fake()
+    names = ["conv1d_state", "state", "qkv", "conv1d_weight", "dt_raw", "b_raw", "z", "A_log", "dt_bias",
+             "norm_weight", "out"]
+    args = {n: f() for n in names}
+    args.update(override)
+    return [args[n] for n in names]
+
+
+def call_decode(shape, **override):
+    return gdn.library().gdn_decode_layer(ctypes.byref(shape), *decode_args(shape, **override), None)
+
+
+def call_sequence(shape, T, ws=None, ws_bytes=0, **override):
+    f = Fake()
+    names = ["conv1d_state", "state", "qkv", "conv1d_weight", "dt_raw", "b_raw", "z", "A_log", "dt_bias",
+             "norm_weight", "out"]
+    args = {n: f() for n in names}
+    args.update(override)
+    return gdn.library().gdn_sequence(ctypes.byref(shape), T, *[args[n] for n in names], ws,
+                                      ctypes.c_size_t(ws_bytes), None)
+
+
+def test_null_shape_and_pointers():
+    lib = gdn.library()
+    assert lib.gdn_decode_layer(None, *decode_args(None), None) == NULL
+    s = qwen()
+    for i in range(11):
+        args = decode_args(s)
+        args[i] = None
+        assert lib.gdn_decode_layer(ctypes.byref(s), *args, None) == NULL, i
+
+
+def test_empty_batch_is_noop_with_null_pointers():
+    s = qwen(batch=0)
+    lib = gdn.library()
+    assert lib.gdn_decode_layer(ctypes.byref(s), *([None] * 11), None) == OK
+    assert lib.gdn_conv_update(ctypes.byref(s), None, None, None, None, None) == OK
+    assert lib.gdn_recurrent_step(ctypes.byref(s), *([None] * 7), None) == OK
+    assert call_sequence(qwen(), 0, **{n: None for n in ["conv1d_state", "state", "qkv"]}) == OK
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", -1, SHAPE), ("num_k_heads", 0, SHAPE), ("num_v_heads", 0, SHAPE), ("num_v_heads", 33, SHAPE),
+    ("head_k_dim", 0, SHAPE), ("conv_kernel", 1, SHAPE), ("conv_kernel", 9, SHAPE),
+    ("l2_eps", -1.0, SHAPE), ("rms_eps", float("nan"), SHAPE), ("l2_eps", float("inf"), SHAPE),
+    ("act_dtype", 7, DTYPE), ("out_dtype", -1, DTYPE),
+    ("head_k_dim", 96, UNSUPPORTED), ("head_v_dim", 64, UNSUPPORTED), ("head_k_dim", 256, UNSUPPORTED),
+])
+def test_bad_shape_fields(field, value, status):
+    s = qwen()
+    if field in ("head_k_dim",) and value in (96, 256):
+        s.head_v_dim = value
+    setattr(s, field, value)
+    assert call_decode(s) == status
+    assert gdn.gdn_sequence_workspace_bytes(s, 4) == ctypes.c_size_t(-1).value
+
+
+def test_too_many_v_heads_per_k_head():
+    s = qwen(num_k_heads=1, num_v_heads=128)
+    assert call_decode(s) == UNSUPPORTED
+
+
+def test_grid_overflow():
+    s = qwen(batch=2 ** 30)
+    assert call_decode(s) == SHAPE
+
+
+def test_misaligned():
+    s = qwen()
+    f = Fake()
+    assert call_decode(s, state=ctypes.c_void_p(f().value + 4)) == ALIGN
+    assert call_decode(s, qkv=ctypes.c_void_p(f().value + 2)) == ALIGN
+    base = f().value
+    assert call_decode(s, dt_raw=ctypes.c_void_p(base + 1)) == ALIGN
+
+
+@pytest.mark.skipif(NO_GPU is False, reason="these calls pass validation and would launch on fake pointers")
+def test_valid_calls_reach_the_launch():
+    """Arguments that validation must accept reach the launch, which fails with
+    GDN_ERR_HIP on a host without a GPU (the pointers are fake)."""
+    s = qwen()
+    f = Fake()
+    # dt_raw only needs element alignment (bf16: 2 bytes)
+    assert call_decode(s, dt_raw=ctypes.c_void_p(f().value + 2)) == HIP
+    # read-only inputs may share memory
+    r = f()
+    assert call_decode(s, A_log=r, dt_bias=r) == HIP
+
+
+def test_aliasing():
+    s = qwen()
+    f = Fake()
+    p = f()
+    assert call_decode(s, state=p, out=p) == ALIAS
+    q = f()
+    # out overlapping the tail of z
+    z_bytes = s.batch * s.num_v_heads * s.head_v_dim * 2
+    assert call_decode(s, z=q, out=ctypes.c_void_p(q.value + z_bytes - 16)) == ALIAS
+
+
+def test_sequence_validation():
+    s = qwen()
+    assert call_sequence(s, -1) == SHAPE
+    assert gdn.gdn_sequence_workspace_bytes(s, 16) == 0
+    assert gdn.gdn_sequence_workspace_bytes(s, -1) == ctypes.c_size_t(-1).value
+    f = Fake()
+    assert call_sequence(s, 3, out=ctypes.c_void_p(f().value + 8)) == ALIGN
+
+
+def test_header_mentions_every_status():
+    text = open(HEADER).read()
+    for name in gdn.STATUS.values():
+        assert name in text

@@ -1,0 +1,204 @@
+"""GPU edge cases through the C-ABI: other head counts, head dims and tap counts
+(including the generic multi-pass and runtime-K kernels), ragged and empty batches,
+multi-token resume, determinism, full overwrite of poisoned outputs, guard regions,
+and error returns that leave every buffer untouched."""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_causal_amd import gdn
+from gated_deltanet_linear_causal_amd import inputs as I
+import gdn_cases as GC
+
+pytestmark = pytest.mark.gpu
+
+
+def cfg_of(name, B, Hk, Hv, d, K, act="bf16", steps=3, mode="decode"):
+    return I.GdnConfig(name=name, batch=B, num_k_heads=Hk, num_v_heads=Hv, head_k_dim=d, head_v_dim=d,
+                       conv_kernel=K, act_dtype=act, steps=steps, seed=1000 + B * 7 + Hv * 3 + d + K,
+                       mode=mode, state_std=0.02, conv_state_std=1.0)
+
+
+SHAPES = [
+    # name, B, Hk, Hv, d, K, act
+    ("G1_d128_fast", 3, 4, 4, 128, 4, "bf16"),
+    ("G4_d128_multipass", 2, 2, 8, 128, 4, "bf16"),
+    ("G3_d64_odd_group", 2, 2, 6, 64, 4, "bf16"),
+    ("G2_d64_K3", 5, 4, 8, 64, 3, "bf16"),
+    ("G2_d32_K2_f32", 3, 2, 4, 32, 2, "f32"),
+    ("G1_d32_K5_f32", 2, 3, 3, 32, 5, "f32"),
+    ("G2_d128_f32_acts", 2, 2, 4, 128, 4, "f32"),
+    ("G2_d128_ragged_B17", 17, 2, 4, 128, 4, "bf16"),
+]
+
+
+@pytest.mark.parametrize("name,B,Hk,Hv,d,K,act", SHAPES, ids=[s[0] for s in SHAPES])
+def test_decode_shapes(name, B, Hk, Hv, d, K, act):
+    cfg = cfg_of(name, B, Hk, Hv, d, K, act)
+    data = I.generate(cfg)
+    dv = GC.DeviceInputs(cfg, data)
+    outs = GC.gpu_decode(cfg, dv, cfg.steps)
+    r_out, r_st, r_cs = GC.oracle_decode(cfg, data, cfg.steps)
+    GC.compare(name + " out", GC.host_f64(outs), r_out, act)
+    GC.compare(name + " state", GC.host_f64(dv.state), r_st, act)
+    np.testing.assert_array_equal(GC.host_bits(dv.conv_state), GC.conv_state_bits_expected(r_cs, act))
+
+
+@pytest.mark.parametrize("name,B,Hk,Hv,d,K,act", SHAPES, ids=[s[0] for s in SHAPES])
+def test_sequence_shapes(name, B, Hk, Hv, d, K, act):
+    cfg = cfg_of(name, B, Hk, Hv, d, K, act, steps=6, mode="sequence")
+    data = I.generate(cfg)
+    dv = GC.DeviceInputs(cfg, data)
+    s = GC.shape_for(cfg)
+    out = torch.empty((B, cfg.steps, cfg.z_dim), dtype=torch.float32, device="cuda")
+    gdn.gdn_sequence(s, cfg.steps, dv.conv_state, dv.state, dv.qkv, dv.conv_w, dv.a, dv.b, dv.z, dv.A_log,
+                     dv.dt_bias, dv.norm_w, out)
+    torch.cuda.synchronize()
+    r_out, r_st, r_cs = GC.oracle_sequence(cfg, data)
+    GC.compare(name + " seq out", GC.host_f64(out), r_out, act)
+    GC.compare(name + " seq state", GC.host_f64(dv.state), r_st, act)
+    np.testing.assert_array_equal(GC.host_bits(dv.conv_state), GC.conv_state_bits_expected(r_cs, act))
+
+
+def _seq_inputs(T=9, B=3):
+    cfg = cfg_of("resume", B, 4, 8, 128, 4, "bf16", steps=T, mode="sequence")
+    return cfg, I.generate(cfg)
+
+
+def _run_seq(cfg, dv, lo, hi, out):
+    s = GC.shape_for(cfg)
+    sl = lambda t: t[:, lo:hi].contiguous()
+    o = torch.empty((cfg.batch, hi - lo, cfg.z_dim), dtype=torch.float32, device="cuda")
+    gdn.gdn_sequence(s, hi - lo, dv.conv_state, dv.state, sl(dv.qkv), dv.conv_w, sl(dv.a), sl(dv.b), sl(dv.z),
+                     dv.A_log, dv.dt_bias, dv.norm_w, o)
+    out[:, lo:hi] = o
+
+
+def test_sequence_resume_is_bitwise():
+    """T1 tokens then T2 tokens equal T1 + T2 tokens bit for bit (states carried)."""
+    cfg, data = _seq_inputs()
+    a, b = GC.DeviceInputs(cfg, data), GC.DeviceInputs(cfg, data)
+    out_a = torch.empty((cfg.batch, cfg.steps, cfg.z_dim), device="cuda")
+    out_b = torch.empty_like(out_a)
+    _run_seq(cfg, a, 0, cfg.steps, out_a)
+    for lo, hi in ((0, 2), (2, 3), (3, 9)):
+        _run_seq(cfg, b, lo, hi, out_b)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    assert torch.equal(a.state, b.state)
+    assert torch.equal(a.conv_state, b.conv_state)
+
+
+def test_sequence_equals_repeated_decode():
+    cfg, data = _seq_inputs(T=5)
+    a, b = GC.DeviceInputs(cfg, data), GC.DeviceInputs(cfg, data)
+    out_a = torch.empty((cfg.batch, cfg.steps, cfg.z_dim), device="cuda")
+    _run_seq(cfg, a, 0, cfg.steps, out_a)
+    s = GC.shape_for(cfg)
+    for t in range(cfg.steps):
+        o = torch.empty((cfg.batch, cfg.z_dim), device="cuda")
+        gdn.gdn_decode_layer(s, b.conv_state, b.state, b.qkv[:, t].contiguous(), b.conv_w, b.a[:, t].contiguous(),
+                             b.b[:, t].contiguous(), b.z[:, t].contiguous(), b.A_log, b.dt_bias, b.norm_w, o)
+        torch.cuda.synchronize()
+        GC.compare("decode vs seq t=%d" % t, GC.host_f64(o), GC.host_f64(out_a[:, t]), "bf16", (1e-5, 1e-4, 1e-2))
+    GC.compare("decode vs seq state", GC.host_f64(b.state), GC.host_f64(a.state), "bf16", (1e-6, 1e-4, 1e-2))
+    assert torch.equal(a.conv_state, b.conv_state)
+
+
+def test_empty_batch_and_zero_tokens_are_noops():
+    cfg = I.config(1)
+    data = I.generate(cfg)
+    dv = GC.DeviceInputs(cfg, data)
+    st0, cs0 = dv.state.clone(), dv.conv_state.clone()
+    s0 = GC.shape_for(cfg, batch=0)
+    out = torch.full((1, cfg.z_dim), 7.0, device="cuda")
+    gdn.gdn_decode_layer(s0, dv.conv_state, dv.state, dv.qkv[0], dv.conv_w, dv.a[0], dv.b[0], dv.z[0], dv.A_log,
+                         dv.dt_bias, dv.norm_w, out)
+    s1 = GC.shape_for(cfg)
+    gdn.gdn_sequence(s1, 0, dv.conv_state, dv.state, dv.qkv[0], dv.conv_w, dv.a[0], dv.b[0], dv.z[0], dv.A_log,
+                     dv.dt_bias, dv.norm_w, out)
+    torch.cuda.synchronize()
+    assert torch.equal(dv.state, st0) and torch.equal(dv.conv_state, cs0)
+    assert torch.all(out == 7.0)
+
+
+def test_deterministic_and_poison_overwritten():
+    """Two runs from the same inputs agree bit for bit, and outputs poisoned with NaN
+    are fully overwritten."""
+    cfg = I.config(2).with_(batch=8)
+    data = I.generate(cfg, steps=2)
+    runs = []
+    for _ in range(2):
+        dv = GC.DeviceInputs(cfg, data)
+        s = GC.shape_for(cfg)
+        out = torch.full((2, cfg.batch, cfg.z_dim), float("nan"), device="cuda")
+        for t in range(2):
+            gdn.gdn_decode_layer(s, dv.conv_state, dv.state, dv.qkv[t], dv.conv_w, dv.a[t], dv.b[t], dv.z[t],
+                                 dv.A_log, dv.dt_bias, dv.norm_w, out[t])
+        act = torch.full((cfg.batch, cfg.channels), float("nan"), device="cuda")
+        y = torch.full((cfg.batch, cfg.num_v_heads, cfg.head_v_dim), float("nan"), device="cuda")
+        gdn.gdn_conv_update(s, dv.conv_state, dv.qkv[0], dv.conv_w, act)
+        gdn.gdn_recurrent_step(s, dv.state, act, dv.a[0], dv.b[0], dv.A_log, dv.dt_bias, y)
+        torch.cuda.synchronize()
+        for tns in (out, act, y):
+            assert torch.isfinite(tns).all()
+        runs.append((out, act, y, dv.state, dv.conv_state))
+    for x, y_ in zip(*runs):
+        assert torch.equal(x, y_)
+
+
+def test_guard_regions_intact():
+    """Every buffer sits inside a larger allocation whose guard bytes before and after
+    must survive a decode step and a conv update."""
+    cfg = I.config(2).with_(batch=3)
+    data = I.generate(cfg, steps=1)
+    G = 4096  # guard elements each side
+
+    def guarded(t):
+        flat = t.reshape(-1)
+        big = torch.empty(flat.numel() + 2 * G, dtype=t.dtype, device="cuda")
+        big.view(torch.int16 if t.element_size() == 2 else torch.int32).fill_(0x5A5A if t.element_size() == 2
+                                                                              else 0x5A5A5A5A)
+        big[G:G + flat.numel()] = flat
+        return big, big[G:G + flat.numel()].view(t.shape)
+
+    dv = GC.DeviceInputs(cfg, data)
+    bufs = {}
+    for name in ("conv_state", "state"):
+        bufs[name] = guarded(getattr(dv, name))
+    out_big, out = guarded(torch.zeros((cfg.batch, cfg.z_dim), device="cuda"))
+    act_big, act = guarded(torch.zeros((cfg.batch, cfg.channels), device="cuda"))
+    y_big, y = guarded(torch.zeros((cfg.batch, cfg.num_v_heads, cfg.head_v_dim), device="cuda"))
+    s = GC.shape_for(cfg)
+    gdn.gdn_decode_layer(s, bufs["conv_state"][1], bufs["state"][1], dv.qkv[0], dv.conv_w, dv.a[0], dv.b[0],
+                         dv.z[0], dv.A_log, dv.dt_bias, dv.norm_w, out)
+    gdn.gdn_conv_update(s, bufs["conv_state"][1], dv.qkv[0], dv.conv_w, act)
+    gdn.gdn_recurrent_step(s, bufs["state"][1], act, dv.a[0], dv.b[0], dv.A_log, dv.dt_bias, y)
+    torch.cuda.synchronize()
+    for big in [b[0] for b in bufs.values()] + [out_big, act_big, y_big]:
+        raw = big.view(torch.int16 if big.element_size() == 2 else torch.int32)
+        pat = 0x5A5A if big.element_size() == 2 else 0x5A5A5A5A
+        assert torch.all(raw[:G] == pat) and torch.all(raw[-G:] == pat)
+
+
+def test_error_leaves_buffers_untouched():
+    cfg = I.config(2).with_(batch=2)
+    data = I.generate(cfg, steps=1)
+    dv = GC.DeviceInputs(cfg, data)
+    st0, cs0 = dv.state.clone(), dv.conv_state.clone()
+    out = torch.full((cfg.batch, cfg.z_dim), 3.0, device="cuda")
+    bad = GC.shape_for(cfg)
+    bad.rms_eps = -1.0
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_decode_layer(bad, dv.conv_state, dv.state, dv.qkv[0], dv.conv_w, dv.a[0], dv.b[0], dv.z[0],
+                             dv.A_log, dv.dt_bias, dv.norm_w, out)
+    assert e.value.status == -2
+    s = GC.shape_for(cfg)
+    with pytest.raises(gdn.GdnError) as e:  # out overlaps the state
+        gdn.gdn_decode_layer(s, dv.conv_state, dv.state, dv.qkv[0], dv.conv_w, dv.a[0], dv.b[0], dv.z[0],
+                             dv.A_log, dv.dt_bias, dv.norm_w, dv.state.view(-1)[:cfg.batch * cfg.z_dim])
+    assert e.value.status == -5
+    torch.cuda.synchronize()
+    assert torch.equal(dv.state, st0) and torch.equal(dv.conv_state, cs0)
+    assert torch.all(out == 3.0)

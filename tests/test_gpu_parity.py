@@ -1,0 +1,139 @@
+"""GPU parity of the HIP path (through the C-ABI) against the fp64 oracle on the five
+seeded workloads: tiny fp32, and the Qwen3.5-style layer at B = 1, 64, 512 and a
+B = 8, T = 4096 sequence. Outputs and final recurrent state within tolerance, the
+conv state bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_causal_amd import gdn
+from gated_deltanet_linear_causal_amd import inputs as I
+import gdn_cases as GC
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_decode(cfg, steps, seqs=None, out_dtype="f32"):
+    data = I.generate(cfg, steps=steps)
+    d = GC.DeviceInputs(cfg, data)
+    outs = GC.gpu_decode(cfg, d, steps, out_dtype=out_dtype)
+    idx = np.arange(cfg.batch) if seqs is None else np.asarray(seqs)
+    r_out, r_st, r_cs = GC.oracle_decode(cfg, data, steps, idx)
+    got = GC.host_f64(outs)[:, idx]
+    if out_dtype == "bf16":
+        # a bf16 output is the fp32 result rounded once: within one bf16 ulp (2^-7 |x|)
+        err = np.abs(got - r_out) - (2.0 ** -7 * np.abs(r_out) + 1e-6)
+        print("%s bf16 out: worst margin %.3e (<= 0 passes)" % (cfg.name, err.max()))
+        assert np.all(err <= 0)
+    else:
+        GC.compare("%s out" % cfg.name, got, r_out, cfg.act_dtype)
+    GC.compare("%s state" % cfg.name, GC.host_f64(d.state)[idx], r_st, cfg.act_dtype)
+    cs_bits = GC.host_bits(d.conv_state)
+    np.testing.assert_array_equal(cs_bits[idx], GC.conv_state_bits_expected(r_cs, cfg.act_dtype))
+    return data, d
+
+
+def test_tiny_fp32_decode_16_steps():
+    _check_decode(I.config(0), 16)
+
+
+def test_tiny_fp32_decode_bf16_output():
+    _check_decode(I.config(0), 4, out_dtype="bf16")
+
+
+def test_tiny_fp32_staged_entry_points():
+    """gdn_conv_update then gdn_recurrent_step equal the oracle's step-3 output and
+    step-7 readout, step after step."""
+    from oracle import oracle as O
+    cfg = I.config(0)
+    data = I.generate(cfg)
+    d = GC.DeviceInputs(cfg, data)
+    s = GC.shape_for(cfg)
+    os_ = O.shape_of(cfg)
+    cs = data["conv_state"].astype(np.float64)
+    st = data["state"].astype(np.float64)
+    act = torch.empty((cfg.batch, cfg.channels), dtype=torch.float32, device="cuda")
+    y = torch.empty((cfg.batch, cfg.num_v_heads, cfg.head_v_dim), dtype=torch.float32, device="cuda")
+    for t in range(cfg.steps):
+        gdn.gdn_conv_update(s, d.conv_state, d.qkv[t], d.conv_w, act)
+        gdn.gdn_recurrent_step(s, d.state, act, d.a[t], d.b[t], d.A_log, d.dt_bias, y)
+        r_act = O.conv_update(os_, cs, data["qkv"][t], data["conv_w"])
+        r_o, _, _ = O.recurrent_step(os_, st, r_act, data["a"][t], data["b"][t], data["A_log"], data["dt_bias"])
+        torch.cuda.synchronize()
+        GC.compare("tiny qkv_act t=%d" % t, GC.host_f64(act), r_act, "f32")
+        GC.compare("tiny y t=%d" % t, GC.host_f64(y), r_o, "f32")
+    GC.compare("tiny staged state", GC.host_f64(d.state), st, "f32")
+    np.testing.assert_array_equal(GC.host_bits(d.conv_state), GC.conv_state_bits_expected(cs, "f32"))
+
+
+def test_tiny_fp32_sequence():
+    cfg = I.config(0).with_(mode="sequence")
+    data = I.generate(cfg)
+    d = GC.DeviceInputs(cfg, data)
+    s = GC.shape_for(cfg)
+    out = torch.empty((cfg.batch, cfg.steps, cfg.z_dim), dtype=torch.float32, device="cuda")
+    gdn.gdn_sequence(s, cfg.steps, d.conv_state, d.state, d.qkv, d.conv_w, d.a, d.b, d.z, d.A_log, d.dt_bias,
+                     d.norm_w, out)
+    torch.cuda.synchronize()
+    r_out, r_st, r_cs = GC.oracle_sequence(cfg, data)
+    GC.compare("tiny seq out", GC.host_f64(out), r_out, "f32")
+    GC.compare("tiny seq state", GC.host_f64(d.state), r_st, "f32")
+    np.testing.assert_array_equal(GC.host_bits(d.conv_state), GC.conv_state_bits_expected(r_cs, "f32"))
+
+
+def test_qwen35_B1_one_step():
+    _check_decode(I.config(1), 1)
+
+
+def test_qwen35_B1_staged_entry_points():
+    from oracle import oracle as O
+    cfg = I.config(1)
+    data = I.generate(cfg)
+    d = GC.DeviceInputs(cfg, data)
+    s = GC.shape_for(cfg)
+    os_ = O.shape_of(cfg)
+    act = torch.empty((1, cfg.channels), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, cfg.num_v_heads, cfg.head_v_dim), dtype=torch.float32, device="cuda")
+    gdn.gdn_conv_update(s, d.conv_state, d.qkv[0], d.conv_w, act)
+    gdn.gdn_recurrent_step(s, d.state, act, d.a[0], d.b[0], d.A_log, d.dt_bias, y)
+    torch.cuda.synchronize()
+    cs = I.widen(data["conv_state"], "bf16").astype(np.float64)
+    st = data["state"].astype(np.float64)
+    r_act = O.conv_update(os_, cs, I.widen(data["qkv"][0], "bf16"), I.widen(data["conv_w"], "bf16"))
+    r_o, _, _ = O.recurrent_step(os_, st, r_act, I.widen(data["a"][0], "bf16"), I.widen(data["b"][0], "bf16"),
+                                 data["A_log"], data["dt_bias"])
+    GC.compare("B1 qkv_act", GC.host_f64(act), r_act, "bf16")
+    GC.compare("B1 y", GC.host_f64(y), r_o, "bf16")
+    GC.compare("B1 staged state", GC.host_f64(d.state), st, "bf16")
+    np.testing.assert_array_equal(GC.host_bits(d.conv_state), GC.conv_state_bits_expected(cs, "bf16"))
+
+
+def test_qwen35_B64_32_steps():
+    _check_decode(I.config(2), 32)
+
+
+def test_qwen35_B512_32_steps_sampled():
+    """All 512 sequences run on the GPU; the oracle recomputes 16 of them (sequences
+    are independent). The conv state of every sequence must hold the last K-1 = 3
+    inputs bit for bit."""
+    cfg = I.config(3)
+    rng = np.random.default_rng(123)
+    seqs = np.unique(np.concatenate([[0, 1, 255, 511], rng.choice(512, 12, replace=False)]))
+    data, d = _check_decode(cfg, 32, seqs)
+    np.testing.assert_array_equal(GC.host_bits(d.conv_state), np.swapaxes(data["qkv"][29:32], 0, 1))
+
+
+def test_qwen35_sequence_B8_T4096():
+    cfg = I.config(4)
+    data = I.generate(cfg)
+    d = GC.DeviceInputs(cfg, data)
+    s = GC.shape_for(cfg)
+    out = torch.empty((cfg.batch, cfg.steps, cfg.z_dim), dtype=torch.float32, device="cuda")
+    gdn.gdn_sequence(s, cfg.steps, d.conv_state, d.state, d.qkv, d.conv_w, d.a, d.b, d.z, d.A_log, d.dt_bias,
+                     d.norm_w, out)
+    torch.cuda.synchronize()
+    r_out, r_st, r_cs = GC.oracle_sequence(cfg, data)
+    GC.compare("seq B8 T4096 out", GC.host_f64(out), r_out, "bf16")
+    GC.compare("seq B8 T4096 state", GC.host_f64(d.state), r_st, "bf16")
+    np.testing.assert_array_equal(GC.host_bits(d.conv_state), GC.conv_state_bits_expected(r_cs, "bf16"))
