@@ -12,6 +12,16 @@
 
 namespace {
 
+// A recurrent state larger than this cannot stay in MI355X's 256 MB Infinity Cache
+// from one step to the next, so its loads and stores are marked non-temporal; smaller
+// states keep the default policy and are re-read from the cache. Measured on MI355X
+// (Qwen3.5-style layer, 2 MiB of state per sequence): the default policy is faster up
+// to B = 128 (256 MiB), the streaming one from B = 160 (320 MiB) on.
+#ifndef GDN_STREAM_STATE_BYTES
+#define GDN_STREAM_STATE_BYTES (256ull << 20)
+#endif
+constexpr uint64_t kStreamStateBytes = GDN_STREAM_STATE_BYTES;
+
 struct Buf {
   const void* p;
   size_t bytes;
@@ -92,6 +102,8 @@ gdn::KernelArgs base_args(const gdn_shape_t* s) {
   a.rms_eps = s->rms_eps;
   a.act_bf16 = s->act_dtype == GDN_BF16;
   a.out_bf16 = s->out_dtype == GDN_BF16;
+  const uint64_t state_bytes = static_cast<uint64_t>(s->batch) * s->num_v_heads * s->head_k_dim * s->head_v_dim * 4;
+  a.stream_state = state_bytes > kStreamStateBytes;
   return a;
 }
 

@@ -16,6 +16,7 @@ struct KernelArgs {
   int B, Hk, Hv, G, K, C, T;
   float l2_eps, rms_eps;
   int act_bf16, out_bf16;
+  int stream_state;        // 1: state accesses marked non-temporal (state larger than the cache)
   void* conv_state;        // [B][K-1][C] act dtype, in place
   float* state;            // [B][Hv][D][D] fp32, in place
   const void* qkv;         // act dtype

@@ -75,21 +75,34 @@ __device__ __forceinline__ void store_out4(void* p, long i, float4 v, bool bf16)
 // Accesses outside [0, bytes) read 0 and are not written (hardware range check).
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
+// Cache policy of the state's buffer accesses (gfx940-family bits: 0 sc0, 1 nt, 4 sc1).
+// STREAM = true marks loads and stores non-temporal (nt): for a state larger than the
+// 256 MB Infinity Cache every step streams it from HBM anyway, and on MI355X the nt
+// pair lifts the B = 512 step from ~5.45 to ~6.3 TB/s. A state that fits the cache is
+// accessed with the default policy so the next step finds it there.
+template <bool STREAM>
+struct StatePolicy {
+  static constexpr int kLoad = STREAM ? 2 : 0;
+  static constexpr int kStore = STREAM ? 2 : 0;
+};
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
                                            0x00020000);
 }
+template <bool STREAM>
 __device__ __forceinline__ float4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, StatePolicy<STREAM>::kLoad);
   return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
+template <bool STREAM>
 __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float4 f) {
   u32x4 v;
   v.x = __float_as_uint(f.x);
   v.y = __float_as_uint(f.y);
   v.z = __float_as_uint(f.z);
   v.w = __float_as_uint(f.w);
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, StatePolicy<STREAM>::kStore);
 }
 
 // ----------------------------------------------------------------------------------
@@ -275,7 +288,7 @@ __device__ __forceinline__ float conv_channel_generic(const KernelArgs& a, long 
 // and returns o = H'^T q / sqrt(D) = (alpha p + (k.q) delta) / sqrt(D) for the lane's
 // 4 columns.
 // ----------------------------------------------------------------------------------
-template <int D, int P, bool STORE, int R>
+template <int D, int P, bool STORE, bool STREAM, int R>
 __device__ __forceinline__ float4 delta_rule(float4 (&hreg)[R], const float* kr, const float* qr, float4 v4,
                                              float alpha, float beta, float kq, __amdgpu_buffer_rsrc_t srs,
                                              uint32_t voff, uint32_t soff) {
@@ -322,7 +335,7 @@ __device__ __forceinline__ float4 delta_rule(float4 (&hreg)[R], const float* kr,
       h.y = fmaf(kv[e], delta.y, alpha * h.y);
       h.z = fmaf(kv[e], delta.z, alpha * h.z);
       h.w = fmaf(kv[e], delta.w, alpha * h.w);
-      if constexpr (STORE) buf_store4(srs, voff, soff + (4 * k4 + e) * kRowBytes, h);
+      if constexpr (STORE) buf_store4<STREAM>(srs, voff, soff + (4 * k4 + e) * kRowBytes, h);
     }
   }
   return (1.0f / sqrtf(static_cast<float>(D))) * (alpha * pq + kq * delta);
@@ -354,7 +367,7 @@ __device__ __forceinline__ float4 gated(float4 o, float r, float4 w4, float4 z4)
 // kModeRec (steps 4-7 from qkv_act), kModeFused (steps 3-11).
 // Grid: B*Hk workgroups of Layout::NT lanes. LDS: q[D], k[D], v[P*D], red, hred.
 // ----------------------------------------------------------------------------------
-template <int D, int P, int MODE, bool BF, int KT>
+template <int D, int P, int MODE, bool BF, int KT, bool STREAM>
 __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_fast(const KernelArgs a) {
   using L = Layout<D, P>;
   using CR = ConvRegs<BF, KT, (2 + P) * D, L::NT, D>;
@@ -412,7 +425,7 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_fast(const Kernel
   float4 hreg[R];
   if constexpr (MODE != kModeConv) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) hreg[k] = buf_load4(srs, voff, k * kRowBytes);
+    for (int k = 0; k < R; ++k) hreg[k] = buf_load4<STREAM>(srs, voff, k * kRowBytes);
   }
 
   // ---- 3. prelude: conv + SiLU (+ roll), L2 norms of q and k
@@ -473,7 +486,7 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_fast(const Kernel
     const float alpha = gate_alpha(dt, dt_bias, A_log);
     const float beta = gate_beta(braw);
     const float4 v4 = *reinterpret_cast<const float4*>(s_v + ph * D + 4 * cg);
-    const float4 o = delta_rule<D, P, true>(hreg, s_k + rg * R, s_q + rg * R, v4, alpha, beta, kq, srs, voff, 0);
+    const float4 o = delta_rule<D, P, true, STREAM>(hreg, s_k + rg * R, s_q + rg * R, v4, alpha, beta, kq, srs, voff, 0);
     if constexpr (MODE == kModeRec) {
       if (rg == 0) store_out4(a.out, b * a.out_bs + static_cast<long>(h) * D + 4 * cg, o, a.out_bf16 != 0);
     } else {
@@ -489,7 +502,7 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_fast(const Kernel
 // supported shape; the fast kernel covers K = 4 with G <= 2.
 // Dynamic LDS: q[D], k[D], v[G*D], red[NW*4], hred[NW] floats.
 // ----------------------------------------------------------------------------------
-template <int D, int P, int MODE, bool BF>
+template <int D, int P, int MODE, bool BF, bool STREAM>
 __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_generic(const KernelArgs a) {
   using L = Layout<D, P>;
   constexpr int NT = L::NT, R = L::R, CGL = L::CGL, NW = L::NW;
@@ -584,10 +597,10 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_generic(const Ker
       const float beta = gate_beta(Act<BF>::load(a.b_raw, b * a.ab_bs + h));
       float4 hreg[R];
 #pragma unroll
-      for (int k = 0; k < R; ++k) hreg[k] = buf_load4(srs, voff, soff + k * kRowBytes);
+      for (int k = 0; k < R; ++k) hreg[k] = buf_load4<STREAM>(srs, voff, soff + k * kRowBytes);
       const float4 v4 = *reinterpret_cast<const float4*>(s_v + hl * D + 4 * cg);
       const float4 o =
-          delta_rule<D, P, true>(hreg, s_k + rg * R, s_q + rg * R, v4, alpha, beta, kq, srs, voff, soff);
+          delta_rule<D, P, true, STREAM>(hreg, s_k + rg * R, s_q + rg * R, v4, alpha, beta, kq, srs, voff, soff);
       if constexpr (MODE == kModeRec) {
         if (rg == 0) store_out4(a.out, b * a.out_bs + static_cast<long>(h) * D + 4 * cg, o, a.out_bf16 != 0);
       } else {
@@ -650,7 +663,7 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_seq_kernel(const Kerne
       make_rsrc(a.state + (static_cast<long>(b) * a.Hv + static_cast<long>(g) * P) * (D * D), P * kHeadBytes);
   float4 hreg[R];
 #pragma unroll
-  for (int k = 0; k < R; ++k) hreg[k] = buf_load4(srs, voff, k * kRowBytes);
+  for (int k = 0; k < R; ++k) hreg[k] = buf_load4<false>(srs, voff, k * kRowBytes);
 
   for (int tok = 0; tok < a.T; ++tok) {
     cr.compute(s_q, s_k, s_v);
@@ -683,7 +696,7 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_seq_kernel(const Kerne
     }
     __syncthreads();
     const float4 v4 = *reinterpret_cast<const float4*>(s_v + ph * D + 4 * cg);
-    const float4 o = delta_rule<D, P, false>(hreg, s_k + rg * R, s_q + rg * R, v4, alpha, beta, kq, srs, voff, 0);
+    const float4 o = delta_rule<D, P, false, false>(hreg, s_k + rg * R, s_q + rg * R, v4, alpha, beta, kq, srs, voff, 0);
     const float r = head_rms_scale<D, P>(o, rg == 0, ph, hred, a.rms_eps);
     if (rg == 0)
       store_out4(a.out, b * a.out_bs + tok * a.out_ts + static_cast<long>(h) * D + 4 * cg, gated(o, r, w4, zc), obf);
@@ -691,7 +704,7 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_seq_kernel(const Kerne
   }
 
 #pragma unroll
-  for (int k = 0; k < R; ++k) buf_store4(srs, voff, k * kRowBytes, hreg[k]);
+  for (int k = 0; k < R; ++k) buf_store4<false>(srs, voff, k * kRowBytes, hreg[k]);
   cr.store_window(a.conv_state, cs_base, a.C);
 }
 
@@ -699,25 +712,33 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_seq_kernel(const Kerne
 // launchers
 // ----------------------------------------------------------------------------------
 
-template <int D, int P, bool BF>
-hipError_t launch_step_d(int mode, bool fast, const KernelArgs& a, hipStream_t s) {
+template <int D, int P, bool BF, bool ST>
+void launch_step_s(int mode, bool fast, const KernelArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hk));
   const dim3 block(Layout<D, P>::NT);
   if (fast) {
     switch (mode) {
-      case kModeConv: gdn_step_fast<D, P, kModeConv, BF, 4><<<grid, block, 0, s>>>(a); break;
-      case kModeRec: gdn_step_fast<D, P, kModeRec, BF, 4><<<grid, block, 0, s>>>(a); break;
-      default: gdn_step_fast<D, P, kModeFused, BF, 4><<<grid, block, 0, s>>>(a); break;
+      case kModeConv: gdn_step_fast<D, P, kModeConv, BF, 4, false><<<grid, block, 0, s>>>(a); break;
+      case kModeRec: gdn_step_fast<D, P, kModeRec, BF, 4, ST><<<grid, block, 0, s>>>(a); break;
+      default: gdn_step_fast<D, P, kModeFused, BF, 4, ST><<<grid, block, 0, s>>>(a); break;
     }
   } else {
     const size_t lds =
         sizeof(float) * (2 * D + static_cast<size_t>(a.G) * D + Layout<D, P>::NW * 4 + Layout<D, P>::NW);
     switch (mode) {
-      case kModeConv: gdn_step_generic<D, P, kModeConv, BF><<<grid, block, lds, s>>>(a); break;
-      case kModeRec: gdn_step_generic<D, P, kModeRec, BF><<<grid, block, lds, s>>>(a); break;
-      default: gdn_step_generic<D, P, kModeFused, BF><<<grid, block, lds, s>>>(a); break;
+      case kModeConv: gdn_step_generic<D, P, kModeConv, BF, false><<<grid, block, lds, s>>>(a); break;
+      case kModeRec: gdn_step_generic<D, P, kModeRec, BF, ST><<<grid, block, lds, s>>>(a); break;
+      default: gdn_step_generic<D, P, kModeFused, BF, ST><<<grid, block, lds, s>>>(a); break;
     }
   }
+}
+
+template <int D, int P, bool BF>
+hipError_t launch_step_d(int mode, bool fast, const KernelArgs& a, hipStream_t s) {
+  if (a.stream_state)
+    launch_step_s<D, P, BF, true>(mode, fast, a, s);
+  else
+    launch_step_s<D, P, BF, false>(mode, fast, a, s);
   return hipGetLastError();
 }
 
