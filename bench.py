@@ -112,6 +112,39 @@ def time_decode(cfg, d, steps, warmup, torch, gdn):
     return e0.elapsed_time(e1) / 1e3 / steps
 
 
+def time_pooled(cfg, d, pool, steps, warmup, torch, gdn):
+    """gdn_decode_layer_pooled: the batch's states are B distinct random slots of a
+    pool of `pool` states (the batch's own states are copied into those slots)."""
+    g = torch.Generator(device="cpu").manual_seed(7)
+    slots = torch.randperm(pool, generator=g)[:cfg.batch].to(torch.int32).cuda()
+    st_pool = torch.zeros((pool,) + tuple(d["state"].shape[1:]), dtype=torch.float32, device="cuda")
+    cs_pool = torch.zeros((pool,) + tuple(d["conv_state"].shape[1:]), dtype=d["conv_state"].dtype, device="cuda")
+    st_pool[slots.long()] = d["state"]
+    cs_pool[slots.long()] = d["conv_state"]
+    s = gdn.make_shape(cfg.batch, cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim,
+                       cfg.conv_kernel, cfg.l2_eps, cfg.rms_eps, cfg.act_dtype, "f32")
+    nin = d["qkv"].shape[0]
+    out = torch.empty((cfg.batch, cfg.z_dim), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        j = i % nin
+        gdn.gdn_decode_layer_pooled(s, slots, cs_pool, st_pool, d["qkv"][j], d["conv_w"], d["a"][j], d["b"][j],
+                                    d["z"][j], d["A_log"], d["dt_bias"], d["norm_w"], out, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del st_pool, cs_pool
+    return e0.elapsed_time(e1) / 1e3 / steps
+
+
 def time_sequence(cfg, d, reps, torch, gdn):
     s = gdn.make_shape(cfg.batch, cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim,
                        cfg.conv_kernel, cfg.l2_eps, cfg.rms_eps, cfg.act_dtype, "f32")
@@ -271,6 +304,12 @@ def main():
                      "kernel": "gdn_step_fast<128, 2, fused, bf16, K=4>", "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": round(sec * 1e6, 2)},
     }
+    if not args.no_sweep:
+        pool = 2 * cfg.batch
+        psec = time_pooled(cfg, d, pool, args.steps, args.warmup, torch, gdn)
+        result["pooled"] = {"workload": "B=512 active sequences in random distinct slots of a %d-state pool" % pool,
+                            "us_per_step": round(psec * 1e6, 2), "steps_per_s": round(cfg.batch / psec, 1),
+                            "GB_s": round(nbytes / psec / 1e9, 1), "frac": round(nbytes / psec / 1e9 / HBM_PEAK_GBS, 4)}
     del d
     torch.cuda.empty_cache()
     if not args.no_sweep:

@@ -104,6 +104,8 @@ gdn::KernelArgs base_args(const gdn_shape_t* s) {
   a.out_bf16 = s->out_dtype == GDN_BF16;
   const uint64_t state_bytes = static_cast<uint64_t>(s->batch) * s->num_v_heads * s->head_k_dim * s->head_v_dim * 4;
   a.stream_state = state_bytes > kStreamStateBytes;
+  a.slots = nullptr;
+  a.pool = s->batch;
   return a;
 }
 
@@ -212,6 +214,56 @@ gdn_status_t gdn_decode_layer(const gdn_shape_t* shape, void* conv1d_state, floa
   gdn::KernelArgs a = base_args(shape);
   a.conv_state = conv1d_state;
   a.state = state;
+  a.qkv = qkv;
+  a.qkv_bs = static_cast<long>(z.C);
+  a.conv_w = conv1d_weight;
+  a.dt_raw = dt_raw;
+  a.b_raw = b_raw;
+  a.ab_bs = static_cast<long>(z.Hv);
+  a.z = z_in;
+  a.z_bs = static_cast<long>(z.Hv * z.d);
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.norm_w = norm_weight;
+  a.out = out;
+  a.out_bs = static_cast<long>(z.Hv * z.d);
+  (void)hipGetLastError();
+  return launched(gdn::launch_step(gdn::kModeFused, shape->head_k_dim, heads_per_pass(shape), a,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_decode_layer_pooled(const gdn_shape_t* shape, int32_t pool_size, const int32_t* slots,
+                                     void* conv1d_state_pool, float* state_pool, const void* qkv,
+                                     const void* conv1d_weight, const void* dt_raw, const void* b_raw,
+                                     const void* z_in, const float* A_log, const float* dt_bias,
+                                     const float* norm_weight, void* out, void* stream) {
+  gdn_status_t st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (pool_size < 0) return GDN_ERR_SHAPE;
+  const Sizes z(shape);
+  if (z.B == 0) return GDN_OK;
+  const size_t P = static_cast<size_t>(pool_size);
+  const Buf bufs[] = {
+      {slots, z.B * 4, false, 4},
+      {conv1d_state_pool, P * (z.K - 1) * z.C * z.ea, true, 16},
+      {state_pool, P * z.Hv * z.d * z.d * 4, true, 16},
+      {qkv, z.B * z.C * z.ea, false, 16},
+      {conv1d_weight, z.conv_w(), false, 16},
+      {dt_raw, z.B * z.Hv * z.ea, false, z.ea},
+      {b_raw, z.B * z.Hv * z.ea, false, z.ea},
+      {z_in, z.B * z.Hv * z.d * z.ea, false, 16},
+      {A_log, z.Hv * 4, false, 4},
+      {dt_bias, z.Hv * 4, false, 4},
+      {norm_weight, z.d * 4, false, 16},
+      {out, z.B * z.Hv * z.d * z.eo, true, 16},
+  };
+  if ((st = check_buffers(bufs, 12)) != GDN_OK) return st;
+  if (pool_size == 0) return GDN_OK;  // every slot is outside the pool: nothing to do
+  gdn::KernelArgs a = base_args(shape);
+  a.slots = slots;
+  a.pool = pool_size;
+  a.conv_state = conv1d_state_pool;
+  a.state = state_pool;
   a.qkv = qkv;
   a.qkv_bs = static_cast<long>(z.C);
   a.conv_w = conv1d_weight;

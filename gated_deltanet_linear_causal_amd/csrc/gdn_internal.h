@@ -17,6 +17,8 @@ struct KernelArgs {
   float l2_eps, rms_eps;
   int act_bf16, out_bf16;
   int stream_state;        // 1: state accesses marked non-temporal (state larger than the cache)
+  const int* slots;        // [B] state-pool slot of each sequence, or null (slot = b)
+  int pool;                // number of state slots; slots outside [0, pool) are skipped
   void* conv_state;        // [B][K-1][C] act dtype, in place
   float* state;            // [B][Hv][D][D] fp32, in place
   const void* qkv;         // act dtype

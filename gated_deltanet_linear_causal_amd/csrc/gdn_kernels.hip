@@ -270,9 +270,9 @@ struct ConvRegs {
 
 // Generic conv of one channel (runtime K): window loads, conv, SiLU, in-place roll.
 template <bool BF>
-__device__ __forceinline__ float conv_channel_generic(const KernelArgs& a, long b, long gc) {
+__device__ __forceinline__ float conv_channel_generic(const KernelArgs& a, long b, long sb, long gc) {
   using raw_t = typename Act<BF>::raw_t;
-  const long cs0 = b * (a.K - 1) * static_cast<long>(a.C) + gc;
+  const long cs0 = sb * (a.K - 1) * static_cast<long>(a.C) + gc;
   raw_t win[kMaxConvTaps];
   for (int j = 0; j < a.K - 1; ++j) win[j] = Act<BF>::raw(a.conv_state, cs0 + static_cast<long>(j) * a.C);
   win[a.K - 1] = Act<BF>::raw(a.qkv, b * a.qkv_bs + gc);
@@ -387,7 +387,11 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_fast(const Kernel
   const int cg = (u >> 6) * CGL + (u & (CGL - 1));
   const int rg = (u & 63) / CGL;
   const int h = g * P + ph;
-  const long cs_base = static_cast<long>(b) * (KT - 1) * a.C;
+  // state slot of sequence b: b itself, or a pool entry; a slot outside the pool marks
+  // an inactive sequence whose workgroups do nothing (uniform per workgroup)
+  const int sb = a.slots ? a.slots[b] : b;
+  if (sb < 0 || sb >= a.pool) return;
+  const long cs_base = static_cast<long>(sb) * (KT - 1) * a.C;
 
   // ---- 1. small loads first
   CR cr;
@@ -421,7 +425,7 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_fast(const Kernel
   const uint32_t voff = static_cast<uint32_t>(ph) * kHeadBytes + static_cast<uint32_t>(rg * R) * kRowBytes +
                         static_cast<uint32_t>(cg) * 16u;
   const __amdgpu_buffer_rsrc_t srs =
-      make_rsrc(a.state + (static_cast<long>(b) * a.Hv + static_cast<long>(g) * P) * (D * D), P * kHeadBytes);
+      make_rsrc(a.state + (static_cast<long>(sb) * a.Hv + static_cast<long>(g) * P) * (D * D), P * kHeadBytes);
   float4 hreg[R];
   if constexpr (MODE != kModeConv) {
 #pragma unroll
@@ -523,6 +527,8 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_generic(const Ker
   const int cg = (u >> 6) * CGL + (u & (CGL - 1));
   const int rg = (u & 63) / CGL;
   const int nch = (2 + G) * D;
+  const int sb = a.slots ? a.slots[b] : b;  // state slot (see gdn_step_fast)
+  if (sb < 0 || sb >= a.pool) return;
 
   float kq;
   if constexpr (MODE == kModeRec) {
@@ -541,7 +547,7 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_generic(const Ker
   } else {
     for (int c = t; c < nch; c += NT) {
       const long gc = unit_channel<D>(c, g, a.Hk, G);
-      const float v = conv_channel_generic<BF>(a, b, gc);
+      const float v = conv_channel_generic<BF>(a, b, sb, gc);
       if (c < D) s_q[c] = v;
       else if (c < 2 * D) s_k[c - D] = v;
       else {
@@ -580,7 +586,7 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_generic(const Ker
     const uint32_t voff = static_cast<uint32_t>(ph) * kHeadBytes + static_cast<uint32_t>(rg * R) * kRowBytes +
                           static_cast<uint32_t>(cg) * 16u;
     const __amdgpu_buffer_rsrc_t srs =
-        make_rsrc(a.state + (static_cast<long>(b) * a.Hv + static_cast<long>(g) * G) * (D * D),
+        make_rsrc(a.state + (static_cast<long>(sb) * a.Hv + static_cast<long>(g) * G) * (D * D),
                   static_cast<uint32_t>(G) * kHeadBytes);
     const int passes = G / P;
     for (int pass = 0; pass < passes; ++pass) {

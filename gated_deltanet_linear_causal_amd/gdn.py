@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "GdnShape", "make_shape", "library", "library_path",
-    "gdn_conv_update", "gdn_recurrent_step", "gdn_decode_layer", "gdn_sequence",
+    "gdn_conv_update", "gdn_recurrent_step", "gdn_decode_layer", "gdn_decode_layer_pooled", "gdn_sequence",
     "gdn_sequence_workspace_bytes", "gdn_status_string", "gdn_abi_version", "STATUS",
 ]
 
@@ -81,7 +81,9 @@ def library():
         lib.gdn_recurrent_step.argtypes = [S, P, P, P, P, P, P, P, P]
         lib.gdn_decode_layer.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.gdn_sequence.argtypes = [S, I32] + [P] * 12 + [ctypes.c_size_t, P]
-        for f in (lib.gdn_conv_update, lib.gdn_recurrent_step, lib.gdn_decode_layer, lib.gdn_sequence):
+        lib.gdn_decode_layer_pooled.argtypes = [S, I32] + [P] * 13
+        for f in (lib.gdn_conv_update, lib.gdn_recurrent_step, lib.gdn_decode_layer, lib.gdn_sequence,
+                  lib.gdn_decode_layer_pooled):
             f.restype = I32
         lib.gdn_sequence_workspace_bytes.argtypes = [S, I32]
         lib.gdn_sequence_workspace_bytes.restype = ctypes.c_size_t
@@ -174,6 +176,26 @@ def gdn_decode_layer(shape: GdnShape, conv1d_state, state, qkv, conv1d_weight, d
         _p(dt_bias, "dt_bias", torch.float32, Hv), _p(norm_weight, "norm_weight", torch.float32, dv),
         _p(out, "out", od, B * Hv * dv), _stream(stream))
     return _done(st, "gdn_decode_layer", check)
+
+
+def gdn_decode_layer_pooled(shape: GdnShape, slots, conv1d_state_pool, state_pool, qkv, conv1d_weight, dt_raw,
+                            b_raw, z, A_log, dt_bias, norm_weight, out, stream=None, check=True) -> int:
+    """gdn_decode_layer with the states in a pool: sequence b uses slot slots[b]
+    (int32 GPU tensor [B]; a slot outside the pool skips the sequence). The pool size
+    is taken from state_pool's first dimension."""
+    s = shape
+    act, od = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
+    B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
+    pool = int(state_pool.shape[0]) if isinstance(state_pool, torch.Tensor) else 0
+    st = library().gdn_decode_layer_pooled(
+        ctypes.byref(s), pool, _p(slots, "slots", torch.int32, B),
+        _p(conv1d_state_pool, "conv1d_state_pool", act, pool * (K - 1) * C),
+        _p(state_pool, "state_pool", torch.float32, pool * Hv * dk * dv), _p(qkv, "qkv", act, B * C),
+        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(dt_raw, "dt_raw", act, B * Hv),
+        _p(b_raw, "b_raw", act, B * Hv), _p(z, "z", act, B * Hv * dv), _p(A_log, "A_log", torch.float32, Hv),
+        _p(dt_bias, "dt_bias", torch.float32, Hv), _p(norm_weight, "norm_weight", torch.float32, dv),
+        _p(out, "out", od, B * Hv * dv), _stream(stream))
+    return _done(st, "gdn_decode_layer_pooled", check)
 
 
 def gdn_sequence(shape: GdnShape, T: int, conv1d_state, state, qkv, conv1d_weight, dt_raw, b_raw, z, A_log,

@@ -120,6 +120,25 @@ gdn_status_t gdn_decode_layer(const gdn_shape_t* shape, void* conv1d_state, floa
                               const float* dt_bias, const float* norm_weight, void* out,
                               void* stream);
 
+/* gdn_decode_layer for a batch whose states live in a pool (continuous batching).
+ * For callers that keep one state slot per live sequence and run a changing subset
+ * of them each step. Sequence b of the batch (its qkv, dt_raw, b_raw and z rows, and
+ * its out row) uses the conv state and recurrent state of pool slot slots[b]:
+ *   slots           [B] int32 (device): slot per sequence; a value outside
+ *                   [0, pool_size) marks an inactive sequence. Its slot is not touched
+ *                   and its out row is not written.
+ *   conv1d_state_pool [pool_size][K-1][C] act dtype, state_pool
+ *                   [pool_size][H_v][d_k][d_v] fp32; active slots are updated in place.
+ * The arithmetic is the same as gdn_decode_layer's. Two active sequences of one call
+ * must not share a slot: their updates would race (slot values are device data and
+ * are not checked on the host). Validation and errors are as for gdn_decode_layer,
+ * plus pool_size < 0 -> GDN_ERR_SHAPE. */
+gdn_status_t gdn_decode_layer_pooled(const gdn_shape_t* shape, int32_t pool_size, const int32_t* slots,
+                                     void* conv1d_state_pool, float* state_pool, const void* qkv,
+                                     const void* conv1d_weight, const void* dt_raw, const void* b_raw,
+                                     const void* z, const float* A_log, const float* dt_bias,
+                                     const float* norm_weight, void* out, void* stream);
+
 /* T consecutive tokens of gdn_decode_layer per sequence, with both states carried
  * from token to token (the rolled conv state of "ple.rs" serves prefill and decode
  * alike). Inputs are [B][T][...]: qkv [B][T][C], dt_raw and b_raw [B][T][H_v],

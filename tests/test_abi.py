@@ -179,3 +179,21 @@ def test_header_mentions_every_status():
     text = open(HEADER).read()
     for name in gdn.STATUS.values():
         assert name in text
+
+
+def test_pooled_validation():
+    s = qwen()
+    f = Fake()
+    args = [f() for _ in range(12)]  # slots, two pools, qkv, taps, dt, b, z, A_log, dt_bias, norm_w, out
+    lib = gdn.library()
+    assert lib.gdn_decode_layer_pooled(ctypes.byref(s), -1, *args, None) == SHAPE
+    bad = list(args)
+    bad[0] = ctypes.c_void_p(args[0].value + 2)  # slots must be 4-byte aligned
+    assert lib.gdn_decode_layer_pooled(ctypes.byref(s), 8, *bad, None) == ALIGN
+    bad = list(args)
+    bad[1] = None
+    assert lib.gdn_decode_layer_pooled(ctypes.byref(s), 8, *bad, None) == NULL
+    # an empty pool needs no state pointers and launches nothing
+    bad = list(args)
+    bad[1] = bad[2] = None
+    assert lib.gdn_decode_layer_pooled(ctypes.byref(s), 0, *bad, None) == OK

@@ -202,3 +202,45 @@ def test_error_leaves_buffers_untouched():
     torch.cuda.synchronize()
     assert torch.equal(dv.state, st0) and torch.equal(dv.conv_state, cs0)
     assert torch.all(out == 3.0)
+
+
+@pytest.mark.parametrize("name,Hk,Hv,d,K,act", [("qwen_fast", 16, 32, 128, 4, "bf16"),
+                                                 ("generic_K3_G3", 2, 6, 64, 3, "bf16"),
+                                                 ("tiny_f32", 2, 2, 32, 4, "f32")])
+def test_pooled_decode(name, Hk, Hv, d, K, act):
+    """gdn_decode_layer_pooled: sequence b uses pool slot slots[b]; slots outside the
+    pool skip the sequence (its out row and every other slot stay untouched)."""
+    pool, B = 10, 6
+    slots = np.array([7, 2, -1, 9, 0, 12], dtype=np.int32)
+    active = [b for b in range(B) if 0 <= slots[b] < pool]
+    cfg_pool = cfg_of(name, pool, Hk, Hv, d, K, act, steps=2)
+    pdata = I.generate(cfg_pool)  # pool states (batch = pool) and per-step inputs for B rows below
+    cfg = cfg_pool.with_(batch=B)
+    data = I.generate(cfg.with_(seed=cfg.seed + 1))
+    st_pool = GC.dev(pdata["state"], "f32")
+    cs_pool = GC.dev(pdata["conv_state"], act)
+    st0, cs0 = st_pool.clone(), cs_pool.clone()
+    dv_ = GC.DeviceInputs(cfg, data)
+    s = GC.shape_for(cfg)
+    slots_t = torch.from_numpy(slots).cuda()
+    out = torch.full((2, B, cfg.z_dim), 1234.5, device="cuda")
+    for t in range(2):
+        gdn.gdn_decode_layer_pooled(s, slots_t, cs_pool, st_pool, dv_.qkv[t], dv_.conv_w, dv_.a[t], dv_.b[t], dv_.z[t],
+                                    dv_.A_log, dv_.dt_bias, dv_.norm_w, out[t])
+    torch.cuda.synchronize()
+    # oracle on the gathered states of the active sequences
+    ref_data = dict(data)
+    ref_data["state"] = pdata["state"][slots[active]]
+    ref_data["conv_state"] = pdata["conv_state"][slots[active]]
+    for k_ in ("qkv", "z", "a", "b"):
+        ref_data[k_] = data[k_][:, active]
+    rcfg = cfg.with_(batch=len(active))
+    r_out, r_st, r_cs = GC.oracle_decode(rcfg, ref_data, 2)
+    GC.compare(name + " pooled out", GC.host_f64(out)[:, active], r_out, act)
+    GC.compare(name + " pooled state", GC.host_f64(st_pool)[slots[active]], r_st, act)
+    np.testing.assert_array_equal(GC.host_bits(cs_pool)[slots[active]], GC.conv_state_bits_expected(r_cs, act))
+    inactive = [b for b in range(B) if b not in active]
+    assert torch.all(out[:, inactive] == 1234.5)
+    untouched = [p for p in range(pool) if p not in slots[active]]
+    assert torch.equal(st_pool[untouched], st0[untouched])
+    assert torch.equal(cs_pool[untouched], cs0[untouched])
