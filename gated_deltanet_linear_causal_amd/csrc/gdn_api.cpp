@@ -22,6 +22,13 @@ namespace {
 #endif
 constexpr uint64_t kStreamStateBytes = GDN_STREAM_STATE_BYTES;
 
+// gdn_sequence switches from the token-by-token kernel to the chunked MFMA form at
+// this many tokens (one chunk).
+#ifndef GDN_CHUNKED_MIN_TOKENS
+#define GDN_CHUNKED_MIN_TOKENS 32
+#endif
+constexpr int32_t kChunkedMinTokens = GDN_CHUNKED_MIN_TOKENS;
+
 struct Buf {
   const void* p;
   size_t bytes;
@@ -339,6 +346,7 @@ gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_stat
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int d = shape->head_k_dim, G = a.G;
   (void)hipGetLastError();
+  if (T >= kChunkedMinTokens && gdn::chunked_supported(d, a.K)) return launched(gdn::launch_chunked_sequence(a, s));
   if (G <= 2 && a.K == 4) return launched(gdn::launch_sequence(d, G, a, s));
   // Shapes whose state or taps do not stay resident: one fused step launch per token.
   const size_t ea = z.ea, eo = z.eo;

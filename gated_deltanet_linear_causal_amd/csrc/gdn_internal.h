@@ -47,5 +47,9 @@ hipError_t launch_step(int mode, int d, int p, const KernelArgs& a, hipStream_t 
 // Multi-token kernel that keeps the state on chip for all T tokens; needs G == p
 // and K == 4.
 hipError_t launch_sequence(int d, int p, const KernelArgs& a, hipStream_t stream);
+// Chunked multi-token form on MFMA (gdn_chunked.hip): d == 128, K == 4, any G. One
+// workgroup per (sequence, v-head); enqueues the chunk kernel and the conv-state tail.
+bool chunked_supported(int d, int K);
+hipError_t launch_chunked_sequence(const KernelArgs& a, hipStream_t stream);
 
 }  // namespace gdn
