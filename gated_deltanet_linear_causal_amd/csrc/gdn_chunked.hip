@@ -41,6 +41,8 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 constexpr int kD = 128;   // head dim (d_k = d_v)
 constexpr int kC = 32;    // tokens per chunk
@@ -58,19 +60,89 @@ constexpr int kRawLd = 2 * kD + 4;
 // these operands go to fresh accumulators and are scaled back by 2^-15 in fp32.
 constexpr float kUp = 32768.0f, kDown = 1.0f / 32768.0f;
 
-struct ChunkSmem {
-  uint16_t q_hi[kC][kQKLd], q_lo[kC][kQKLd];
-  uint16_t k_hi[kC][kQKLd], k_lo[kC][kQKLd];
-  uint16_t kt_hi[kD][kKTLd], kt_lo[kD][kKTLd];
-  uint16_t p_hi[kC][kPLd], p_lo[kC][kPLd];
-  float a[kC][kALd];       // A, strictly lower
-  float raw[kC][kRawLd];   // silu(conv) of q (0..127) and k (128..255) before the L2 norm
-  float v[kC][kXLd];       // silu(conv) of v
-  float x[kC][kXLd];       // right-hand side, then Delta
-  float g[kC];             // running sum of log(alpha)
-  float beta[kC];
-  float ss[4][kC];         // per-wave partial sums of o^2
+constexpr int kUnits = 3 * kD;  // conv channels of a workgroup: q, k of its k-head, v of its v-head
+
+// Inputs of the next chunk, prefetched into LDS while the current chunk is solved
+// (bf16 activations only; with fp32 activations the inputs are read directly).
+template <bool BF>
+struct Staging {
+  uint32_t x[kC][kUnits / 2 + 4];  // conv inputs, two bf16 channels per word
+  uint32_t z[2][kC][kD / 2 + 4];   // z rows of this v-head, double-buffered by chunk parity
+  uint16_t dt[2][kC], br[2][kC];   // gate inputs
 };
+template <>
+struct Staging<false> {};
+
+template <bool BF>
+struct alignas(16) ChunkSmem {
+  alignas(16) uint16_t q_hi[kC][kQKLd], q_lo[kC][kQKLd];
+  alignas(16) uint16_t k_hi[kC][kQKLd], k_lo[kC][kQKLd];
+  alignas(16) uint16_t kt_hi[kD][kKTLd], kt_lo[kD][kKTLd];
+  union {
+    float raw[kC][kRawLd];  // silu(conv) of q (0..127) and k (128..255) before the L2 norm (steps 1-2)
+    struct {
+      alignas(16) float at[kC][kALd];  // -A transposed: at[s][t] = -A[t][s], zero for s >= t (steps 3-4)
+      float x[kC][kXLd];    // right-hand side, then Delta (steps 3-5)
+      uint16_t p_hi[kC][kPLd], p_lo[kC][kPLd];  // 2^15 P (steps 3-5)
+    } s;
+  } u;
+  float v[kC][kXLd];        // silu(conv) of v
+  float g[kC];              // running sum of log(alpha)
+  float beta[kC];
+  alignas(16) float ss[kC][4];  // per-wave partial sums of o^2
+  Staging<BF> st;
+};
+
+// Prefetch chunk `ch` (bf16 activations): conv inputs, z rows and gate inputs into
+// LDS. Done by NW waves, the calling one being number WV among them. Every load is a
+// wave-uniform row address plus the lane's dword, so a row of 64 dwords is one
+// coalesced 256-byte access. Rows of tokens past T (last chunk) repeat the last token:
+// the conv, the window update and the outputs of such tokens are masked, so their
+// values are never used.
+template <int NW, int WV>
+__device__ __forceinline__ void stage_chunk(Staging<true>& st, const KernelArgs& a, int b, int g, int h, int ch,
+                                            int lane) {
+  const int T = a.T, t0 = ch * kC, nt = min(kC, T - t0);
+  // Row strides and segment offsets in dwords, opaque to the optimiser so that the
+  // per-row offsets are recomputed here (a few scalar ops) instead of being hoisted
+  // out of the chunk loop into registers.
+  int cw = a.C / 2, zw = a.Hv * (kD / 2), hk = a.Hk;
+  asm volatile("" : "+s"(cw), "+s"(zw), "+s"(hk));
+  // conv rows: (token t, segment s) with s = 0 q, 1 k of k-head g, 2 v of v-head h
+  constexpr int kXPer = 3 * kC / NW, kZPer = kC / NW;
+  const uint32_t* xb = reinterpret_cast<const uint32_t*>(a.qkv) + (static_cast<long>(b) * T + t0) * cw + lane;
+  const uint32_t* zb = reinterpret_cast<const uint32_t*>(a.z) + (static_cast<long>(b) * T + t0) * zw + h * (kD / 2) + lane;
+  const int so[3] = {g * (kD / 2), (hk + g) * (kD / 2), (2 * hk + h) * (kD / 2)};
+  uint32_t xv[kXPer], zv[kZPer];
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int r = WV * kXPer + i, t = r / 3, sg = r - 3 * t;
+    xv[i] = xb[min(t, nt - 1) * cw + so[sg]];
+  }
+#pragma unroll
+  for (int i = 0; i < kZPer; ++i) {
+    const int t = WV * kZPer + i;
+    zv[i] = zb[min(t, nt - 1) * zw];
+  }
+  uint32_t dtv = 0, brv = 0;
+  if (WV == 0 && lane < nt) {
+    const long ai = (static_cast<long>(b) * T + t0 + lane) * a.Hv + h;
+    dtv = static_cast<const uint16_t*>(a.dt_raw)[ai];
+    brv = static_cast<const uint16_t*>(a.b_raw)[ai];
+  }
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int r = WV * kXPer + i, t = r / 3, sg = r - 3 * t;
+    st.x[t][sg * (kD / 2) + lane] = xv[i];
+  }
+  const int par = ch & 1;
+#pragma unroll
+  for (int i = 0; i < kZPer; ++i) st.z[par][WV * kZPer + i][lane] = zv[i];
+  if (WV == 0 && lane < kC) {
+    st.dt[par][lane] = static_cast<uint16_t>(dtv);
+    st.br[par][lane] = static_cast<uint16_t>(brv);
+  }
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t u) { return __uint_as_float(u << 16); }
 
@@ -89,7 +161,30 @@ __device__ __forceinline__ float raw_f32(uint32_t v) {
     return __uint_as_float(v);
 }
 
-__device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+// silu with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an IEEE divide
+__device__ __forceinline__ float silu(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
+
+// Cross-lane adds inside a row of 16 lanes via DPP (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+// sum over the 16 lanes of each row (every lane of the row gets it)
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+// total over the wave of a value already summed within each row of 16 lanes
+__device__ __forceinline__ float rows_total(float v) {
+  const int iv = __builtin_bit_cast(int, v);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48)));
+}
 __device__ __forceinline__ float softplus(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
 
 // x = hi + lo in fp16, both rounded to nearest: hi = fp16(x), lo = fp16(x - hi)
@@ -101,17 +196,25 @@ __device__ __forceinline__ void split1(float x, uint32_t& hi, uint32_t& lo) {
   hi = __builtin_bit_cast(uint16_t, h);
   lo = __builtin_bit_cast(uint16_t, r);
 }
+// two fp32 -> packed fp16 pairs (hi0 | hi1 << 16), (lo0 | lo1 << 16), same rounding as
+// split1 (v_cvt_pk_f16_f32 rounds to nearest even)
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const f32x2 x = {x0, x1};
+  const f16x2 h = __builtin_convertvector(x, f16x2);
+  const f32x2 back = __builtin_convertvector(h, f32x2);
+  const f32x2 res = {x0 - back[0], x1 - back[1]};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(res, f16x2));
+}
 // four fp32 -> (hi pair, hi pair), (lo pair, lo pair)
 __device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo) {
-  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-  split1(x[0], h0, l0);
-  split1(x[1], h1, l1);
-  split1(x[2], h2, l2);
-  split1(x[3], h3, l3);
-  hi[0] = h0 | (h1 << 16);
-  hi[1] = h2 | (h3 << 16);
-  lo[0] = l0 | (l1 << 16);
-  lo[1] = l2 | (l3 << 16);
+  uint32_t h0, h1, l0, l1;
+  split2(x[0], x[1], h0, l0);
+  split2(x[2], x[3], h1, l1);
+  hi[0] = h0;
+  hi[1] = h1;
+  lo[0] = l0;
+  lo[1] = l1;
 }
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
@@ -163,15 +266,9 @@ __device__ __forceinline__ void put_split(uint16_t* hi_plane, uint16_t* lo_plane
   lo_plane[idx] = static_cast<uint16_t>(l);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
 template <bool BF>
 __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
-  __shared__ ChunkSmem sm;
+  __shared__ ChunkSmem<BF> sm;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, q = l >> 4, c16 = l & 15;
   const int b = blockIdx.x / a.Hv;
@@ -197,7 +294,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
   gch[0] = (tid < kD) ? static_cast<long>(g) * kD + tid : static_cast<long>(a.Hk) * kD + static_cast<long>(g) * kD + (tid - kD);
   gch[1] = 2L * a.Hk * kD + static_cast<long>(h) * kD + tid;  // valid when two
   float wt[2][4];
-  uint32_t win[2][3];
+  float win[2][3];  // the channel's last three inputs (exact widening of the stored values)
   const long cs0 = static_cast<long>(b) * 3 * C;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -205,46 +302,76 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) wt[m][j] = raw_f32<BF>(load_raw<BF>(a.conv_w, gch[m] * 4 + j));
 #pragma unroll
-    for (int j = 0; j < 3; ++j) win[m][j] = load_raw<BF>(a.conv_state, cs0 + j * C + gch[m]);
+    for (int j = 0; j < 3; ++j) win[m][j] = raw_f32<BF>(load_raw<BF>(a.conv_state, cs0 + j * C + gch[m]));
   }
   const float A_exp = __expf(a.A_log[h]);
   const float dt_bias = a.dt_bias[h];
   const float rsd = 1.0f / sqrtf(static_cast<float>(kD));
+  const float nw[2] = {a.norm_w[32 * w + c16], a.norm_w[32 * w + 16 + c16]};  // norm weights of the output columns
 
   const int nchunks = (T + kC - 1) / kC;
+  if constexpr (BF) {
+    if (nchunks > 0) {
+      switch (__builtin_amdgcn_readfirstlane(w)) {
+        case 0: stage_chunk<4, 0>(sm.st, a, b, g, h, 0, l); break;
+        case 1: stage_chunk<4, 1>(sm.st, a, b, g, h, 0, l); break;
+        case 2: stage_chunk<4, 2>(sm.st, a, b, g, h, 0, l); break;
+        default: stage_chunk<4, 3>(sm.st, a, b, g, h, 0, l); break;
+      }
+    }
+    __syncthreads();
+  }
   for (int ch = 0; ch < nchunks; ++ch) {
     const int t0 = ch * kC;
     const int nt = min(kC, T - t0);
+    const int par = ch & 1;
+    // lane indices re-derived per chunk (opaque to the optimiser), so that the many
+    // lane-dependent LDS addresses are recomputed instead of held across the loop
+    int tid_ = tid;
+    asm volatile("" : "+v"(tid_));
+    const int tid = tid_;
+    const int w = tid >> 6, l = tid & 63, q = l >> 4, c16 = l & 15;
 
     // ---- 1. conv + SiLU of this chunk's tokens, gates
     {
-      constexpr int kTB = 8;  // tokens loaded per batch of loads
+      // one token of channel m of this lane: x is the new input
+      auto conv_token = [&](int m, int t, float xf) {
+        float u = wt[m][0] * win[m][0];
+        u = fmaf(wt[m][1], win[m][1], u);
+        u = fmaf(wt[m][2], win[m][2], u);
+        u = fmaf(wt[m][3], xf, u);
+        const float val = (t < nt) ? silu(u) : 0.0f;
+        if (m == 0)
+          sm.u.raw[t][tid] = val;
+        else
+          sm.v[t][tid] = val;
+        if (t < nt) {
+          win[m][0] = win[m][1];
+          win[m][1] = win[m][2];
+          win[m][2] = xf;
+        }
+      };
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         if (m == 1 && !two) break;
+        if constexpr (BF) {
+          // inputs staged in LDS: unit u = 256 m + tid is half (u & 1) of word u / 2
+          const int pw = (m * kNT + tid) >> 1, sh = 16 * (tid & 1);
+          uint32_t xw[kC];  // all reads issued before the first use
+#pragma unroll
+          for (int t = 0; t < kC; ++t) xw[t] = sm.st.x[t][pw];
+#pragma unroll
+          for (int t = 0; t < kC; ++t) conv_token(m, t, bf16_to_f32((xw[t] >> sh) & 0xffffu));
+        } else {
+          constexpr int kTB = 8;  // tokens loaded per batch of loads
 #pragma unroll 1
-        for (int tb = 0; tb < kC; tb += kTB) {
-          uint32_t xv[kTB];
+          for (int tb = 0; tb < kC; tb += kTB) {
+            uint32_t xv[kTB];
 #pragma unroll
-          for (int e = 0; e < kTB; ++e)
-            xv[e] = (tb + e < nt) ? load_raw<BF>(a.qkv, (static_cast<long>(b) * T + t0 + tb + e) * C + gch[m]) : 0u;
+            for (int e = 0; e < kTB; ++e)
+              xv[e] = (tb + e < nt) ? load_raw<BF>(a.qkv, (static_cast<long>(b) * T + t0 + tb + e) * C + gch[m]) : 0u;
 #pragma unroll
-          for (int e = 0; e < kTB; ++e) {
-            const int t = tb + e;
-            float u = wt[m][0] * raw_f32<BF>(win[m][0]);
-            u = fmaf(wt[m][1], raw_f32<BF>(win[m][1]), u);
-            u = fmaf(wt[m][2], raw_f32<BF>(win[m][2]), u);
-            u = fmaf(wt[m][3], raw_f32<BF>(xv[e]), u);
-            const float val = (t < nt) ? silu(u) : 0.0f;
-            if (m == 0)
-              sm.raw[t][tid] = val;
-            else
-              sm.v[t][tid] = val;
-            if (t < nt) {
-              win[m][0] = win[m][1];
-              win[m][1] = win[m][2];
-              win[m][2] = xv[e];
-            }
+            for (int e = 0; e < kTB; ++e) conv_token(m, tb + e, raw_f32<BF>(xv[e]));
           }
         }
       }
@@ -252,9 +379,15 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         // lanes 0..31: one token each; inclusive scan of log(alpha)
         float la = 0.0f, bt = 0.0f;
         if (l < nt) {
-          const long ai = (static_cast<long>(b) * T + t0 + l) * a.Hv + h;
-          const float dt = raw_f32<BF>(load_raw<BF>(a.dt_raw, ai));
-          const float br = raw_f32<BF>(load_raw<BF>(a.b_raw, ai));
+          float dt, br;
+          if constexpr (BF) {
+            dt = bf16_to_f32(sm.st.dt[par][l]);
+            br = bf16_to_f32(sm.st.br[par][l]);
+          } else {
+            const long ai = (static_cast<long>(b) * T + t0 + l) * a.Hv + h;
+            dt = raw_f32<BF>(load_raw<BF>(a.dt_raw, ai));
+            br = raw_f32<BF>(load_raw<BF>(a.b_raw, ai));
+          }
           la = -A_exp * softplus(dt + dt_bias);
           bt = 1.0f / (1.0f + __expf(-br));
         }
@@ -271,21 +404,61 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     }
     __syncthreads();
 
-    // ---- 2. L2 norms of q and k; split planes [t][i] and [i][t]
+    // ---- 2. L2 norms of q and k; split planes [t][i] and [i][t]. Wave w takes tokens
+    // 8w .. 8w+7, lane l channels 2l and 2l+1; the 16 reductions run side by side.
+    {
+      constexpr int kTW = kC / 4;
+      const int tb = w * kTW;
+      float2 qv[kTW], kv[kTW];
+      float ss[2 * kTW];
 #pragma unroll
-    for (int tt = 0; tt < kC / 4; ++tt) {
-      const int t = w * (kC / 4) + tt;
-      const float q0 = sm.raw[t][2 * l], q1 = sm.raw[t][2 * l + 1];
-      const float k0 = sm.raw[t][kD + 2 * l], k1 = sm.raw[t][kD + 2 * l + 1];
-      const float sq = wave_sum(q0 * q0 + q1 * q1);
-      const float sk = wave_sum(k0 * k0 + k1 * k1);
-      const float rq = 1.0f / sqrtf(sq + a.l2_eps), rk = 1.0f / sqrtf(sk + a.l2_eps);
-      put_split(&sm.q_hi[0][0], &sm.q_lo[0][0], t * kQKLd + 2 * l, q0 * rq * kUp);
-      put_split(&sm.q_hi[0][0], &sm.q_lo[0][0], t * kQKLd + 2 * l + 1, q1 * rq * kUp);
-      put_split(&sm.k_hi[0][0], &sm.k_lo[0][0], t * kQKLd + 2 * l, k0 * rk * kUp);
-      put_split(&sm.k_hi[0][0], &sm.k_lo[0][0], t * kQKLd + 2 * l + 1, k1 * rk * kUp);
-      put_split(&sm.kt_hi[0][0], &sm.kt_lo[0][0], (2 * l) * kKTLd + t, k0 * rk);
-      put_split(&sm.kt_hi[0][0], &sm.kt_lo[0][0], (2 * l + 1) * kKTLd + t, k1 * rk);
+      for (int tt = 0; tt < kTW; ++tt) {
+        qv[tt] = *reinterpret_cast<const float2*>(&sm.u.raw[tb + tt][2 * l]);
+        kv[tt] = *reinterpret_cast<const float2*>(&sm.u.raw[tb + tt][kD + 2 * l]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < kTW; ++tt) {
+        ss[2 * tt] = qv[tt].x * qv[tt].x + qv[tt].y * qv[tt].y;
+        ss[2 * tt + 1] = kv[tt].x * kv[tt].x + kv[tt].y * kv[tt].y;
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * kTW; ++i) ss[i] += dpp<0xB1>(ss[i]);
+#pragma unroll
+      for (int i = 0; i < 2 * kTW; ++i) ss[i] += dpp<0x4E>(ss[i]);
+#pragma unroll
+      for (int i = 0; i < 2 * kTW; ++i) ss[i] += dpp<0x141>(ss[i]);
+#pragma unroll
+      for (int i = 0; i < 2 * kTW; ++i) ss[i] += dpp<0x140>(ss[i]);
+#pragma unroll
+      for (int i = 0; i < 2 * kTW; ++i) ss[i] = __builtin_amdgcn_rsqf(rows_total(ss[i]) + a.l2_eps);
+      float kn[2][kTW];  // normalised k of channels 2l, 2l+1
+#pragma unroll
+      for (int tt = 0; tt < kTW; ++tt) {
+        const int t = tb + tt;
+        const float rq = ss[2 * tt], rk = ss[2 * tt + 1];
+        uint32_t h, lo;
+        split2(qv[tt].x * rq * kUp, qv[tt].y * rq * kUp, h, lo);
+        *reinterpret_cast<uint32_t*>(&sm.q_hi[t][2 * l]) = h;
+        *reinterpret_cast<uint32_t*>(&sm.q_lo[t][2 * l]) = lo;
+        kn[0][tt] = kv[tt].x * rk;
+        kn[1][tt] = kv[tt].y * rk;
+        split2(kn[0][tt] * kUp, kn[1][tt] * kUp, h, lo);
+        *reinterpret_cast<uint32_t*>(&sm.k_hi[t][2 * l]) = h;
+        *reinterpret_cast<uint32_t*>(&sm.k_lo[t][2 * l]) = lo;
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        u32x4 hv, lv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t h, lo;
+          split2(kn[c][2 * e], kn[c][2 * e + 1], h, lo);
+          hv[e] = h;
+          lv[e] = lo;
+        }
+        *reinterpret_cast<u32x4*>(&sm.kt_hi[2 * l + c][tb]) = hv;
+        *reinterpret_cast<u32x4*>(&sm.kt_lo[2 * l + c][tb]) = lv;
+      }
     }
     __syncthreads();
 
@@ -310,8 +483,8 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         const float dg = sm.g[t] - sm.g[s];
         const float e = (s <= t) ? __expf(dg) : 0.0f;
         // kk and qk carry the 2^15 x 2^15 operand scale
-        sm.a[t][s] = (s < t) ? sm.beta[t] * e * (kk[r] * (kDown * kDown)) : 0.0f;
-        put_split(&sm.p_hi[0][0], &sm.p_lo[0][0], t * kPLd + s, e * (qk[r] * kDown));  // = 2^15 P
+        sm.u.s.at[s][t] = (s < t) ? -(sm.beta[t] * e * (kk[r] * (kDown * kDown))) : 0.0f;
+        put_split(&sm.u.s.p_hi[0][0], &sm.u.s.p_lo[0][0], t * kPLd + s, e * (qk[r] * kDown));  // = 2^15 P
       }
     }
 
@@ -352,23 +525,38 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * tt + 4 * q + r, j = 32 * w + 16 * jt + c16;
           const float gam = __expf(sm.g[t]);
-          sm.x[t][j] = sm.beta[t] * (sm.v[t][j] - gam * (kh[tt][jt][r] * kDown));
+          sm.u.s.x[t][j] = sm.beta[t] * (sm.v[t][j] - gam * (kh[tt][jt][r] * kDown));
           oacc[tt][jt][r] = gam * (qh[tt][jt][r] * kDown);
         }
     __syncthreads();
 
-    // ---- 4. forward substitution: (I + A) Delta = rhs, one lane per column j
+    // ---- 4. forward substitution (I + A) Delta = rhs, one lane per column j, in
+    // right-looking order: once delta_s is final it is eliminated from every later row,
+    // so the updates of different rows are independent.
     if (tid < kD) {
       float d[kC];
 #pragma unroll
-      for (int t = 0; t < kC; ++t) {
-        float acc = sm.x[t][tid];
+      for (int t = 0; t < kC; ++t) d[t] = sm.u.s.x[t][tid];
 #pragma unroll
-        for (int s = 0; s < t; ++s) acc = fmaf(-sm.a[t][s], d[s], acc);
-        d[t] = acc;
+      for (int s = 0; s < kC - 1; ++s) {
+#pragma unroll
+        for (int t4 = (s + 1) / 4; t4 < kC / 4; ++t4) {
+          const f32x4 m = *reinterpret_cast<const f32x4*>(&sm.u.s.at[s][4 * t4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * t4 + e > s) d[4 * t4 + e] = fmaf(m[e], d[s], d[4 * t4 + e]);
+        }
       }
 #pragma unroll
-      for (int t = 0; t < kC; ++t) sm.x[t][tid] = d[t];
+      for (int t = 0; t < kC; ++t) sm.u.s.x[t][tid] = d[t];
+    } else if constexpr (BF) {
+      // waves 2-3 prefetch the next chunk's inputs meanwhile
+      if (ch + 1 < nchunks) {
+        if (__builtin_amdgcn_readfirstlane(w) == 2)
+          stage_chunk<2, 0>(sm.st, a, b, g, h, ch + 1, l);
+        else
+          stage_chunk<2, 1>(sm.st, a, b, g, h, ch + 1, l);
+      }
     }
     __syncthreads();
 
@@ -383,8 +571,8 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int s0 = 4 * q + r, s1 = 16 + 4 * q + r;
-          top[r] = sm.x[s0][j];
-          bot[r] = sm.x[s1][j];
+          top[r] = sm.u.s.x[s0][j];
+          bot[r] = sm.u.s.x[s1][j];
           top2[r] = __expf(gC - sm.g[s0]) * top[r];
           bot2[r] = __expf(gC - sm.g[s1]) * bot[r];
         }
@@ -393,8 +581,8 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         bfrag(top2, bot2, eh, el);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const u32x4 ph = frag(&sm.p_hi[0][0], kPLd, 16 * tt + c16, 0, q);
-          const u32x4 pl = frag(&sm.p_lo[0][0], kPLd, 16 * tt + c16, 0, q);
+          const u32x4 ph = frag(&sm.u.s.p_hi[0][0], kPLd, 16 * tt + c16, 0, q);
+          const u32x4 pl = frag(&sm.u.s.p_lo[0][0], kPLd, 16 * tt + c16, 0, q);
           const f32x4 pd = mfma3(ph, pl, dh, dl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});  // 2^15 P Delta
 #pragma unroll
           for (int r = 0; r < 4; ++r) oacc[tt][jt][r] = fmaf(pd[r], kDown, oacc[tt][jt][r]);
@@ -421,13 +609,12 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
           float v = 0.0f;
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) v += oacc[tt][jt][r] * oacc[tt][jt][r];
-#pragma unroll
-          for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 64);
+          v = row16_sum(v);
           s4[r] = v;
         }
         if (c16 == 0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sm.ss[w][16 * tt + 4 * q + r] = s4[r];
+          for (int r = 0; r < 4; ++r) sm.ss[16 * tt + 4 * q + r][w] = s4[r];
         }
       }
       __syncthreads();
@@ -438,14 +625,19 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * tt + 4 * q + r;
           if (t < nt) {
-            const float tot = (sm.ss[0][t] + sm.ss[1][t] + sm.ss[2][t] + sm.ss[3][t]) * (rsd * rsd);
-            const float rr = 1.0f / sqrtf(tot / static_cast<float>(kD) + a.rms_eps);
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(&sm.ss[t][0]);
+            const float tot = (sv[0] + sv[1] + sv[2] + sv[3]) * (rsd * rsd);
+            const float rr = __builtin_amdgcn_rsqf(tot * (1.0f / kD) + a.rms_eps);
             const long row = (static_cast<long>(b) * T + t0 + t) * zrow + static_cast<long>(h) * kD;
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
               const int j = 32 * w + 16 * jt + c16;
-              const float zz = raw_f32<BF>(load_raw<BF>(a.z, row + j));
-              const float y = oacc[tt][jt][r] * rsd * rr * a.norm_w[j] * silu(zz);
+              float zz;
+              if constexpr (BF)
+                zz = bf16_to_f32((sm.st.z[par][t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+              else
+                zz = raw_f32<BF>(load_raw<BF>(a.z, row + j));
+              const float y = oacc[tt][jt][r] * rsd * rr * nw[jt] * silu(zz);
               if (a.out_bf16) {
                 uint32_t u = __float_as_uint(y);
                 u += 0x7fffu + ((u >> 16) & 1u);
