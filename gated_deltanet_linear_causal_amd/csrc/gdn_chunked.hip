@@ -61,14 +61,18 @@ constexpr int kRawLd = 2 * kD + 4;
 constexpr float kUp = 32768.0f, kDown = 1.0f / 32768.0f;
 
 constexpr int kUnits = 3 * kD;  // conv channels of a workgroup: q, k of its k-head, v of its v-head
+constexpr int kPairs = kUnits / 2;  // bf16 channel pairs (one dword each)
+constexpr int kTaps = 4;             // conv taps (K)
 
 // Inputs of the next chunk, prefetched into LDS while the current chunk is solved
-// (bf16 activations only; with fp32 activations the inputs are read directly).
+// (bf16 activations only; with fp32 activations the inputs are read directly). Row
+// j of x holds the conv inputs of token j - 3 of the chunk: rows 0..2 are the three
+// inputs before it (the conv state for the first chunk), so every conv output of the
+// chunk can be formed from LDS alone.
 template <bool BF>
 struct Staging {
-  uint32_t x[kC][kUnits / 2 + 4];  // conv inputs, two bf16 channels per word
-  uint32_t z[2][kC][kD / 2 + 4];   // z rows of this v-head, double-buffered by chunk parity
-  uint16_t dt[2][kC], br[2][kC];   // gate inputs
+  uint32_t x[kC + kTaps - 1][kPairs + 4];  // two bf16 channels per word
+  uint32_t z[2][kC][kD / 2 + 4];           // z rows of this v-head, double-buffered by chunk parity
 };
 template <>
 struct Staging<false> {};
@@ -87,21 +91,31 @@ struct alignas(16) ChunkSmem {
     } s;
   } u;
   float v[kC][kXLd];        // silu(conv) of v
-  float g[kC];              // running sum of log(alpha)
-  float beta[kC];
+  float g[2][kC];           // running sum of log(alpha) inside the chunk, by chunk parity
+  float beta[2][kC];
   alignas(16) float ss[kC][4];  // per-wave partial sums of o^2
   Staging<BF> st;
 };
 
-// Prefetch chunk `ch` (bf16 activations): conv inputs, z rows and gate inputs into
-// LDS. Done by NW waves, the calling one being number WV among them. Every load is a
-// wave-uniform row address plus the lane's dword, so a row of 64 dwords is one
-// coalesced 256-byte access. Rows of tokens past T (last chunk) repeat the last token:
-// the conv, the window update and the outputs of such tokens are masked, so their
-// values are never used.
+// Gates of the tokens of chunk `ch`, computed by one wave (lanes 0..31, one token
+// each): beta_t = sigmoid(b_t) and the inclusive running sum over the chunk of
+// log(alpha_t) = -exp(A_log) softplus(dt_t + dt_bias). Tokens past T get 0 and 0.
+template <bool BF>
+__device__ __forceinline__ void chunk_gates(const KernelArgs& a, int b, int h, int ch, int lane, float A_exp,
+                                            float dt_bias, float* g_out, float* beta_out);
+
+// Prefetch chunk `ch` (bf16 activations): conv inputs and z rows into LDS, and the
+// chunk's gates. Done by NW waves, the calling one being number WV among them. Every
+// load is a wave-uniform row address plus the lane's dword, so a row of 64 dwords is
+// one coalesced 256-byte access. Rows of tokens past T (last chunk) repeat the last
+// token: the conv outputs and the outputs of such tokens are masked, so their values
+// are never used. With `first`, rows 0..2 come from the conv state; otherwise the last
+// wave first moves the previous chunk's last three rows there (it is the wave that
+// overwrites them, and a wave's LDS accesses complete in order).
 template <int NW, int WV>
-__device__ __forceinline__ void stage_chunk(Staging<true>& st, const KernelArgs& a, int b, int g, int h, int ch,
-                                            int lane) {
+__device__ __forceinline__ void stage_chunk(ChunkSmem<true>& sm, const KernelArgs& a, int b, int g, int h, int ch,
+                                            int lane, bool first, float A_exp, float dt_bias) {
+  Staging<true>& st = sm.st;
   const int T = a.T, t0 = ch * kC, nt = min(kC, T - t0);
   // Row strides and segment offsets in dwords, opaque to the optimiser so that the
   // per-row offsets are recomputed here (a few scalar ops) instead of being hoisted
@@ -124,24 +138,31 @@ __device__ __forceinline__ void stage_chunk(Staging<true>& st, const KernelArgs&
     const int t = WV * kZPer + i;
     zv[i] = zb[min(t, nt - 1) * zw];
   }
-  uint32_t dtv = 0, brv = 0;
-  if (WV == 0 && lane < nt) {
-    const long ai = (static_cast<long>(b) * T + t0 + lane) * a.Hv + h;
-    dtv = static_cast<const uint16_t*>(a.dt_raw)[ai];
-    brv = static_cast<const uint16_t*>(a.b_raw)[ai];
+  constexpr int kHist = (kTaps - 1) * 3;  // history rows x segments
+  if (first) {
+    // conv state rows 0..2 ([B][K-1][C], same channel layout as a qkv row)
+    const uint32_t* cb = reinterpret_cast<const uint32_t*>(a.conv_state) + static_cast<long>(b) * (kTaps - 1) * cw + lane;
+#pragma unroll
+    for (int r = WV; r < kHist; r += NW) {
+      const int j = r / 3, sg = r - 3 * j;
+      st.x[j][sg * (kD / 2) + lane] = cb[j * cw + so[sg]];
+    }
+  } else if (WV == NW - 1) {
+    uint32_t hist[kHist];
+#pragma unroll
+    for (int r = 0; r < kHist; ++r) hist[r] = st.x[kC + r / 3][(r % 3) * (kD / 2) + lane];
+#pragma unroll
+    for (int r = 0; r < kHist; ++r) st.x[r / 3][(r % 3) * (kD / 2) + lane] = hist[r];
   }
+  if (WV == 0) chunk_gates<true>(a, b, h, ch, lane, A_exp, dt_bias, sm.g[ch & 1], sm.beta[ch & 1]);
 #pragma unroll
   for (int i = 0; i < kXPer; ++i) {
     const int r = WV * kXPer + i, t = r / 3, sg = r - 3 * t;
-    st.x[t][sg * (kD / 2) + lane] = xv[i];
+    st.x[kTaps - 1 + t][sg * (kD / 2) + lane] = xv[i];
   }
   const int par = ch & 1;
 #pragma unroll
   for (int i = 0; i < kZPer; ++i) st.z[par][WV * kZPer + i][lane] = zv[i];
-  if (WV == 0 && lane < kC) {
-    st.dt[par][lane] = static_cast<uint16_t>(dtv);
-    st.br[par][lane] = static_cast<uint16_t>(brv);
-  }
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t u) { return __uint_as_float(u << 16); }
@@ -186,6 +207,29 @@ __device__ __forceinline__ float rows_total(float v) {
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48)));
 }
 __device__ __forceinline__ float softplus(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
+
+template <bool BF>
+__device__ __forceinline__ void chunk_gates(const KernelArgs& a, int b, int h, int ch, int lane, float A_exp,
+                                            float dt_bias, float* g_out, float* beta_out) {
+  const int t0 = ch * kC, nt = min(kC, a.T - t0);
+  float la = 0.0f, bt = 0.0f;
+  if (lane < nt) {
+    const long ai = (static_cast<long>(b) * a.T + t0 + lane) * a.Hv + h;
+    const float dt = raw_f32<BF>(load_raw<BF>(a.dt_raw, ai));
+    const float br = raw_f32<BF>(load_raw<BF>(a.b_raw, ai));
+    la = -A_exp * softplus(dt + dt_bias);
+    bt = 1.0f / (1.0f + __expf(-br));
+  }
+#pragma unroll
+  for (int off = 1; off < kC; off <<= 1) {
+    const float o = __shfl_up(la, off, 64);
+    if (lane >= off) la += o;
+  }
+  if (lane < kC) {
+    g_out[lane] = la;
+    beta_out[lane] = bt;
+  }
+}
 
 // x = hi + lo in fp16, both rounded to nearest: hi = fp16(x), lo = fp16(x - hi)
 // (x - hi is exact in fp32). 11 + 11 significant bits: |x - hi - lo| <= 2^-22 |x|
@@ -287,36 +331,53 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) hacc[it][jt][r] = hst[(16 * it + 4 * q + r) * kD + 32 * w + 16 * jt + c16];
 
-  // ---- conv channels of this lane: unit index u = tid (and tid + 256 when < 384);
-  // [0,128) q of k-head g, [128,256) k of k-head g, [256,384) v of v-head h
-  const bool two = tid < 128;
-  long gch[2];
-  gch[0] = (tid < kD) ? static_cast<long>(g) * kD + tid : static_cast<long>(a.Hk) * kD + static_cast<long>(g) * kD + (tid - kD);
-  gch[1] = 2L * a.Hk * kD + static_cast<long>(h) * kD + tid;  // valid when two
-  float wt[2][4];
-  float win[2][3];  // the channel's last three inputs (exact widening of the stored values)
-  const long cs0 = static_cast<long>(b) * 3 * C;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    if (m == 1 && !two) break;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wt[m][j] = raw_f32<BF>(load_raw<BF>(a.conv_w, gch[m] * 4 + j));
-#pragma unroll
-    for (int j = 0; j < 3; ++j) win[m][j] = raw_f32<BF>(load_raw<BF>(a.conv_state, cs0 + j * C + gch[m]));
-  }
   const float A_exp = __expf(a.A_log[h]);
   const float dt_bias = a.dt_bias[h];
   const float rsd = 1.0f / sqrtf(static_cast<float>(kD));
   const float nw[2] = {a.norm_w[32 * w + c16], a.norm_w[32 * w + 16 + c16]};  // norm weights of the output columns
 
+  // ---- conv weights of this lane's channels. Unit channel c of the workgroup:
+  // [0,128) q of k-head g, [128,256) k of k-head g, [256,384) v of v-head h.
+  // bf16: lane takes 3 work units u = tid + 256 i, each the channel pair p = u % 192
+  // (unit channels 2p, 2p+1) over the 8 tokens 8 (u / 192) .. +7 of a chunk.
+  // fp32: lane takes unit channel tid, and tid + 256 when below 384, over all tokens.
+  constexpr int kCU = BF ? 3 : 2;  // work units (bf16) or channels (fp32) of a lane
+  constexpr int kCW = BF ? 2 : 1;  // channels per unit
+  float wt[kCU][kCW][kTaps];
+  auto unit_channel = [&](int c) -> long {  // unit channel -> channel of the qkv row
+    return c < kD ? static_cast<long>(g) * kD + c
+                  : (c < 2 * kD ? static_cast<long>(a.Hk + g) * kD + (c - kD)
+                                : static_cast<long>(2 * a.Hk + h) * kD + (c - 2 * kD));
+  };
+#pragma unroll
+  for (int i = 0; i < kCU; ++i) {
+    const int c0 = BF ? 2 * ((tid + kNT * i) % kPairs) : min(tid + kNT * i, kUnits - 1);
+#pragma unroll
+    for (int e = 0; e < kCW; ++e) {
+      const long gc = unit_channel(c0 + e);
+#pragma unroll
+      for (int j = 0; j < kTaps; ++j) wt[i][e][j] = raw_f32<BF>(load_raw<BF>(a.conv_w, gc * kTaps + j));
+    }
+  }
+  float win[2][kTaps - 1];  // fp32: the channel's last three inputs
+  if constexpr (!BF) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const long gc = unit_channel(min(tid + kNT * m, kUnits - 1));
+#pragma unroll
+      for (int j = 0; j < kTaps - 1; ++j)
+        win[m][j] = raw_f32<BF>(load_raw<BF>(a.conv_state, (static_cast<long>(b) * (kTaps - 1) + j) * C + gc));
+    }
+  }
+
   const int nchunks = (T + kC - 1) / kC;
   if constexpr (BF) {
     if (nchunks > 0) {
       switch (__builtin_amdgcn_readfirstlane(w)) {
-        case 0: stage_chunk<4, 0>(sm.st, a, b, g, h, 0, l); break;
-        case 1: stage_chunk<4, 1>(sm.st, a, b, g, h, 0, l); break;
-        case 2: stage_chunk<4, 2>(sm.st, a, b, g, h, 0, l); break;
-        default: stage_chunk<4, 3>(sm.st, a, b, g, h, 0, l); break;
+        case 0: stage_chunk<4, 0>(sm, a, b, g, h, 0, l, true, A_exp, dt_bias); break;
+        case 1: stage_chunk<4, 1>(sm, a, b, g, h, 0, l, true, A_exp, dt_bias); break;
+        case 2: stage_chunk<4, 2>(sm, a, b, g, h, 0, l, true, A_exp, dt_bias); break;
+        default: stage_chunk<4, 3>(sm, a, b, g, h, 0, l, true, A_exp, dt_bias); break;
       }
     }
     __syncthreads();
@@ -332,75 +393,66 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     const int tid = tid_;
     const int w = tid >> 6, l = tid & 63, q = l >> 4, c16 = l & 15;
 
-    // ---- 1. conv + SiLU of this chunk's tokens, gates
-    {
-      // one token of channel m of this lane: x is the new input
-      auto conv_token = [&](int m, int t, float xf) {
-        float u = wt[m][0] * win[m][0];
-        u = fmaf(wt[m][1], win[m][1], u);
-        u = fmaf(wt[m][2], win[m][2], u);
-        u = fmaf(wt[m][3], xf, u);
-        const float val = (t < nt) ? silu(u) : 0.0f;
-        if (m == 0)
-          sm.u.raw[t][tid] = val;
-        else
-          sm.v[t][tid] = val;
-        if (t < nt) {
-          win[m][0] = win[m][1];
-          win[m][1] = win[m][2];
-          win[m][2] = xf;
+    // ---- 1. conv + SiLU of this chunk's tokens (and, fp32, the gates)
+    if constexpr (BF) {
+#pragma unroll
+      for (int i = 0; i < kCU; ++i) {
+        const int u = tid + kNT * i, p = u % kPairs, t8 = 8 * (u / kPairs);
+        float xl[8 + kTaps - 1], xh[8 + kTaps - 1];  // inputs of channels 2p, 2p+1
+#pragma unroll
+        for (int j = 0; j < 8 + kTaps - 1; ++j) {
+          const uint32_t wv = sm.st.x[t8 + j][p];
+          xl[j] = bf16_to_f32(wv & 0xffffu);
+          xh[j] = __uint_as_float(wv & 0xffff0000u);
         }
-      };
+        float* dst = p < kD ? &sm.u.raw[0][2 * p] : &sm.v[0][2 * p - 2 * kD];
+        const int ld = p < kD ? kRawLd : kXLd;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float u0 = wt[i][0][0] * xl[e], u1 = wt[i][1][0] * xh[e];
+#pragma unroll
+          for (int j = 1; j < kTaps; ++j) {
+            u0 = fmaf(wt[i][0][j], xl[e + j], u0);
+            u1 = fmaf(wt[i][1][j], xh[e + j], u1);
+          }
+          const bool live = t8 + e < nt;
+          *reinterpret_cast<f32x2*>(dst + (t8 + e) * ld) = f32x2{live ? silu(u0) : 0.0f, live ? silu(u1) : 0.0f};
+        }
+      }
+    } else {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        if (m == 1 && !two) break;
-        if constexpr (BF) {
-          // inputs staged in LDS: unit u = 256 m + tid is half (u & 1) of word u / 2
-          const int pw = (m * kNT + tid) >> 1, sh = 16 * (tid & 1);
-          uint32_t xw[kC];  // all reads issued before the first use
-#pragma unroll
-          for (int t = 0; t < kC; ++t) xw[t] = sm.st.x[t][pw];
-#pragma unroll
-          for (int t = 0; t < kC; ++t) conv_token(m, t, bf16_to_f32((xw[t] >> sh) & 0xffffu));
-        } else {
-          constexpr int kTB = 8;  // tokens loaded per batch of loads
+        if (m == 1 && tid >= kUnits - kNT) break;
+        const long gc = unit_channel(tid + kNT * m);
+        constexpr int kTB = 8;  // tokens loaded per batch of loads
 #pragma unroll 1
-          for (int tb = 0; tb < kC; tb += kTB) {
-            uint32_t xv[kTB];
+        for (int tb = 0; tb < kC; tb += kTB) {
+          uint32_t xv[kTB];
 #pragma unroll
-            for (int e = 0; e < kTB; ++e)
-              xv[e] = (tb + e < nt) ? load_raw<BF>(a.qkv, (static_cast<long>(b) * T + t0 + tb + e) * C + gch[m]) : 0u;
+          for (int e = 0; e < kTB; ++e)
+            xv[e] = (tb + e < nt) ? load_raw<BF>(a.qkv, (static_cast<long>(b) * T + t0 + tb + e) * C + gc) : 0u;
 #pragma unroll
-            for (int e = 0; e < kTB; ++e) conv_token(m, tb + e, raw_f32<BF>(xv[e]));
+          for (int e = 0; e < kTB; ++e) {
+            const int t = tb + e;
+            const float xf = raw_f32<BF>(xv[e]);
+            float uu = wt[m][0][0] * win[m][0];
+            uu = fmaf(wt[m][0][1], win[m][1], uu);
+            uu = fmaf(wt[m][0][2], win[m][2], uu);
+            uu = fmaf(wt[m][0][3], xf, uu);
+            const float val = (t < nt) ? silu(uu) : 0.0f;
+            if (m == 0)
+              sm.u.raw[t][tid] = val;
+            else
+              sm.v[t][tid] = val;
+            if (t < nt) {
+              win[m][0] = win[m][1];
+              win[m][1] = win[m][2];
+              win[m][2] = xf;
+            }
           }
         }
       }
-      if (w == 0) {
-        // lanes 0..31: one token each; inclusive scan of log(alpha)
-        float la = 0.0f, bt = 0.0f;
-        if (l < nt) {
-          float dt, br;
-          if constexpr (BF) {
-            dt = bf16_to_f32(sm.st.dt[par][l]);
-            br = bf16_to_f32(sm.st.br[par][l]);
-          } else {
-            const long ai = (static_cast<long>(b) * T + t0 + l) * a.Hv + h;
-            dt = raw_f32<BF>(load_raw<BF>(a.dt_raw, ai));
-            br = raw_f32<BF>(load_raw<BF>(a.b_raw, ai));
-          }
-          la = -A_exp * softplus(dt + dt_bias);
-          bt = 1.0f / (1.0f + __expf(-br));
-        }
-#pragma unroll
-        for (int off = 1; off < kC; off <<= 1) {
-          const float o = __shfl_up(la, off, 64);
-          if (l >= off) la += o;
-        }
-        if (l < kC) {
-          sm.g[l] = la;
-          sm.beta[l] = bt;
-        }
-      }
+      if (w == 0) chunk_gates<BF>(a, b, h, ch, l, A_exp, dt_bias, sm.g[par], sm.beta[par]);
     }
     __syncthreads();
 
@@ -480,10 +532,10 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tt + 4 * q + r, s = 16 * st + c16;
-        const float dg = sm.g[t] - sm.g[s];
+        const float dg = sm.g[par][t] - sm.g[par][s];
         const float e = (s <= t) ? __expf(dg) : 0.0f;
         // kk and qk carry the 2^15 x 2^15 operand scale
-        sm.u.s.at[s][t] = (s < t) ? -(sm.beta[t] * e * (kk[r] * (kDown * kDown))) : 0.0f;
+        sm.u.s.at[s][t] = (s < t) ? -(sm.beta[par][t] * e * (kk[r] * (kDown * kDown))) : 0.0f;
         put_split(&sm.u.s.p_hi[0][0], &sm.u.s.p_lo[0][0], t * kPLd + s, e * (qk[r] * kDown));  // = 2^15 P
       }
     }
@@ -524,8 +576,8 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * tt + 4 * q + r, j = 32 * w + 16 * jt + c16;
-          const float gam = __expf(sm.g[t]);
-          sm.u.s.x[t][j] = sm.beta[t] * (sm.v[t][j] - gam * (kh[tt][jt][r] * kDown));
+          const float gam = __expf(sm.g[par][t]);
+          sm.u.s.x[t][j] = sm.beta[par][t] * (sm.v[t][j] - gam * (kh[tt][jt][r] * kDown));
           oacc[tt][jt][r] = gam * (qh[tt][jt][r] * kDown);
         }
     __syncthreads();
@@ -553,16 +605,16 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
       // waves 2-3 prefetch the next chunk's inputs meanwhile
       if (ch + 1 < nchunks) {
         if (__builtin_amdgcn_readfirstlane(w) == 2)
-          stage_chunk<2, 0>(sm.st, a, b, g, h, ch + 1, l);
+          stage_chunk<2, 0>(sm, a, b, g, h, ch + 1, l, false, A_exp, dt_bias);
         else
-          stage_chunk<2, 1>(sm.st, a, b, g, h, ch + 1, l);
+          stage_chunk<2, 1>(sm, a, b, g, h, ch + 1, l, false, A_exp, dt_bias);
       }
     }
     __syncthreads();
 
     // ---- 5. O += P Delta;  H = gamma_C H + K^T diag(exp(g_C - g)) Delta
     {
-      const float gC = sm.g[kC - 1];
+      const float gC = sm.g[par][kC - 1];
       const float gamC = __expf(gC);
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
@@ -573,8 +625,8 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
           const int s0 = 4 * q + r, s1 = 16 + 4 * q + r;
           top[r] = sm.u.s.x[s0][j];
           bot[r] = sm.u.s.x[s1][j];
-          top2[r] = __expf(gC - sm.g[s0]) * top[r];
-          bot2[r] = __expf(gC - sm.g[s1]) * bot[r];
+          top2[r] = __expf(gC - sm.g[par][s0]) * top[r];
+          bot2[r] = __expf(gC - sm.g[par][s1]) * bot[r];
         }
         u32x4 dh, dl, eh, el;
         bfrag(top, bot, dh, dl);
