@@ -91,18 +91,21 @@ struct alignas(16) ChunkSmem {
     } s;
   } u;
   float v[kC][kXLd];        // silu(conv) of v
-  float g[2][kC];           // running sum of log(alpha) inside the chunk, by chunk parity
-  float beta[2][kC];
+  alignas(16) float g[2][kC];  // running sum of log(alpha) inside the chunk, by chunk parity
+  alignas(16) float beta[2][kC];
   alignas(16) float ss[kC][4];  // per-wave partial sums of o^2
   Staging<BF> st;
 };
 
-// Gates of the tokens of chunk `ch`, computed by one wave (lanes 0..31, one token
-// each): beta_t = sigmoid(b_t) and the inclusive running sum over the chunk of
+// Gates of the tokens of a chunk, computed by one wave (lanes 0..31, one token each):
+// beta_t = sigmoid(b_t) and the inclusive running sum over the chunk of
 // log(alpha_t) = -exp(A_log) softplus(dt_t + dt_bias). Tokens past T get 0 and 0.
+// `left` = tokens of the sequence from the chunk's first on.
 template <bool BF>
-__device__ __forceinline__ void chunk_gates(const KernelArgs& a, int b, int h, int ch, int lane, float A_exp,
-                                            float dt_bias, float* g_out, float* beta_out);
+__device__ __forceinline__ void chunk_gate_inputs(const KernelArgs& a, int b, int h, int ch, int lane, float& dt,
+                                                  float& br);
+__device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float br, float A_exp, float dt_bias,
+                                            float* g_out, float* beta_out);
 
 // Prefetch chunk `ch` (bf16 activations): conv inputs and z rows into LDS, and the
 // chunk's gates. Done by NW waves, the calling one being number WV among them. Every
@@ -124,6 +127,8 @@ __device__ __forceinline__ void stage_chunk(ChunkSmem<true>& sm, const KernelArg
   asm volatile("" : "+s"(cw), "+s"(zw), "+s"(hk));
   // conv rows: (token t, segment s) with s = 0 q, 1 k of k-head g, 2 v of v-head h
   constexpr int kXPer = 3 * kC / NW, kZPer = kC / NW;
+  float dt = 0.0f, br = 0.0f;  // gate inputs, loaded first (the gate math then overlaps the other loads)
+  if (WV == 0) chunk_gate_inputs<true>(a, b, h, ch, lane, dt, br);
   const uint32_t* xb = reinterpret_cast<const uint32_t*>(a.qkv) + (static_cast<long>(b) * T + t0) * cw + lane;
   const uint32_t* zb = reinterpret_cast<const uint32_t*>(a.z) + (static_cast<long>(b) * T + t0) * zw + h * (kD / 2) + lane;
   const int so[3] = {g * (kD / 2), (hk + g) * (kD / 2), (2 * hk + h) * (kD / 2)};
@@ -154,7 +159,7 @@ __device__ __forceinline__ void stage_chunk(ChunkSmem<true>& sm, const KernelArg
 #pragma unroll
     for (int r = 0; r < kHist; ++r) st.x[r / 3][(r % 3) * (kD / 2) + lane] = hist[r];
   }
-  if (WV == 0) chunk_gates<true>(a, b, h, ch, lane, A_exp, dt_bias, sm.g[ch & 1], sm.beta[ch & 1]);
+  if (WV == 0) chunk_gates(a.T - t0, lane, dt, br, A_exp, dt_bias, sm.g[ch & 1], sm.beta[ch & 1]);
 #pragma unroll
   for (int i = 0; i < kXPer; ++i) {
     const int r = WV * kXPer + i, t = r / 3, sg = r - 3 * t;
@@ -206,25 +211,35 @@ __device__ __forceinline__ float rows_total(float v) {
          (__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48)));
 }
-__device__ __forceinline__ float softplus(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
 
 template <bool BF>
-__device__ __forceinline__ void chunk_gates(const KernelArgs& a, int b, int h, int ch, int lane, float A_exp,
-                                            float dt_bias, float* g_out, float* beta_out) {
-  const int t0 = ch * kC, nt = min(kC, a.T - t0);
-  float la = 0.0f, bt = 0.0f;
-  if (lane < nt) {
+__device__ __forceinline__ void chunk_gate_inputs(const KernelArgs& a, int b, int h, int ch, int lane, float& dt,
+                                                  float& br) {
+  const int t0 = ch * kC;
+  if (lane < min(kC, a.T - t0)) {
     const long ai = (static_cast<long>(b) * a.T + t0 + lane) * a.Hv + h;
-    const float dt = raw_f32<BF>(load_raw<BF>(a.dt_raw, ai));
-    const float br = raw_f32<BF>(load_raw<BF>(a.b_raw, ai));
-    la = -A_exp * softplus(dt + dt_bias);
-    bt = 1.0f / (1.0f + __expf(-br));
+    dt = raw_f32<BF>(load_raw<BF>(a.dt_raw, ai));
+    br = raw_f32<BF>(load_raw<BF>(a.b_raw, ai));
   }
-#pragma unroll
-  for (int off = 1; off < kC; off <<= 1) {
-    const float o = __shfl_up(la, off, 64);
-    if (lane >= off) la += o;
+}
+
+__device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float br, float A_exp, float dt_bias,
+                                            float* g_out, float* beta_out) {
+  float la = 0.0f, bt = 0.0f;
+  if (lane < min(kC, left)) {
+    // softplus(x) = max(x, 0) + log(1 + exp(-|x|)); the log's argument lies in (1, 2]
+    const float x = dt + dt_bias;
+    la = -A_exp * (fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))));
+    bt = __builtin_amdgcn_rcpf(1.0f + __expf(-br));
   }
+  // inclusive scan over lanes 0..31: within each row of 16 lanes by DPP row shifts
+  // (lanes shifted in from outside the row read 0), then row 1 adds row 0's total
+  la += dpp<0x111>(la);  // row_shr:1
+  la += dpp<0x112>(la);  // row_shr:2
+  la += dpp<0x114>(la);  // row_shr:4
+  la += dpp<0x118>(la);  // row_shr:8
+  const float row0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), 15));
+  if (lane >= 16) la += row0;
   if (lane < kC) {
     g_out[lane] = la;
     beta_out[lane] = bt;
@@ -452,7 +467,11 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
           }
         }
       }
-      if (w == 0) chunk_gates<BF>(a, b, h, ch, l, A_exp, dt_bias, sm.g[par], sm.beta[par]);
+      if (w == 0) {
+        float dt = 0.0f, br = 0.0f;
+        chunk_gate_inputs<BF>(a, b, h, ch, l, dt, br);
+        chunk_gates(T - t0, l, dt, br, A_exp, dt_bias, sm.g[par], sm.beta[par]);
+      }
     }
     __syncthreads();
 
@@ -517,25 +536,35 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     // ---- 3a. K K^T and Q K^T (32 x 32): wave w computes tile (w/2, w%2) of each
     {
       const int tt = w >> 1, st = w & 1;
+      u32x4 fr[kD / 32][6];  // all operand fragments read before the first product
+#pragma unroll
+      for (int kb = 0; kb < kD / 32; ++kb) {
+        fr[kb][0] = frag(&sm.k_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+        fr[kb][1] = frag(&sm.k_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+        fr[kb][2] = frag(&sm.q_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+        fr[kb][3] = frag(&sm.q_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+        fr[kb][4] = frag(&sm.k_hi[0][0], kQKLd, 16 * st + c16, 32 * kb, q);
+        fr[kb][5] = frag(&sm.k_lo[0][0], kQKLd, 16 * st + c16, 32 * kb, q);
+      }
       f32x4 kk = {0.0f, 0.0f, 0.0f, 0.0f}, qk = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < kD / 32; ++kb) {
-        const u32x4 kah = frag(&sm.k_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        const u32x4 kal = frag(&sm.k_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        const u32x4 qah = frag(&sm.q_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        const u32x4 qal = frag(&sm.q_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        const u32x4 kbh = frag(&sm.k_hi[0][0], kQKLd, 16 * st + c16, 32 * kb, q);
-        const u32x4 kbl = frag(&sm.k_lo[0][0], kQKLd, 16 * st + c16, 32 * kb, q);
-        kk = mfma3(kah, kal, kbh, kbl, kk);
-        qk = mfma3(qah, qal, kbh, kbl, qk);
+        kk = mfma3(fr[kb][0], fr[kb][1], fr[kb][4], fr[kb][5], kk);
+        qk = mfma3(fr[kb][2], fr[kb][3], fr[kb][4], fr[kb][5], qk);
       }
+      const int t4 = 16 * tt + 4 * q, s = 16 * st + c16;
+      const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
+      const float gs = sm.g[par][s];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tt + 4 * q + r, s = 16 * st + c16;
-        const float dg = sm.g[par][t] - sm.g[par][s];
-        const float e = (s <= t) ? __expf(dg) : 0.0f;
+        const int t = t4 + r;
+        // exp(g_t - g_s) <= 1 for s <= t; the other entries are masked (argument clamped)
+        const float ex = __expf(fminf(gt[r] - gs, 0.0f));
+        const float e = (s <= t) ? ex : 0.0f;
         // kk and qk carry the 2^15 x 2^15 operand scale
-        sm.u.s.at[s][t] = (s < t) ? -(sm.beta[par][t] * e * (kk[r] * (kDown * kDown))) : 0.0f;
+        const float av = -(bt[r] * e * (kk[r] * (kDown * kDown)));
+        sm.u.s.at[s][t] = (s < t) ? av : 0.0f;
         put_split(&sm.u.s.p_hi[0][0], &sm.u.s.p_lo[0][0], t * kPLd + s, e * (qk[r] * kDown));  // = 2^15 P
       }
     }
@@ -549,37 +578,53 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         kh[tt][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         qh[tt][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
+    {
+      // K and Q fragments of block kb + 1 are read while block kb is multiplied
+      u32x4 fq[2][2][4];
+      auto load_fq = [&](int kb, u32x4(&dst)[2][4]) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      u32x4 hb_hi[2], hb_lo[2];
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) bfrag(hacc[2 * kb][jt], hacc[2 * kb + 1][jt], hb_hi[jt], hb_lo[jt]);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const u32x4 kah = frag(&sm.k_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        const u32x4 kal = frag(&sm.k_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        const u32x4 qah = frag(&sm.q_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        const u32x4 qal = frag(&sm.q_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          kh[tt][jt] = mfma3(kah, kal, hb_hi[jt], hb_lo[jt], kh[tt][jt]);
-          qh[tt][jt] = mfma3(qah, qal, hb_hi[jt], hb_lo[jt], qh[tt][jt]);
+        for (int tt = 0; tt < 2; ++tt) {
+          dst[tt][0] = frag(&sm.k_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+          dst[tt][1] = frag(&sm.k_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+          dst[tt][2] = frag(&sm.q_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+          dst[tt][3] = frag(&sm.q_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
         }
+      };
+      load_fq(0, fq[0]);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb + 1 < 4) load_fq(kb + 1, fq[(kb + 1) & 1]);
+        u32x4 hb_hi[2], hb_lo[2];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) bfrag(hacc[2 * kb][jt], hacc[2 * kb + 1][jt], hb_hi[jt], hb_lo[jt]);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const u32x4(&f)[4] = fq[kb & 1][tt];
+            kh[tt][jt] = mfma3(f[0], f[1], hb_hi[jt], hb_lo[jt], kh[tt][jt]);
+            qh[tt][jt] = mfma3(f[2], f[3], hb_hi[jt], hb_lo[jt], qh[tt][jt]);
+          }
       }
     }
     // rhs[t][j] = beta_t (v_t[j] - gamma_t (K H0)[t][j]);  O starts as gamma_t (Q H0)[t][j]
     f32x4 oacc[2][2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t4 = 16 * tt + 4 * q;
+      const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
+      for (int r = 0; r < 4; ++r) {
+        const float gam = __expf(gt[r]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * tt + 4 * q + r, j = 32 * w + 16 * jt + c16;
-          const float gam = __expf(sm.g[par][t]);
-          sm.u.s.x[t][j] = sm.beta[par][t] * (sm.v[t][j] - gam * (kh[tt][jt][r] * kDown));
+        for (int jt = 0; jt < 2; ++jt) {
+          const int j = 32 * w + 16 * jt + c16;
+          sm.u.s.x[t4 + r][j] = bt[r] * (sm.v[t4 + r][j] - gam * (kh[tt][jt][r] * kDown));
           oacc[tt][jt][r] = gam * (qh[tt][jt][r] * kDown);
         }
+      }
+    }
     __syncthreads();
 
     // ---- 4. forward substitution (I + A) Delta = rhs, one lane per column j, in
@@ -589,11 +634,20 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
       float d[kC];
 #pragma unroll
       for (int t = 0; t < kC; ++t) d[t] = sm.u.s.x[t][tid];
+      // rows of -A^T are read two rows ahead of their use
+      f32x4 ring[3][kC / 4];
+      auto fetch = [&](int s_, f32x4(&dst)[kC / 4]) {
+#pragma unroll
+        for (int t4 = (s_ + 1) / 4; t4 < kC / 4; ++t4) dst[t4] = *reinterpret_cast<const f32x4*>(&sm.u.s.at[s_][4 * t4]);
+      };
+      fetch(0, ring[0]);
+      fetch(1, ring[1]);
 #pragma unroll
       for (int s = 0; s < kC - 1; ++s) {
+        if (s + 2 < kC - 1) fetch(s + 2, ring[(s + 2) % 3]);
 #pragma unroll
         for (int t4 = (s + 1) / 4; t4 < kC / 4; ++t4) {
-          const f32x4 m = *reinterpret_cast<const f32x4*>(&sm.u.s.at[s][4 * t4]);
+          const f32x4 m = ring[s % 3][t4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (4 * t4 + e > s) d[4 * t4 + e] = fmaf(m[e], d[s], d[4 * t4 + e]);
@@ -614,41 +668,54 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 
     // ---- 5. O += P Delta;  H = gamma_C H + K^T diag(exp(g_C - g)) Delta
     {
+      // operand fragments first: P rows of this wave's two row tiles, K^T rows of all 8
+      u32x4 ph[2], pl[2], kth[8], ktl[8];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        ph[tt] = frag(&sm.u.s.p_hi[0][0], kPLd, 16 * tt + c16, 0, q);
+        pl[tt] = frag(&sm.u.s.p_lo[0][0], kPLd, 16 * tt + c16, 0, q);
+      }
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        kth[it] = frag(&sm.kt_hi[0][0], kKTLd, 16 * it + c16, 0, q);
+        ktl[it] = frag(&sm.kt_lo[0][0], kKTLd, 16 * it + c16, 0, q);
+      }
       const float gC = sm.g[par][kC - 1];
       const float gamC = __expf(gC);
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.g[par][4 * q]);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.g[par][16 + 4 * q]);
+      u32x4 dh[2], dl[2], eh[2], el[2];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
         const int j = 32 * w + 16 * jt + c16;
         f32x4 top, bot, top2, bot2;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int s0 = 4 * q + r, s1 = 16 + 4 * q + r;
-          top[r] = sm.u.s.x[s0][j];
-          bot[r] = sm.u.s.x[s1][j];
-          top2[r] = __expf(gC - sm.g[par][s0]) * top[r];
-          bot2[r] = __expf(gC - sm.g[par][s1]) * bot[r];
+          top[r] = sm.u.s.x[4 * q + r][j];
+          bot[r] = sm.u.s.x[16 + 4 * q + r][j];
+          top2[r] = __expf(gC - g0[r]) * top[r];
+          bot2[r] = __expf(gC - g1[r]) * bot[r];
         }
-        u32x4 dh, dl, eh, el;
-        bfrag(top, bot, dh, dl);
-        bfrag(top2, bot2, eh, el);
+        bfrag(top, bot, dh[jt], dl[jt]);
+        bfrag(top2, bot2, eh[jt], el[jt]);
+      }
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const u32x4 ph = frag(&sm.u.s.p_hi[0][0], kPLd, 16 * tt + c16, 0, q);
-          const u32x4 pl = frag(&sm.u.s.p_lo[0][0], kPLd, 16 * tt + c16, 0, q);
-          const f32x4 pd = mfma3(ph, pl, dh, dl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});  // 2^15 P Delta
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          const f32x4 pd = mfma3(ph[tt], pl[tt], dh[jt], dl[jt], f32x4{0.0f, 0.0f, 0.0f, 0.0f});  // 2^15 P Delta
 #pragma unroll
           for (int r = 0; r < 4; ++r) oacc[tt][jt][r] = fmaf(pd[r], kDown, oacc[tt][jt][r]);
         }
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
+      for (int it = 0; it < 8; ++it)
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
           f32x4 hv = hacc[it][jt];
 #pragma unroll
           for (int r = 0; r < 4; ++r) hv[r] *= gamC;
-          const u32x4 kh_ = frag(&sm.kt_hi[0][0], kKTLd, 16 * it + c16, 0, q);
-          const u32x4 kl_ = frag(&sm.kt_lo[0][0], kKTLd, 16 * it + c16, 0, q);
-          hacc[it][jt] = mfma3(kh_, kl_, eh, el, hv);
+          hacc[it][jt] = mfma3(kth[it], ktl[it], eh[jt], el[jt], hv);
         }
-      }
     }
 
     // ---- 6. gated RMSNorm of o = O / sqrt(d) and the output rows
@@ -670,36 +737,60 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         }
       }
       __syncthreads();
+      // all inputs first (row sums, z), then the 16 outputs of this lane, then the stores
       const long zrow = static_cast<long>(a.Hv) * kD;
+      const long row0 = (static_cast<long>(b) * T + t0) * zrow + static_cast<long>(h) * kD;
+      f32x4 sv[2][4];
+      float zz[2][4][2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * tt + 4 * q + r;
-          if (t < nt) {
-            const f32x4 sv = *reinterpret_cast<const f32x4*>(&sm.ss[t][0]);
-            const float tot = (sv[0] + sv[1] + sv[2] + sv[3]) * (rsd * rsd);
-            const float rr = __builtin_amdgcn_rsqf(tot * (1.0f / kD) + a.rms_eps);
-            const long row = (static_cast<long>(b) * T + t0 + t) * zrow + static_cast<long>(h) * kD;
+          sv[tt][r] = *reinterpret_cast<const f32x4*>(&sm.ss[t][0]);
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-              const int j = 32 * w + 16 * jt + c16;
-              float zz;
-              if constexpr (BF)
-                zz = bf16_to_f32((sm.st.z[par][t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
-              else
-                zz = raw_f32<BF>(load_raw<BF>(a.z, row + j));
-              const float y = oacc[tt][jt][r] * rsd * rr * nw[jt] * silu(zz);
-              if (a.out_bf16) {
-                uint32_t u = __float_as_uint(y);
-                u += 0x7fffu + ((u >> 16) & 1u);
-                static_cast<uint16_t*>(a.out)[row + j] = static_cast<uint16_t>(u >> 16);
-              } else {
-                static_cast<float*>(a.out)[row + j] = y;
-              }
-            }
+          for (int jt = 0; jt < 2; ++jt) {
+            const int j = 32 * w + 16 * jt + c16;
+            if constexpr (BF)
+              zz[tt][r][jt] = bf16_to_f32((sm.st.z[par][t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+            else
+              zz[tt][r][jt] = raw_f32<BF>(load_raw<BF>(a.z, row0 + min(t, nt - 1) * zrow + j));
           }
         }
+      float y[2][4][2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 v4 = sv[tt][r];
+          const float tot = (v4[0] + v4[1] + v4[2] + v4[3]) * (rsd * rsd);
+          const float rr = __builtin_amdgcn_rsqf(tot * (1.0f / kD) + a.rms_eps);
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) y[tt][r][jt] = oacc[tt][jt][r] * rsd * rr * nw[jt] * silu(zz[tt][r][jt]);
+        }
+      // rows past the end of the sequence (last chunk only) are not written
+      auto emit = [&](auto* outp, auto cvt) {
+        const bool full = nt == kC;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tt + 4 * q + r;
+            if (full || t < nt) {
+#pragma unroll
+              for (int jt = 0; jt < 2; ++jt) outp[row0 + t * zrow + 32 * w + 16 * jt + c16] = cvt(y[tt][r][jt]);
+            }
+          }
+      };
+      if (a.out_bf16) {
+        emit(static_cast<uint16_t*>(a.out), [](float x) {  // round to nearest even
+          uint32_t u = __float_as_uint(x);
+          u += 0x7fffu + ((u >> 16) & 1u);
+          return static_cast<uint16_t>(u >> 16);
+        });
+      } else {
+        emit(static_cast<float*>(a.out), [](float x) { return x; });
+      }
     }
     __syncthreads();  // LDS is rewritten by the next chunk
   }
