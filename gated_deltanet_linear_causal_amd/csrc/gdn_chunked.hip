@@ -21,6 +21,7 @@
 // A operand reads the same permuted columns from LDS (two 8-byte reads).
 // Precision: every operand is split into two fp16 halves (x = hi + lo, 22 significant
 // bits) and each product is evaluated as hi*hi + hi*lo + lo*hi with fp32 accumulation
+// (the three MFMAs of an accumulator are issued apart, interleaved with independent ones)
 // (~2^-21 relative per product). A bf16 split (8 + 8 bits) measured ~1e-4 relative
 // error on the outputs, too coarse for the fp32 recurrence. Operands must stay below
 // the fp16 range (6.5e4); the normalised q, k, the state and delta of this layer are
@@ -280,14 +281,6 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
                                                 0);
 }
-// c += a * b with split operands (hi*hi + hi*lo + lo*hi)
-__device__ __forceinline__ f32x4 mfma3(u32x4 ahi, u32x4 alo, u32x4 bhi, u32x4 blo, f32x4 c) {
-  c = mfma(ahi, bhi, c);
-  c = mfma(ahi, blo, c);
-  c = mfma(alo, bhi, c);
-  return c;
-}
-
 // A-operand fragment of a row-major bf16 plane: row `row`, 32-column block at `k0`,
 // permuted order (k0+4q .. +3, k0+16+4q .. +3) for lane group q.
 __device__ __forceinline__ u32x4 frag(const uint16_t* plane, int ld, int row, int k0, int q) {
@@ -546,12 +539,20 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         fr[kb][4] = frag(&sm.k_hi[0][0], kQKLd, 16 * st + c16, 32 * kb, q);
         fr[kb][5] = frag(&sm.k_lo[0][0], kQKLd, 16 * st + c16, 32 * kb, q);
       }
-      f32x4 kk = {0.0f, 0.0f, 0.0f, 0.0f}, qk = {0.0f, 0.0f, 0.0f, 0.0f};
+      // four independent accumulators (K K^T and Q K^T, even and odd blocks) so that
+      // consecutive MFMAs never wait on each other's result
+      f32x4 kk2[2] = {}, qk2[2] = {};
 #pragma unroll
       for (int kb = 0; kb < kD / 32; ++kb) {
-        kk = mfma3(fr[kb][0], fr[kb][1], fr[kb][4], fr[kb][5], kk);
-        qk = mfma3(fr[kb][2], fr[kb][3], fr[kb][4], fr[kb][5], qk);
+#pragma unroll
+        for (int part = 0; part < 3; ++part) {
+          const u32x4 ka = part == 2 ? fr[kb][1] : fr[kb][0], qa = part == 2 ? fr[kb][3] : fr[kb][2];
+          const u32x4 bb = part == 1 ? fr[kb][5] : fr[kb][4];
+          kk2[kb & 1] = mfma(ka, bb, kk2[kb & 1]);
+          qk2[kb & 1] = mfma(qa, bb, qk2[kb & 1]);
+        }
       }
+      const f32x4 kk = kk2[0] + kk2[1], qk = qk2[0] + qk2[1];
       const int t4 = 16 * tt + 4 * q, s = 16 * st + c16;
       const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
       const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
@@ -597,14 +598,18 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         u32x4 hb_hi[2], hb_lo[2];
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) bfrag(hacc[2 * kb][jt], hacc[2 * kb + 1][jt], hb_hi[jt], hb_lo[jt]);
+        // hi*hi, hi*lo, lo*hi of all eight accumulators in turn (independent neighbours)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int part = 0; part < 3; ++part)
 #pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            const u32x4(&f)[4] = fq[kb & 1][tt];
-            kh[tt][jt] = mfma3(f[0], f[1], hb_hi[jt], hb_lo[jt], kh[tt][jt]);
-            qh[tt][jt] = mfma3(f[2], f[3], hb_hi[jt], hb_lo[jt], qh[tt][jt]);
-          }
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+              const u32x4(&f)[4] = fq[kb & 1][tt];
+              const u32x4 bb = part == 1 ? hb_lo[jt] : hb_hi[jt];
+              kh[tt][jt] = mfma(part == 2 ? f[1] : f[0], bb, kh[tt][jt]);
+              qh[tt][jt] = mfma(part == 2 ? f[3] : f[2], bb, qh[tt][jt]);
+            }
       }
     }
     // rhs[t][j] = beta_t (v_t[j] - gamma_t (K H0)[t][j]);  O starts as gamma_t (Q H0)[t][j]
@@ -699,23 +704,33 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         bfrag(top, bot, dh[jt], dl[jt]);
         bfrag(top2, bot2, eh[jt], el[jt]);
       }
+      f32x4 pd[2][2] = {};  // 2^15 P Delta
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+            pd[tt][jt] = mfma(part == 2 ? pl[tt] : ph[tt], part == 1 ? dl[jt] : dh[jt], pd[tt][jt]);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          const f32x4 pd = mfma3(ph[tt], pl[tt], dh[jt], dl[jt], f32x4{0.0f, 0.0f, 0.0f, 0.0f});  // 2^15 P Delta
+        for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) oacc[tt][jt][r] = fmaf(pd[r], kDown, oacc[tt][jt][r]);
-        }
+          for (int r = 0; r < 4; ++r) oacc[tt][jt][r] = fmaf(pd[tt][jt][r], kDown, oacc[tt][jt][r]);
 #pragma unroll
       for (int it = 0; it < 8; ++it)
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          f32x4 hv = hacc[it][jt];
+        for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) hv[r] *= gamC;
-          hacc[it][jt] = mfma3(kth[it], ktl[it], eh[jt], el[jt], hv);
-        }
+          for (int r = 0; r < 4; ++r) hacc[it][jt][r] *= gamC;
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+            hacc[it][jt] = mfma(part == 2 ? ktl[it] : kth[it], part == 1 ? el[jt] : eh[jt], hacc[it][jt]);
     }
 
     // ---- 6. gated RMSNorm of o = O / sqrt(d) and the output rows
