@@ -118,11 +118,26 @@ gdn::KernelArgs base_args(const gdn_shape_t* s) {
 
 gdn_status_t launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
+// Trail of gdn_decode_verify (fp32): delta [B][T][H_v][d_v], then unit k
+// [B][T][H_k][d_k], then alpha [B][T][H_v]. Both arrays of d-vectors start 16-byte
+// aligned (d is a multiple of 32).
+struct TrailLayout {
+  size_t delta, k, alpha, bytes;  // byte offsets and total
+  TrailLayout(const Sizes& z, size_t T)
+      : delta(0), k(z.B * T * z.Hv * z.d * 4), alpha(k + z.B * T * z.Hk * z.d * 4), bytes(alpha + z.B * T * z.Hv * 4) {}
+  void assign(gdn::KernelArgs& a, void* base) const {
+    char* p = static_cast<char*>(base);
+    a.trail_delta = reinterpret_cast<float*>(p + delta);
+    a.trail_k = reinterpret_cast<float*>(p + k);
+    a.trail_alpha = reinterpret_cast<float*>(p + alpha);
+  }
+};
+
 }  // namespace
 
 extern "C" {
 
-int32_t gdn_abi_version(void) { return (1 << 16) | 0; }
+int32_t gdn_abi_version(void) { return (1 << 16) | 1; }
 
 const char* gdn_status_string(int32_t st) {
   switch (st) {
@@ -362,6 +377,102 @@ gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_stat
     if (st != GDN_OK) return st;
   }
   return GDN_OK;
+}
+
+size_t gdn_verify_trail_bytes(const gdn_shape_t* shape, int32_t T) {
+  if (check_shape(shape) != GDN_OK || T < 0 || T > gdn::kMaxVerifyTokens) return SIZE_MAX;
+  const Sizes z(shape);
+  return TrailLayout(z, static_cast<size_t>(T)).bytes;
+}
+
+gdn_status_t gdn_decode_verify(const gdn_shape_t* shape, int32_t T, const void* conv1d_state,
+                               const float* state, const void* qkv, const void* conv1d_weight,
+                               const void* dt_raw, const void* b_raw, const void* z_in,
+                               const float* A_log, const float* dt_bias, const float* norm_weight,
+                               void* out, void* trail, size_t trail_bytes, void* stream) {
+  gdn_status_t st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (T < 0 || T > gdn::kMaxVerifyTokens) return GDN_ERR_SHAPE;
+  const Sizes z(shape);
+  if (z.B == 0 || T == 0) return GDN_OK;
+  const size_t Tz = static_cast<size_t>(T);
+  const TrailLayout tl(z, Tz);
+  if (trail_bytes < tl.bytes) return GDN_ERR_WORKSPACE;
+  const Buf bufs[] = {
+      {conv1d_state, z.conv_state(), false, 16},
+      {state, z.state(), false, 16},
+      {qkv, z.B * Tz * z.C * z.ea, false, 16},
+      {conv1d_weight, z.conv_w(), false, 16},
+      {dt_raw, z.B * Tz * z.Hv * z.ea, false, z.ea},
+      {b_raw, z.B * Tz * z.Hv * z.ea, false, z.ea},
+      {z_in, z.B * Tz * z.Hv * z.d * z.ea, false, 16},
+      {A_log, z.Hv * 4, false, 4},
+      {dt_bias, z.Hv * 4, false, 4},
+      {norm_weight, z.d * 4, false, 16},
+      {out, z.B * Tz * z.Hv * z.d * z.eo, true, 16},
+      {trail, tl.bytes, true, 16},
+  };
+  if ((st = check_buffers(bufs, 12)) != GDN_OK) return st;
+  if (static_cast<int64_t>(shape->batch) * shape->num_v_heads > std::numeric_limits<int32_t>::max())
+    return GDN_ERR_SHAPE;  // grid = B * H_v workgroups
+  gdn::KernelArgs a = base_args(shape);
+  a.T = T;
+  a.conv_state = const_cast<void*>(conv1d_state);  // read only in this call
+  a.state = const_cast<float*>(state);              // read only in this call
+  a.qkv = qkv;
+  a.qkv_bs = static_cast<long>(Tz * z.C);
+  a.qkv_ts = static_cast<long>(z.C);
+  a.conv_w = conv1d_weight;
+  a.dt_raw = dt_raw;
+  a.b_raw = b_raw;
+  a.ab_bs = static_cast<long>(Tz * z.Hv);
+  a.ab_ts = static_cast<long>(z.Hv);
+  a.z = z_in;
+  a.z_bs = static_cast<long>(Tz * z.Hv * z.d);
+  a.z_ts = static_cast<long>(z.Hv * z.d);
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.norm_w = norm_weight;
+  a.out = out;
+  a.out_bs = static_cast<long>(Tz * z.Hv * z.d);
+  a.out_ts = static_cast<long>(z.Hv * z.d);
+  tl.assign(a, trail);
+  (void)hipGetLastError();
+  return launched(gdn::launch_verify(shape->head_k_dim, a, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_decode_commit(const gdn_shape_t* shape, int32_t T, const int32_t* accepted,
+                               void* conv1d_state, float* state, const void* qkv, const void* trail,
+                               size_t trail_bytes, void* stream) {
+  gdn_status_t st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (T < 0 || T > gdn::kMaxVerifyTokens) return GDN_ERR_SHAPE;
+  const Sizes z(shape);
+  if (z.B == 0 || T == 0) return GDN_OK;
+  const size_t Tz = static_cast<size_t>(T);
+  const TrailLayout tl(z, Tz);
+  if (trail_bytes < tl.bytes) return GDN_ERR_WORKSPACE;
+  const Buf bufs[] = {
+      {accepted, z.B * 4, false, 4},
+      {conv1d_state, z.conv_state(), true, 16},
+      {state, z.state(), true, 16},
+      {qkv, z.B * Tz * z.C * z.ea, false, 16},
+      {trail, tl.bytes, false, 16},
+  };
+  if ((st = check_buffers(bufs, 5)) != GDN_OK) return st;
+  if (static_cast<int64_t>(shape->batch) * shape->num_v_heads > std::numeric_limits<int32_t>::max())
+    return GDN_ERR_SHAPE;
+  gdn::KernelArgs a = base_args(shape);
+  a.T = T;
+  a.accepted = accepted;
+  a.conv_state = conv1d_state;
+  a.state = state;
+  a.qkv = qkv;
+  a.qkv_bs = static_cast<long>(Tz * z.C);
+  a.qkv_ts = static_cast<long>(z.C);
+  tl.assign(a, const_cast<void*>(trail));  // read only in this call
+  (void)hipGetLastError();
+  return launched(gdn::launch_commit(shape->head_k_dim, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -36,6 +36,11 @@ struct KernelArgs {
   long ab_bs, ab_ts;
   long z_bs, z_ts;
   long out_bs, out_ts;
+  // speculative verification: per-token updates of the draft, and the accepted counts
+  float* trail_delta;      // [B][T][Hv][D]  delta_t of each v-head
+  float* trail_k;          // [B][T][Hk][D]  unit-norm k_t of each k-head
+  float* trail_alpha;      // [B][T][Hv]     alpha_t of each v-head
+  const int* accepted;     // [B] tokens to commit per sequence
 };
 
 enum Mode : int { kModeConv = 0, kModeRec = 1, kModeFused = 2 };
@@ -51,5 +56,11 @@ hipError_t launch_sequence(int d, int p, const KernelArgs& a, hipStream_t stream
 // workgroup per (sequence, v-head); enqueues the chunk kernel and the conv-state tail.
 bool chunked_supported(int d, int K);
 hipError_t launch_chunked_sequence(const KernelArgs& a, hipStream_t stream);
+// Speculative verification (gdn_kernels.hip): up to kMaxVerifyTokens draft tokens per
+// sequence with both states read only, writing the outputs and the trail; and the
+// commit of the accepted prefix (state and conv state). Grid B * Hv (any G and K).
+constexpr int kMaxVerifyTokens = 8;
+hipError_t launch_verify(int d, const KernelArgs& a, hipStream_t stream);
+hipError_t launch_commit(int d, const KernelArgs& a, hipStream_t stream);
 
 }  // namespace gdn

@@ -291,7 +291,7 @@ __device__ __forceinline__ float conv_channel_generic(const KernelArgs& a, long 
 template <int D, int P, bool STORE, bool STREAM, int R>
 __device__ __forceinline__ float4 delta_rule(float4 (&hreg)[R], const float* kr, const float* qr, float4 v4,
                                              float alpha, float beta, float kq, __amdgpu_buffer_rsrc_t srs,
-                                             uint32_t voff, uint32_t soff) {
+                                             uint32_t voff, uint32_t soff, float4* delta_out = nullptr) {
   using L = Layout<D, P>;
   static_assert(R == L::R, "rows per lane");
   constexpr int CGL = L::CGL;
@@ -322,6 +322,7 @@ __device__ __forceinline__ float4 delta_rule(float4 (&hreg)[R], const float* kr,
     pq.w += __shfl_xor(pq.w, msk, 64);
   }
   const float4 delta = beta * (v4 - alpha * m);
+  if (delta_out) *delta_out = delta;
   // keep k out of registers across the shuffles: re-read it from LDS
   __asm__ volatile("" ::: "memory");
 #pragma unroll
@@ -715,6 +716,186 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_seq_kernel(const Kerne
 }
 
 // ----------------------------------------------------------------------------------
+// Speculative verification of T <= kMaxVerifyTokens draft tokens. One workgroup per
+// (sequence b, v-head h), any G and K: both states are only read, so the G workgroups
+// of a k-head may all read its Q/K conv columns. The K-1 conv-state rows and the T
+// token rows of the workgroup's 3D conv channels are staged in LDS, the state stays in
+// VGPRs. Per token: outputs as gdn_decode_layer would give after the previous draft
+// tokens, and the trail of the token's update H <- alpha H + k delta^T (delta, unit k,
+// alpha), from which gdn_commit_kernel rebuilds the state after any accepted prefix.
+// ----------------------------------------------------------------------------------
+template <int D, bool BF>
+__global__ __launch_bounds__((Layout<D, 1>::NT)) void gdn_verify_kernel(const KernelArgs a) {
+  using L = Layout<D, 1>;
+  constexpr int NT = L::NT, R = L::R, CGL = L::CGL, NW = L::NW;
+  constexpr int NCH = 3 * D, NCPL = (NCH + NT - 1) / NT;
+  constexpr int kRows = kMaxConvTaps - 1 + kMaxVerifyTokens;
+  constexpr uint32_t kRowBytes = D * 4;
+  __shared__ __attribute__((aligned(16))) float s_x[kRows][NCH];  // K-1 conv-state rows, then T token rows
+  __shared__ __attribute__((aligned(16))) float s_q[D];
+  __shared__ __attribute__((aligned(16))) float s_k[D];
+  __shared__ __attribute__((aligned(16))) float s_v[D];
+  __shared__ float red[NW * 4];
+  __shared__ float hred[NW];
+
+  const int t = threadIdx.x;
+  const int b = blockIdx.x / a.Hv;
+  const int h = blockIdx.x - b * a.Hv;
+  const int g = h / a.G;
+  const int cg = (t >> 6) * CGL + (t & (CGL - 1));
+  const int rg = (t & 63) / CGL;
+  const int K = a.K, T = a.T;
+  const long C = a.C;
+  // unit channel c: [0, D) Q of k-head g, [D, 2D) K of k-head g, [2D, 3D) V of v-head h
+  auto chan = [&](int c) -> long {
+    return c < D ? static_cast<long>(g) * D + c
+                 : (c < 2 * D ? static_cast<long>(a.Hk + g) * D + (c - D) : static_cast<long>(2 * a.Hk + h) * D + (c - 2 * D));
+  };
+
+  // ---- small loads: conv inputs into LDS, taps, norm weight
+  float wt[NCPL][kMaxConvTaps];
+#pragma unroll
+  for (int m = 0; m < NCPL; ++m) {
+    const int c = t + m * NT;
+    if (c < NCH) {
+      const long gc = chan(c);
+      for (int j = 0; j < K - 1; ++j) s_x[j][c] = Act<BF>::load(a.conv_state, (static_cast<long>(b) * (K - 1) + j) * C + gc);
+      for (int tok = 0; tok < T; ++tok) s_x[K - 1 + tok][c] = Act<BF>::load(a.qkv, b * a.qkv_bs + tok * a.qkv_ts + gc);
+#pragma unroll
+      for (int j = 0; j < kMaxConvTaps; ++j) wt[m][j] = j < K ? Act<BF>::load(a.conv_w, gc * K + j) : 0.0f;
+    }
+  }
+  float4 w4 = f4(0.0f);
+  if (rg == 0) w4 = *reinterpret_cast<const float4*>(a.norm_w + 4 * cg);
+  const float A_log = a.A_log[h], dt_bias = a.dt_bias[h];
+
+  // ---- the state of head h, read only
+  const uint32_t voff = static_cast<uint32_t>(rg * R) * kRowBytes + static_cast<uint32_t>(cg) * 16u;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.state + (static_cast<long>(b) * a.Hv + h) * (D * D), D * D * 4);
+  float4 hreg[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) hreg[k] = buf_load4<false>(srs, voff, k * kRowBytes);
+  __syncthreads();
+
+  const bool obf = a.out_bf16 != 0;
+  for (int tok = 0; tok < T; ++tok) {
+    // conv + SiLU of the token (tap K-1 on the token itself)
+#pragma unroll
+    for (int m = 0; m < NCPL; ++m) {
+      const int c = t + m * NT;
+      if (c < NCH) {
+        float u = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kMaxConvTaps; ++j)
+          if (j < K) u = fmaf(wt[m][j], s_x[tok + j][c], u);
+        const float v = silu(u);
+        if (c < D) s_q[c] = v;
+        else if (c < 2 * D) s_k[c - D] = v;
+        else s_v[c - 2 * D] = v;
+      }
+    }
+    const long ab = b * a.ab_bs + tok * a.ab_ts + h;
+    const float alpha = gate_alpha(Act<BF>::load(a.dt_raw, ab), dt_bias, A_log);
+    const float beta = gate_beta(Act<BF>::load(a.b_raw, ab));
+    float4 z4 = f4(0.0f);
+    if (rg == 0) z4 = Act<BF>::load4(a.z, b * a.z_bs + tok * a.z_ts + static_cast<long>(h) * D + 4 * cg);
+    __syncthreads();
+    float s3[3] = {0.0f, 0.0f, 0.0f};
+    for (int i = t; i < D; i += NT) {
+      const float q = s_q[i], k = s_k[i];
+      s3[0] = fmaf(q, q, s3[0]);
+      s3[1] = fmaf(k, k, s3[1]);
+      s3[2] = fmaf(q, k, s3[2]);
+    }
+    block_sum<NW, 3>(s3, red);
+    const float rq = 1.0f / sqrtf(s3[0] + a.l2_eps);
+    const float rk = 1.0f / sqrtf(s3[1] + a.l2_eps);
+    const float kq = s3[2] * rq * rk;
+    const long bt = static_cast<long>(b) * T + tok;
+    for (int i = t; i < D; i += NT) {
+      const float kn = s_k[i] * rk;
+      s_q[i] *= rq;
+      s_k[i] = kn;
+      if (h % a.G == 0) a.trail_k[(bt * a.Hk + g) * D + i] = kn;
+    }
+    __syncthreads();
+    const float4 v4 = *reinterpret_cast<const float4*>(s_v + 4 * cg);
+    float4 delta;
+    const float4 o =
+        delta_rule<D, 1, false, false>(hreg, s_k + rg * R, s_q + rg * R, v4, alpha, beta, kq, srs, voff, 0, &delta);
+    if (rg == 0) *reinterpret_cast<float4*>(a.trail_delta + (bt * a.Hv + h) * D + 4 * cg) = delta;
+    if (t == 0) a.trail_alpha[bt * a.Hv + h] = alpha;
+    const float r = head_rms_scale<D, 1>(o, rg == 0, 0, hred, a.rms_eps);
+    if (rg == 0) store_out4(a.out, b * a.out_bs + tok * a.out_ts + static_cast<long>(h) * D + 4 * cg, gated(o, r, w4, z4), obf);
+    __syncthreads();  // s_q, s_k, s_v, red and hred are rewritten by the next token
+  }
+}
+
+// Commit of the accepted prefix: H <- alpha_t H + k_t delta_t^T for t < n = accepted[b]
+// (the expression delta_rule evaluates, so the result is bit-identical to the verify
+// kernel's state after n tokens). n outside [1, T] leaves the sequence untouched.
+template <int D>
+__global__ __launch_bounds__((Layout<D, 1>::NT)) void gdn_commit_kernel(const KernelArgs a) {
+  using L = Layout<D, 1>;
+  constexpr int R = L::R, CGL = L::CGL;
+  constexpr uint32_t kRowBytes = D * 4;
+  const int t = threadIdx.x;
+  const int b = blockIdx.x / a.Hv;
+  const int h = blockIdx.x - b * a.Hv;
+  const int g = h / a.G;
+  const int n = a.accepted[b];
+  if (n < 1 || n > a.T) return;
+  const int cg = (t >> 6) * CGL + (t & (CGL - 1));
+  const int rg = (t & 63) / CGL;
+  const uint32_t voff = static_cast<uint32_t>(rg * R) * kRowBytes + static_cast<uint32_t>(cg) * 16u;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.state + (static_cast<long>(b) * a.Hv + h) * (D * D), D * D * 4);
+  float4 hreg[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) hreg[k] = buf_load4<false>(srs, voff, k * kRowBytes);
+  for (int tok = 0; tok < n; ++tok) {
+    const long bt = static_cast<long>(b) * a.T + tok;
+    const float alpha = a.trail_alpha[bt * a.Hv + h];
+    const float4 delta = *reinterpret_cast<const float4*>(a.trail_delta + (bt * a.Hv + h) * D + 4 * cg);
+    const float* kr = a.trail_k + (bt * a.Hk + g) * D + rg * R;
+#pragma unroll
+    for (int k4 = 0; k4 < R / 4; ++k4) {
+      const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * k4);
+      const float kv[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float4& hh = hreg[4 * k4 + e];
+        hh.x = fmaf(kv[e], delta.x, alpha * hh.x);
+        hh.y = fmaf(kv[e], delta.y, alpha * hh.y);
+        hh.z = fmaf(kv[e], delta.z, alpha * hh.z);
+        hh.w = fmaf(kv[e], delta.w, alpha * hh.w);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k) buf_store4<false>(srs, voff, k * kRowBytes, hreg[k]);
+}
+
+// Conv state after the accepted prefix: row j <- element n + j of (old rows 0..K-2,
+// x_0 .. x_{T-1}), a bit-exact copy; rows in increasing order, so an old row is read
+// before it is overwritten. One thread per (sequence, channel).
+template <bool BF>
+__global__ __launch_bounds__(256) void gdn_conv_commit(const KernelArgs a) {
+  const long C = a.C;
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<long>(a.B) * C) return;
+  const long b = idx / C, c = idx - b * C;
+  const int n = a.accepted[b];
+  if (n < 1 || n > a.T) return;
+  const int Km1 = a.K - 1;
+  for (int j = 0; j < Km1; ++j) {
+    const int e = n + j;
+    const auto v = e < Km1 ? Act<BF>::raw(a.conv_state, (b * Km1 + e) * C + c)
+                           : Act<BF>::raw(a.qkv, b * a.qkv_bs + (e - Km1) * a.qkv_ts + c);
+    Act<BF>::put(a.conv_state, (b * Km1 + j) * C + c, v);
+  }
+}
+
+// ----------------------------------------------------------------------------------
 // launchers
 // ----------------------------------------------------------------------------------
 
@@ -764,7 +945,41 @@ hipError_t launch_seq_t(const KernelArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_verify_d(const KernelArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv));
+  if (a.act_bf16)
+    gdn_verify_kernel<D, true><<<grid, Layout<D, 1>::NT, 0, s>>>(a);
+  else
+    gdn_verify_kernel<D, false><<<grid, Layout<D, 1>::NT, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_commit_d(const KernelArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv));
+  gdn_commit_kernel<D><<<grid, Layout<D, 1>::NT, 0, s>>>(a);
+  const dim3 cgrid(static_cast<unsigned>((static_cast<long>(a.B) * a.C + 255) / 256));
+  if (a.act_bf16)
+    gdn_conv_commit<true><<<cgrid, 256, 0, s>>>(a);
+  else
+    gdn_conv_commit<false><<<cgrid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_verify(int d, const KernelArgs& a, hipStream_t s) {
+  if (d == 128) return launch_verify_d<128>(a, s);
+  if (d == 64) return launch_verify_d<64>(a, s);
+  return launch_verify_d<32>(a, s);
+}
+
+hipError_t launch_commit(int d, const KernelArgs& a, hipStream_t s) {
+  if (d == 128) return launch_commit_d<128>(a, s);
+  if (d == 64) return launch_commit_d<64>(a, s);
+  return launch_commit_d<32>(a, s);
+}
 
 bool step_supported(int d, int p) { return (d == 32 || d == 64 || d == 128) && (p == 1 || p == 2); }
 

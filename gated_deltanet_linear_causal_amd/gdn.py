@@ -21,11 +21,13 @@ import torch
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "GdnShape", "make_shape", "library", "library_path",
     "gdn_conv_update", "gdn_recurrent_step", "gdn_decode_layer", "gdn_decode_layer_pooled", "gdn_sequence",
-    "gdn_sequence_workspace_bytes", "gdn_status_string", "gdn_abi_version", "STATUS",
+    "gdn_sequence_workspace_bytes", "gdn_verify_trail_bytes", "gdn_decode_verify", "gdn_decode_commit",
+    "GDN_MAX_VERIFY_TOKENS", "gdn_status_string", "gdn_abi_version", "STATUS",
 ]
 
 GDN_F32 = 0
 GDN_BF16 = 1
+GDN_MAX_VERIFY_TOKENS = 8
 
 STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE",
           -4: "GDN_ERR_ALIGN", -5: "GDN_ERR_ALIAS", -6: "GDN_ERR_WORKSPACE",
@@ -82,11 +84,14 @@ def library():
         lib.gdn_decode_layer.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.gdn_sequence.argtypes = [S, I32] + [P] * 12 + [ctypes.c_size_t, P]
         lib.gdn_decode_layer_pooled.argtypes = [S, I32] + [P] * 13
+        lib.gdn_decode_verify.argtypes = [S, I32] + [P] * 12 + [ctypes.c_size_t, P]
+        lib.gdn_decode_commit.argtypes = [S, I32] + [P] * 5 + [ctypes.c_size_t, P]
         for f in (lib.gdn_conv_update, lib.gdn_recurrent_step, lib.gdn_decode_layer, lib.gdn_sequence,
-                  lib.gdn_decode_layer_pooled):
+                  lib.gdn_decode_layer_pooled, lib.gdn_decode_verify, lib.gdn_decode_commit):
             f.restype = I32
-        lib.gdn_sequence_workspace_bytes.argtypes = [S, I32]
-        lib.gdn_sequence_workspace_bytes.restype = ctypes.c_size_t
+        for f in (lib.gdn_sequence_workspace_bytes, lib.gdn_verify_trail_bytes):
+            f.argtypes = [S, I32]
+            f.restype = ctypes.c_size_t
         lib.gdn_status_string.argtypes = [I32]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_abi_version.argtypes = []
@@ -105,6 +110,10 @@ def gdn_abi_version() -> int:
 
 def gdn_sequence_workspace_bytes(shape: GdnShape, T: int) -> int:
     return library().gdn_sequence_workspace_bytes(ctypes.byref(shape), int(T))
+
+
+def gdn_verify_trail_bytes(shape: GdnShape, T: int) -> int:
+    return library().gdn_verify_trail_bytes(ctypes.byref(shape), int(T))
 
 
 _ACT = {GDN_F32: torch.float32, GDN_BF16: torch.bfloat16}
@@ -214,3 +223,39 @@ def gdn_sequence(shape: GdnShape, T: int, conv1d_state, state, qkv, conv1d_weigh
         _p(norm_weight, "norm_weight", torch.float32, dv), _p(out, "out", od, B * T * Hv * dv),
         _p(workspace, "workspace"), ctypes.c_size_t(ws_bytes), _stream(stream))
     return _done(st, "gdn_sequence", check)
+
+
+def gdn_decode_verify(shape: GdnShape, T: int, conv1d_state, state, qkv, conv1d_weight, dt_raw, b_raw, z, A_log,
+                      dt_bias, norm_weight, out, trail, stream=None, check=True) -> int:
+    """Outputs of T draft tokens from the current states, which are only read; the
+    per-token updates go to `trail` (a GPU tensor of gdn_verify_trail_bytes bytes)."""
+    s = shape
+    act, od = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
+    B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
+    T = int(T)
+    tr_bytes = 0 if trail is None else trail.numel() * trail.element_size()
+    st = library().gdn_decode_verify(
+        ctypes.byref(s), T, _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
+        _p(state, "state", torch.float32, B * Hv * dk * dv), _p(qkv, "qkv", act, B * T * C),
+        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(dt_raw, "dt_raw", act, B * T * Hv),
+        _p(b_raw, "b_raw", act, B * T * Hv), _p(z, "z", act, B * T * Hv * dv),
+        _p(A_log, "A_log", torch.float32, Hv), _p(dt_bias, "dt_bias", torch.float32, Hv),
+        _p(norm_weight, "norm_weight", torch.float32, dv), _p(out, "out", od, B * T * Hv * dv),
+        _p(trail, "trail"), ctypes.c_size_t(tr_bytes), _stream(stream))
+    return _done(st, "gdn_decode_verify", check)
+
+
+def gdn_decode_commit(shape: GdnShape, T: int, accepted, conv1d_state, state, qkv, trail, stream=None,
+                      check=True) -> int:
+    """Advance sequence b by its first accepted[b] draft tokens (int32 GPU tensor [B])
+    of the preceding gdn_decode_verify call with the same T, qkv and trail."""
+    s = shape
+    act = _ACT.get(s.act_dtype)
+    B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
+    T = int(T)
+    tr_bytes = 0 if trail is None else trail.numel() * trail.element_size()
+    st = library().gdn_decode_commit(
+        ctypes.byref(s), T, _p(accepted, "accepted", torch.int32, B),
+        _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C), _p(state, "state", torch.float32, B * Hv * dk * dv),
+        _p(qkv, "qkv", act, B * T * C), _p(trail, "trail"), ctypes.c_size_t(tr_bytes), _stream(stream))
+    return _done(st, "gdn_decode_commit", check)

@@ -155,6 +155,45 @@ gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_stat
  * shape is invalid). Host-only, no HIP call. */
 size_t gdn_sequence_workspace_bytes(const gdn_shape_t* shape, int32_t T);
 
+/* Speculative decoding: verify T draft tokens, then commit the accepted prefix.
+ * The page "glm5next_dsa/layer.rs" (decode_k, and its lockstep check of the indexer
+ * cache) decodes k tokens per call and rewinds its caches past a rejected draft. A recurrent state cannot be
+ * rewound, so verification leaves both states untouched and records, per token, the
+ * rank-one update of the delta rule (step 7 of "linear_attention.rs"):
+ *   H_t = alpha_t H_{t-1} + k_t delta_t^T,  delta_t = beta_t (v_t - alpha_t H_{t-1}^T k_t),
+ * from which the commit rebuilds the state after any accepted prefix with one read
+ * and one write of the state.
+ *
+ * Trail (device, caller-owned, fp32; gdn_verify_trail_bytes(shape, T) bytes): delta
+ * [B][T][H_v][d_v], then unit-norm k [B][T][H_k][d_k], then alpha [B][T][H_v]. */
+#define GDN_MAX_VERIFY_TOKENS 8
+
+/* Trail bytes for this shape and T (SIZE_MAX if the shape is invalid or T is outside
+ * [0, GDN_MAX_VERIFY_TOKENS]). Host-only, no HIP call. */
+size_t gdn_verify_trail_bytes(const gdn_shape_t* shape, int32_t T);
+
+/* T draft tokens per sequence (0 <= T <= GDN_MAX_VERIFY_TOKENS, else GDN_ERR_SHAPE),
+ * inputs [B][T][...] as for gdn_sequence. out [B][T][H_v*d_v] receives, for every draft
+ * token, what gdn_sequence would give (up to rounding) from the current states; the
+ * states conv1d_state and state are only read. trail_bytes < the query's value ->
+ * GDN_ERR_WORKSPACE. Any H_v / H_k and K. */
+gdn_status_t gdn_decode_verify(const gdn_shape_t* shape, int32_t T, const void* conv1d_state,
+                               const float* state, const void* qkv, const void* conv1d_weight,
+                               const void* dt_raw, const void* b_raw, const void* z,
+                               const float* A_log, const float* dt_bias, const float* norm_weight,
+                               void* out, void* trail, size_t trail_bytes, void* stream);
+
+/* Advance each sequence b by its first n = accepted[b] draft tokens of the preceding
+ * gdn_decode_verify call (same shape, T, qkv and trail): the state becomes the state
+ * after those n tokens (bit-identical to the one the verify kernel computed) and the
+ * conv state is rolled by n tokens (bit-exact copies of the draft's qkv rows).
+ * accepted: [B] int32 (device). n = 0 leaves the sequence untouched, and so does a
+ * value outside [0, T] (device data, not checked on the host). qkv and trail are read,
+ * conv1d_state and state updated in place. */
+gdn_status_t gdn_decode_commit(const gdn_shape_t* shape, int32_t T, const int32_t* accepted,
+                               void* conv1d_state, float* state, const void* qkv, const void* trail,
+                               size_t trail_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. Host-only. */
 const char* gdn_status_string(int32_t status);
 

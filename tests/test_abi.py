@@ -197,3 +197,71 @@ def test_pooled_validation():
     bad = list(args)
     bad[1] = bad[2] = None
     assert lib.gdn_decode_layer_pooled(ctypes.byref(s), 0, *bad, None) == OK
+
+
+def call_verify(shape, T, trail=None, trail_bytes=None, **override):
+    f = Fake()
+    names = ["conv1d_state", "state", "qkv", "conv1d_weight", "dt_raw", "b_raw", "z", "A_log", "dt_bias",
+             "norm_weight", "out"]
+    args = {n: f() for n in names}
+    args.update(override)
+    if trail is None:
+        trail = f()
+    if trail_bytes is None:
+        trail_bytes = gdn.gdn_verify_trail_bytes(shape, T)
+    return gdn.library().gdn_decode_verify(ctypes.byref(shape), T, *[args[n] for n in names], trail,
+                                           ctypes.c_size_t(trail_bytes), None)
+
+
+def call_commit(shape, T, trail=None, trail_bytes=None, **override):
+    f = Fake()
+    names = ["accepted", "conv1d_state", "state", "qkv"]
+    args = {n: f() for n in names}
+    args.update(override)
+    if trail is None:
+        trail = f()
+    if trail_bytes is None:
+        trail_bytes = gdn.gdn_verify_trail_bytes(shape, T)
+    return gdn.library().gdn_decode_commit(ctypes.byref(shape), T, *[args[n] for n in names], trail,
+                                           ctypes.c_size_t(trail_bytes), None)
+
+
+def test_verify_trail_bytes():
+    s = qwen(batch=3)
+    for T in range(0, gdn.GDN_MAX_VERIFY_TOKENS + 1):
+        # delta [B][T][Hv][d] + unit k [B][T][Hk][d] + alpha [B][T][Hv], fp32
+        assert gdn.gdn_verify_trail_bytes(s, T) == 4 * 3 * T * (32 * 128 + 16 * 128 + 32)
+    for T in (-1, gdn.GDN_MAX_VERIFY_TOKENS + 1):
+        assert gdn.gdn_verify_trail_bytes(s, T) == ctypes.c_size_t(-1).value
+
+
+def test_verify_commit_validation():
+    s = qwen()
+    for T in (-1, gdn.GDN_MAX_VERIFY_TOKENS + 1):
+        assert call_verify(s, T, trail_bytes=0) == SHAPE
+        assert call_commit(s, T, trail_bytes=0) == SHAPE
+    # no tokens, or no sequences: nothing to do, pointers may be NULL
+    assert call_verify(s, 0, trail=None, **{n: None for n in ["conv1d_state", "state", "qkv", "out"]}) == OK
+    assert call_commit(qwen(batch=0), 4, **{n: None for n in ["accepted", "conv1d_state", "state", "qkv"]}) == OK
+    need = gdn.gdn_verify_trail_bytes(s, 4)
+    assert call_verify(s, 4, trail_bytes=need - 4) == WORKSPACE
+    assert call_commit(s, 4, trail_bytes=need - 4) == WORKSPACE
+    assert call_verify(s, 4, out=None) == NULL
+    assert call_commit(s, 4, accepted=None) == NULL
+    f = Fake()
+    assert call_commit(s, 4, accepted=ctypes.c_void_p(f().value + 2)) == ALIGN
+    assert call_verify(s, 4, trail=ctypes.c_void_p(f().value + 8)) == ALIGN
+    # the trail is written by verify and may not overlap the output; commit writes the states
+    p = f()
+    assert call_verify(s, 4, trail=p, out=p) == ALIAS
+    q = f()
+    assert call_commit(s, 4, trail=q, state=q) == ALIAS
+
+
+@pytest.mark.skipif(NO_GPU is False, reason="these calls pass validation and would launch on fake pointers")
+def test_verify_reads_states_only():
+    """gdn_decode_verify only reads the states, so they may share memory with other
+    read-only inputs: validation accepts it (the launch then fails on a host without a
+    GPU, the pointers being fake)."""
+    r = Fake()()
+    assert call_verify(qwen(), 4, conv1d_state=r, qkv=r) == HIP
