@@ -253,3 +253,16 @@ void gdn_oracle_sequence(const gdn_oracle_shape* s, int T, double* conv_state, d
       free(o);
     }
 }
+
+/* Page "linear_attention.rs", step 2 (in_proj_qkv, in_proj_z, in_proj_a, in_proj_b:
+ * x_norm -> qkv, z, dt_raw, b_raw) and steps 9-11 (out_proj applied to the gated
+ * output): each is a matrix-vector product per row. Sum in ascending k. */
+void gdn_oracle_linear(int M, int N, int K, const float* x, const float* w, double* y) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) acc += (double)x[(long)m * K + k] * (double)w[(long)n * K + k];
+      y[(long)m * N + n] = acc;
+    }
+}

@@ -51,6 +51,11 @@ void gdn_oracle_sequence(const gdn_oracle_shape* s, int T, double* conv_state, d
                          const float* b_raw, const float* z, const float* A_log,
                          const float* dt_bias, const float* norm_w, double* out);
 
+/* Dense projection y[m][n] = sum_k x[m][k] w[n][k] in fp64 (x [M][K], w [N][K], exact
+ * float values; y [M][N]): the in_proj_* GEMVs of step 2 and the out_proj GEMV of steps
+ * 9-11 of "linear_attention.rs", one GEMV per row m. */
+void gdn_oracle_linear(int M, int N, int K, const float* x, const float* w, double* y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,8 +92,9 @@ def _bind(lib):
     lib.gdn_oracle_gated_rmsnorm.argtypes = [S, P, P, P, P, P]
     lib.gdn_oracle_decode_step.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P]
     lib.gdn_oracle_sequence.argtypes = [S, ctypes.c_int] + [P] * 11
-    for f in (lib.gdn_oracle_conv_update, lib.gdn_oracle_recurrent_step,
-              lib.gdn_oracle_gated_rmsnorm, lib.gdn_oracle_decode_step, lib.gdn_oracle_sequence):
+    lib.gdn_oracle_linear.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P]
+    for f in (lib.gdn_oracle_conv_update, lib.gdn_oracle_recurrent_step, lib.gdn_oracle_gated_rmsnorm,
+              lib.gdn_oracle_decode_step, lib.gdn_oracle_sequence, lib.gdn_oracle_linear):
         f.restype = None
     return lib
 
@@ -219,3 +220,17 @@ def sequence(s: _Shape, T: int, conv_state: np.ndarray, state: np.ndarray, qkv, 
                                 _ptr(conv_w), _ptr(dt_raw), _ptr(b_raw), _ptr(z), _ptr(A_log),
                                 _ptr(dt_bias), _ptr(norm_w), _ptr(out))
     return out
+
+
+def linear(x, w) -> np.ndarray:
+    """y[m][n] = sum_k x[m][k] w[n][k] in fp64 (x [M, K], w [N, K] exact float values):
+    the projections on either side of the layer ("linear_attention.rs", step 2 and
+    steps 9-11). Returns y [M, N] float64."""
+    x, w = _f32(x), _f32(w)
+    if x.ndim != 2 or w.ndim != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("linear: x [M, K] and w [N, K] expected, got %s and %s" % (x.shape, w.shape))
+    M, K = x.shape
+    N = w.shape[0]
+    y = np.zeros((M, N), dtype=np.float64)
+    _load().gdn_oracle_linear(int(M), int(N), int(K), _ptr(x), _ptr(w), _ptr(y))
+    return y

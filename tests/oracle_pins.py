@@ -440,6 +440,29 @@ def pin_permutation_equivariance():
     np.testing.assert_array_equal(cs_g, cs[:, :, ch])
 
 
+def pin_linear_projection():
+    """The projections (step 2 and steps 9-11 of "linear_attention.rs") as
+    y[m][n] = sum_k x[m][k] w[n][k]: identity weights give x back exactly; all-ones x
+    with integer weights w[n][k] = n + k gives the exact sums K n + K (K - 1) / 2; a
+    rectangular random case equals numpy's float64 matrix product of the same values to
+    rounding, and swapping the roles of x and w transposes the result."""
+    rng = np.random.default_rng(7)
+    K = 24
+    x = rng.standard_normal((3, K)).astype(np.float32)
+    np.testing.assert_array_equal(O.linear(x, np.eye(K, dtype=np.float32)), x.astype(np.float64))
+    N = 5
+    w = (np.arange(N)[:, None] + np.arange(K)[None, :]).astype(np.float32)
+    y = O.linear(np.ones((1, K), dtype=np.float32), w)
+    np.testing.assert_array_equal(y[0], K * np.arange(N) + K * (K - 1) / 2)
+    M, N, K = 4, 7, 33
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    y = O.linear(x, w)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(O.linear(w, x), y.T)
+
+
 ALL_PINS = [
     pin_library_composition,
     pin_stepwise_conv_equals_full_conv,
@@ -454,4 +477,5 @@ ALL_PINS = [
     pin_gated_norm,
     pin_resume_and_decode_equivalence,
     pin_permutation_equivariance,
+    pin_linear_projection,
 ]

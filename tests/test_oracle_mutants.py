@@ -50,6 +50,11 @@ MUTANTS = [
      "return (long)g * s->head_k_dim + i;"),
     ("v_offset_one_segment", "return 2L * s->num_k_heads * s->head_k_dim + (long)h * s->head_v_dim + j;",
      "return 1L * s->num_k_heads * s->head_k_dim + (long)h * s->head_v_dim + j;"),
+    ("linear_transposed_weight", "(double)w[(long)n * K + k];", "(double)w[(long)k * N + n];"),
+    ("linear_drops_last_term", "for (int k = 0; k < K; ++k) acc +=", "for (int k = 0; k < K - 1; ++k) acc +="),
+    ("linear_float_accumulation", "      double acc = 0.0;\n      for (int k = 0; k < K; ++k) acc +=",
+     "      float acc = 0.0f;\n      for (int k = 0; k < K; ++k) acc +="),
+    ("linear_x_row_stride", "acc += (double)x[(long)m * K + k]", "acc += (double)x[(long)m * N + k]"),
 ]
 
 
