@@ -475,4 +475,80 @@ gdn_status_t gdn_decode_commit(const gdn_shape_t* shape, int32_t T, const int32_
   return launched(gdn::launch_commit(shape->head_k_dim, a, static_cast<hipStream_t>(stream)));
 }
 
+// Shared checks of the projections: bf16 activations, K a positive multiple of 64.
+gdn_status_t check_proj(const gdn_shape_t* shape, int32_t hidden, int64_t K) {
+  gdn_status_t st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (hidden < 1) return GDN_ERR_SHAPE;
+  if (shape->act_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (hidden % 64 != 0 || K % 64 != 0) return GDN_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(shape->batch) + 31) / 32 > 65535) return GDN_ERR_SHAPE;  // grid rows
+  return GDN_OK;
+}
+
+gdn_status_t gdn_in_proj(const gdn_shape_t* shape, int32_t hidden, const void* x_norm, const void* w_qkv,
+                         const void* w_z, const void* w_a, const void* w_b, void* qkv, void* z_out, void* dt_raw,
+                         void* b_raw, void* stream) {
+  gdn_status_t st = check_proj(shape, hidden, hidden);
+  if (st != GDN_OK) return st;
+  const Sizes z(shape);
+  if (z.B == 0) return GDN_OK;
+  const size_t Hd = static_cast<size_t>(hidden), zd = z.Hv * z.d;
+  const Buf bufs[] = {
+      {x_norm, z.B * Hd * 2, false, 16},
+      {w_qkv, z.C * Hd * 2, false, 16},
+      {w_z, zd * Hd * 2, false, 16},
+      {w_a, z.Hv * Hd * 2, false, 16},
+      {w_b, z.Hv * Hd * 2, false, 16},
+      {qkv, z.B * z.C * 2, true, 16},
+      {z_out, z.B * zd * 2, true, 16},
+      {dt_raw, z.B * z.Hv * 2, true, 2},
+      {b_raw, z.B * z.Hv * 2, true, 2},
+  };
+  if ((st = check_buffers(bufs, 9)) != GDN_OK) return st;
+  gdn::ProjArgs p{};
+  p.M = shape->batch;
+  p.K = hidden;
+  p.x = static_cast<const uint16_t*>(x_norm);
+  p.nseg = 4;
+  const void* ws[4] = {w_qkv, w_z, w_a, w_b};
+  void* ys[4] = {qkv, z_out, dt_raw, b_raw};
+  const long ns[4] = {static_cast<long>(z.C), static_cast<long>(zd), static_cast<long>(z.Hv), static_cast<long>(z.Hv)};
+  for (int i = 0; i < 4; ++i) {
+    p.seg[i].w = static_cast<const uint16_t*>(ws[i]);
+    p.seg[i].y = ys[i];
+    p.seg[i].n = ns[i];
+    p.seg[i].y_bf16 = 1;
+  }
+  (void)hipGetLastError();
+  return launched(gdn::launch_proj(p, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_out_proj(const gdn_shape_t* shape, int32_t hidden, const void* gated, const void* w_out, void* y,
+                          void* stream) {
+  const int64_t K = static_cast<int64_t>(shape ? shape->num_v_heads : 0) * (shape ? shape->head_v_dim : 0);
+  gdn_status_t st = check_proj(shape, hidden, K);
+  if (st != GDN_OK) return st;
+  const Sizes z(shape);
+  if (z.B == 0) return GDN_OK;
+  const size_t Hd = static_cast<size_t>(hidden), zd = z.Hv * z.d;
+  const Buf bufs[] = {
+      {gated, z.B * zd * 2, false, 16},
+      {w_out, Hd * zd * 2, false, 16},
+      {y, z.B * Hd * z.eo, true, 16},
+  };
+  if ((st = check_buffers(bufs, 3)) != GDN_OK) return st;
+  gdn::ProjArgs p{};
+  p.M = shape->batch;
+  p.K = static_cast<int>(zd);
+  p.x = static_cast<const uint16_t*>(gated);
+  p.nseg = 1;
+  p.seg[0].w = static_cast<const uint16_t*>(w_out);
+  p.seg[0].y = y;
+  p.seg[0].n = hidden;
+  p.seg[0].y_bf16 = shape->out_dtype == GDN_BF16;
+  (void)hipGetLastError();
+  return launched(gdn::launch_proj(p, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -63,4 +63,24 @@ constexpr int kMaxVerifyTokens = 8;
 hipError_t launch_verify(int d, const KernelArgs& a, hipStream_t stream);
 hipError_t launch_commit(int d, const KernelArgs& a, hipStream_t stream);
 
+// Projections (gdn_proj.hip): Y_s[m][n] = sum_k X[m][k] W_s[n][k] for up to
+// kMaxProjSegs weight segments sharing X; bf16 operands, fp32 accumulation.
+constexpr int kMaxProjSegs = 4;
+struct ProjSeg {
+  const uint16_t* w;  // [n][K] bf16
+  void* y;            // [M][n] fp32, or bf16 when y_bf16
+  long n;             // rows of W = columns of Y
+  int y_bf16;
+  long row0;          // first row in the concatenation of all segments (set by launch_proj)
+  int tile0;          // first column tile (set by launch_proj)
+};
+struct ProjArgs {
+  int M, K;           // rows of X, contraction length (a multiple of 64)
+  const uint16_t* x;  // [M][K] bf16
+  int nseg;
+  long rows;          // sum of the segments' n (set by launch_proj)
+  ProjSeg seg[kMaxProjSegs];
+};
+hipError_t launch_proj(ProjArgs p, hipStream_t stream);
+
 }  // namespace gdn

@@ -1,0 +1,264 @@
+// Projections on either side of the GDN layer for CDNA4 (gfx950): the in_proj GEMVs
+// of step 2 of the page "linear_attention.rs" (x_norm -> qkv, z, dt_raw, b_raw) and the
+// out_proj GEMV of steps 9-11 (the gated output -> hidden). Both are
+//   Y[m][n] = sum_k X[m][k] W[n][k]      X [M][K] bf16, W [N][K] bf16, fp32 accumulation,
+// for up to four weight segments (W_s, Y_s, N_s) in one launch, so the four in_proj
+// outputs come from one pass over x_norm.
+//
+// M <= 8 (decode at small batch) is weight-streaming: each wave takes NR output rows
+// at a time, every lane reads 16-byte pieces of the rows (coalesced, K contiguous) and
+// multiplies them with the M rows of X held in LDS; a wave reduction finishes each dot
+// product. The bound is HBM: every weight byte is read once.
+// Larger M uses MFMA (v_mfma_f32_16x16x32_bf16) on BM x BN tiles of Y, BK = 64, X and W
+// tiles double-buffered in LDS. Operand fragments are 8 consecutive k per lane (a
+// 16-byte LDS read) for both X and W: the product pairs A and B register slots of the
+// same lane group and element, so any common k order gives the same sum.
+
+#include <algorithm>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ void put(const ProjSeg& s, long m, long n, float v) {
+  if (s.y_bf16)
+    static_cast<uint16_t*>(s.y)[m * s.n + n] = to_bf16(v);
+  else
+    static_cast<float*>(s.y)[m * s.n + n] = v;
+}
+
+// segment of global output row n (uniform across the caller)
+__device__ __forceinline__ int seg_of(const ProjArgs& p, long n) {
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProjSegs; ++i)
+    if (i < p.nseg && n >= p.seg[i].row0) s = i;
+  return s;
+}
+
+// ----------------------------------------------------------------------------------
+// M <= MT rows: weight streaming. Dynamic LDS: X as MT x K bf16 (rows >= M are zero).
+// ----------------------------------------------------------------------------------
+template <int MT, int NR>
+__global__ __launch_bounds__(256) void gdn_proj_gemv(const ProjArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  const int K = p.K, K8 = K / 8;
+  for (int i = threadIdx.x; i < MT * K8; i += 256) {
+    const int m = i / K8, c = i - m * K8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (m < p.M) v = *reinterpret_cast<const u32x4*>(p.x + static_cast<long>(m) * K + 8 * c);
+    *reinterpret_cast<u32x4*>(xs + static_cast<long>(m) * K + 8 * c) = v;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const long waves = static_cast<long>(gridDim.x) * 4;
+  for (long r0 = (static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * NR; r0 < p.rows; r0 += waves * NR) {
+    const uint16_t* wr[NR];
+    bool live[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const long n = r0 + r;
+      live[r] = n < p.rows;
+      const ProjSeg& s = p.seg[seg_of(p, live[r] ? n : r0)];
+      wr[r] = s.w + (live[r] ? n - s.row0 : 0) * static_cast<long>(K);
+    }
+    float acc[NR][MT];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+    for (int c = lane; c < K8; c += 64) {
+      u32x4 wv[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) wv[r] = *reinterpret_cast<const u32x4*>(wr[r] + 8 * c);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + static_cast<long>(m) * K + 8 * c);
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[r][m] = fmaf(lo_bf16(wv[r][e]), lo_bf16(xv[e]), acc[r][m]);
+            acc[r][m] = fmaf(hi_bf16(wv[r][e]), hi_bf16(xv[e]), acc[r][m]);
+          }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float v = acc[r][m];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        acc[r][m] = v;
+      }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (!live[r]) continue;
+        const long n = r0 + r;
+        const ProjSeg& s = p.seg[seg_of(p, n)];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < p.M) put(s, m, n - s.row0, acc[r][m]);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------
+// MFMA tiles. Grid: x = N-tiles of all segments (tile0 of each segment), y = M-tiles.
+// 4 waves as 2 x 2, each a (BM/2) x (BN/2) block of 16x16 accumulator tiles.
+// ----------------------------------------------------------------------------------
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void gdn_proj_mfma(const ProjArgs p) {
+  constexpr int BK = 64, LD = BK + 8;                 // LDS row stride 144 bytes
+  constexpr int TI = BM / 32, TJ = BN / 32;           // 16x16 tiles per wave
+  constexpr int XC = BM * BK / 8 / 256, WC = BN * BK / 8 / 256;  // 16-byte pieces per thread
+  static_assert(XC >= 1 && WC >= 1, "tile too small for 256 threads");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][LD];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN][LD];
+
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProjSegs; ++i)
+    if (i < p.nseg && static_cast<int>(blockIdx.x) >= p.seg[i].tile0) si = i;
+  const ProjSeg& s = p.seg[si];
+  const long n0 = static_cast<long>(blockIdx.x - s.tile0) * BN;
+  const long m0 = static_cast<long>(blockIdx.y) * BM;
+  const int K = p.K;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
+  const int wm = w >> 1, wn = w & 1;
+
+  // global -> register pieces: piece i of a tile is row i / 8, 8 bf16 at column 8 (i % 8)
+  u32x4 xr[XC], wr_[WC];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+      const int i = t + 256 * c, row = i >> 3, col = 8 * (i & 7);
+      const long m = m0 + row;
+      xr[c] = m < p.M ? *reinterpret_cast<const u32x4*>(p.x + m * K + k0 + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int c = 0; c < WC; ++c) {
+      const int i = t + 256 * c, row = i >> 3, col = 8 * (i & 7);
+      const long n = n0 + row;
+      wr_[c] = n < s.n ? *reinterpret_cast<const u32x4*>(s.w + n * K + k0 + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+      const int i = t + 256 * c;
+      *reinterpret_cast<u32x4*>(&xs[buf][i >> 3][8 * (i & 7)]) = xr[c];
+    }
+#pragma unroll
+    for (int c = 0; c < WC; ++c) {
+      const int i = t + 256 * c;
+      *reinterpret_cast<u32x4*>(&ws[buf][i >> 3][8 * (i & 7)]) = wr_[c];
+    }
+  };
+
+  f32x4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nk = K / BK;
+  load(0);
+  stash(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load((kt + 1) * BK);  // next tile in flight during the products
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      bf16x8 a[TI], bb[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&xs[cur][wm * (BM / 2) + 16 * i + c16][32 * kk + 8 * q]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        bb[j] = *reinterpret_cast<const bf16x8*>(&ws[cur][wn * (BN / 2) + 16 * j + c16][32 * kk + 8 * q]);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      stash(cur ^ 1);  // the other buffer was last read before the previous barrier
+      __syncthreads();
+    }
+  }
+  // accumulator tile (i, j): lane holds rows 4q + r, column c16
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const long n = n0 + wn * (BN / 2) + 16 * j + c16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const long m = m0 + wm * (BM / 2) + 16 * i + 4 * q + r;
+        if (m < p.M && n < s.n) put(s, m, n, acc[i][j][r]);
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_proj(ProjArgs p, hipStream_t st) {
+  long rows = 0;
+  for (int i = 0; i < p.nseg; ++i) {
+    p.seg[i].row0 = rows;
+    rows += p.seg[i].n;
+  }
+  p.rows = rows;
+  if (p.M <= 8) {
+    constexpr int NR = 2;
+    const long groups = (rows + NR - 1) / NR;
+    const unsigned grid = static_cast<unsigned>(std::min<long>((groups + 3) / 4, 2048));
+    const size_t lds = (p.M <= 1 ? 1 : p.M <= 2 ? 2 : p.M <= 4 ? 4 : 8) * static_cast<size_t>(p.K) * 2;
+    if (p.M <= 1)
+      gdn_proj_gemv<1, NR><<<grid, 256, lds, st>>>(p);
+    else if (p.M <= 2)
+      gdn_proj_gemv<2, NR><<<grid, 256, lds, st>>>(p);
+    else if (p.M <= 4)
+      gdn_proj_gemv<4, NR><<<grid, 256, lds, st>>>(p);
+    else
+      gdn_proj_gemv<8, NR><<<grid, 256, lds, st>>>(p);
+    return hipGetLastError();
+  }
+  // 32 x 32 tiles up to M = 64 (more workgroups for the weight stream), 64 x 64 above
+  const bool small = p.M <= 64;
+  const int BM = small ? 32 : 64, BN = small ? 32 : 64;
+  int tiles = 0;
+  for (int i = 0; i < p.nseg; ++i) {
+    p.seg[i].tile0 = tiles;
+    tiles += static_cast<int>((p.seg[i].n + BN - 1) / BN);
+  }
+  const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>((p.M + BM - 1) / BM));
+  if (small)
+    gdn_proj_mfma<32, 32><<<grid, 256, 0, st>>>(p);
+  else
+    gdn_proj_mfma<64, 64><<<grid, 256, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

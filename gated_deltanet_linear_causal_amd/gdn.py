@@ -22,7 +22,7 @@ __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "GdnShape", "make_shape", "library", "library_path",
     "gdn_conv_update", "gdn_recurrent_step", "gdn_decode_layer", "gdn_decode_layer_pooled", "gdn_sequence",
     "gdn_sequence_workspace_bytes", "gdn_verify_trail_bytes", "gdn_decode_verify", "gdn_decode_commit",
-    "GDN_MAX_VERIFY_TOKENS", "gdn_status_string", "gdn_abi_version", "STATUS",
+    "GDN_MAX_VERIFY_TOKENS", "gdn_in_proj", "gdn_out_proj", "gdn_status_string", "gdn_abi_version", "STATUS",
 ]
 
 GDN_F32 = 0
@@ -86,8 +86,11 @@ def library():
         lib.gdn_decode_layer_pooled.argtypes = [S, I32] + [P] * 13
         lib.gdn_decode_verify.argtypes = [S, I32] + [P] * 12 + [ctypes.c_size_t, P]
         lib.gdn_decode_commit.argtypes = [S, I32] + [P] * 5 + [ctypes.c_size_t, P]
+        lib.gdn_in_proj.argtypes = [S, I32] + [P] * 10
+        lib.gdn_out_proj.argtypes = [S, I32] + [P] * 4
         for f in (lib.gdn_conv_update, lib.gdn_recurrent_step, lib.gdn_decode_layer, lib.gdn_sequence,
-                  lib.gdn_decode_layer_pooled, lib.gdn_decode_verify, lib.gdn_decode_commit):
+                  lib.gdn_decode_layer_pooled, lib.gdn_decode_verify, lib.gdn_decode_commit, lib.gdn_in_proj,
+                  lib.gdn_out_proj):
             f.restype = I32
         for f in (lib.gdn_sequence_workspace_bytes, lib.gdn_verify_trail_bytes):
             f.argtypes = [S, I32]
@@ -259,3 +262,29 @@ def gdn_decode_commit(shape: GdnShape, T: int, accepted, conv1d_state, state, qk
         _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C), _p(state, "state", torch.float32, B * Hv * dk * dv),
         _p(qkv, "qkv", act, B * T * C), _p(trail, "trail"), ctypes.c_size_t(tr_bytes), _stream(stream))
     return _done(st, "gdn_decode_commit", check)
+
+
+def gdn_in_proj(shape: GdnShape, hidden: int, x_norm, w_qkv, w_z, w_a, w_b, qkv, z, dt_raw, b_raw, stream=None,
+                check=True) -> int:
+    """x_norm [B, hidden] -> qkv, z, dt_raw, b_raw (bf16), weights [outputs, hidden] bf16."""
+    s = shape
+    bf = torch.bfloat16
+    B, C, Hv, dv, H = s.batch, s.channels, s.num_v_heads, s.head_v_dim, int(hidden)
+    st = library().gdn_in_proj(
+        ctypes.byref(s), H, _p(x_norm, "x_norm", bf, B * H), _p(w_qkv, "w_qkv", bf, C * H),
+        _p(w_z, "w_z", bf, Hv * dv * H), _p(w_a, "w_a", bf, Hv * H), _p(w_b, "w_b", bf, Hv * H),
+        _p(qkv, "qkv", bf, B * C), _p(z, "z", bf, B * Hv * dv), _p(dt_raw, "dt_raw", bf, B * Hv),
+        _p(b_raw, "b_raw", bf, B * Hv), _stream(stream))
+    return _done(st, "gdn_in_proj", check)
+
+
+def gdn_out_proj(shape: GdnShape, hidden: int, gated, w_out, y, stream=None, check=True) -> int:
+    """gated [B, H_v*d_v] bf16 -> y [B, hidden] (out dtype), w_out [hidden, H_v*d_v] bf16."""
+    s = shape
+    bf = torch.bfloat16
+    od = _ACT.get(s.out_dtype)
+    B, Hv, dv, H = s.batch, s.num_v_heads, s.head_v_dim, int(hidden)
+    st = library().gdn_out_proj(
+        ctypes.byref(s), H, _p(gated, "gated", bf, B * Hv * dv), _p(w_out, "w_out", bf, H * Hv * dv),
+        _p(y, "y", od, B * H), _stream(stream))
+    return _done(st, "gdn_out_proj", check)

@@ -21,6 +21,12 @@ Recipe (all draws from ``numpy.random.default_rng(seed)`` in this order):
 Normal draws are made in float32 (``standard_normal(dtype=float32)``) and scaled;
 where the activation dtype is bf16 they are rounded RNE to bf16. Recurrent state
 and A_log, dt_bias, norm_w stay fp32.
+
+Projections around the layer (``generate_projections``, own seed): x_norm [B, hidden]
+~ N(0, 1), then w_qkv [C, hidden], w_z [H_v*d_v, hidden], w_a [H_v, hidden], w_b
+[H_v, hidden] ~ N(0, 1/hidden) and w_out [hidden, H_v*d_v] ~ N(0, 1/(H_v*d_v)), all
+rounded to bf16. The pages do not give the model's hidden size; HIDDEN is the value
+used for measurements.
 """
 
 from __future__ import annotations
@@ -182,4 +188,26 @@ def generate(cfg: GdnConfig, steps: Optional[int] = None) -> Dict[str, np.ndarra
             a[s] = _act(_normal(rng, (B, Hv), 1.0), ad)
             b[s] = _act(_normal(rng, (B, Hv), 1.0), ad)
         out["qkv"], out["z"], out["a"], out["b"] = q, z, a, b
+    return out
+
+
+HIDDEN = 2048
+
+
+def generate_projections(cfg: GdnConfig, hidden: int = HIDDEN, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Synthetic input and weights of the in_proj / out_proj steps (bf16 bits, uint16):
+    ``x_norm`` [B, hidden], ``w_qkv`` [C, hidden], ``w_z`` [H_v*d_v, hidden], ``w_a`` and
+    ``w_b`` [H_v, hidden], ``w_out`` [hidden, H_v*d_v]. Weights are scaled by
+    1/sqrt(fan_in) so the outputs are O(1)."""
+    rng = np.random.default_rng(cfg.seed + 7919 if seed is None else seed)
+    B, Hv, dv, C = cfg.batch, cfg.num_v_heads, cfg.head_v_dim, cfg.channels
+    zd = Hv * dv
+    out: Dict[str, np.ndarray] = {}
+    out["x_norm"] = _act(_normal(rng, (B, hidden), 1.0), "bf16")
+    s_in = 1.0 / math.sqrt(hidden)
+    out["w_qkv"] = _act(_normal(rng, (C, hidden), s_in), "bf16")
+    out["w_z"] = _act(_normal(rng, (zd, hidden), s_in), "bf16")
+    out["w_a"] = _act(_normal(rng, (Hv, hidden), s_in), "bf16")
+    out["w_b"] = _act(_normal(rng, (Hv, hidden), s_in), "bf16")
+    out["w_out"] = _act(_normal(rng, (hidden, zd), 1.0 / math.sqrt(zd)), "bf16")
     return out

@@ -194,6 +194,29 @@ gdn_status_t gdn_decode_commit(const gdn_shape_t* shape, int32_t T, const int32_
                                void* conv1d_state, float* state, const void* qkv, const void* trail,
                                size_t trail_bytes, void* stream);
 
+/* The projections on either side of the layer, with caller-provided (for example
+ * synthetic) weights: step 2 of "linear_attention.rs" (in_proj_qkv, in_proj_z and the
+ * fused in_proj_a / in_proj_b GEMVs of x_norm) and steps 9-11 (out_proj applied to
+ * silu(z) (.) y_norm, which gdn_decode_layer already writes as `out`). Each output is
+ * Y[b][n] = sum_k X[b][k] W[n][k] with bf16 X and W, fp32 accumulation and one final
+ * rounding to the output dtype (round to nearest even for bf16). One launch each.
+ * Requirements: act_dtype == GDN_BF16 and the contraction length (hidden for
+ * gdn_in_proj, H_v*d_v for gdn_out_proj) a multiple of 64, else GDN_ERR_UNSUPPORTED;
+ * hidden < 1 -> GDN_ERR_SHAPE. Alignment: 16 bytes for every buffer except dt_raw and
+ * b_raw (2). Weights are row-major [outputs][inputs] (K contiguous). */
+
+/* x_norm [B][hidden] bf16 -> qkv [B][C], z [B][H_v*d_v], dt_raw [B][H_v], b_raw
+ * [B][H_v], all bf16 (the act-dtype inputs of gdn_decode_layer), with w_qkv [C][hidden],
+ * w_z [H_v*d_v][hidden], w_a and w_b [H_v][hidden] (bf16). */
+gdn_status_t gdn_in_proj(const gdn_shape_t* shape, int32_t hidden, const void* x_norm, const void* w_qkv,
+                         const void* w_z, const void* w_a, const void* w_b, void* qkv, void* z,
+                         void* dt_raw, void* b_raw, void* stream);
+
+/* gated [B][H_v*d_v] bf16 (gdn_decode_layer's out in bf16) -> y [B][hidden] in
+ * out_dtype, with w_out [hidden][H_v*d_v] bf16. */
+gdn_status_t gdn_out_proj(const gdn_shape_t* shape, int32_t hidden, const void* gated, const void* w_out,
+                          void* y, void* stream);
+
 /* Static, NUL-terminated description of a status code. Host-only. */
 const char* gdn_status_string(int32_t status);
 

@@ -265,3 +265,42 @@ def test_verify_reads_states_only():
     GPU, the pointers being fake)."""
     r = Fake()()
     assert call_verify(qwen(), 4, conv1d_state=r, qkv=r) == HIP
+
+
+def call_in_proj(shape, hidden, **override):
+    f = Fake()
+    names = ["x_norm", "w_qkv", "w_z", "w_a", "w_b", "qkv", "z", "dt_raw", "b_raw"]
+    args = {n: f() for n in names}
+    args.update(override)
+    return gdn.library().gdn_in_proj(ctypes.byref(shape), hidden, *[args[n] for n in names], None)
+
+
+def call_out_proj(shape, hidden, **override):
+    f = Fake()
+    names = ["gated", "w_out", "y"]
+    args = {n: f() for n in names}
+    args.update(override)
+    return gdn.library().gdn_out_proj(ctypes.byref(shape), hidden, *[args[n] for n in names], None)
+
+
+def test_projection_validation():
+    s = qwen()
+    assert call_in_proj(s, 0) == SHAPE
+    assert call_out_proj(s, -64) == SHAPE
+    assert call_in_proj(s, 2000) == UNSUPPORTED      # hidden not a multiple of 64
+    assert call_out_proj(s, 100) == UNSUPPORTED
+    assert call_in_proj(qwen(act_dtype="f32"), 2048) == UNSUPPORTED
+    assert call_out_proj(qwen(act_dtype="f32"), 2048) == UNSUPPORTED
+    # out_proj contracts over H_v * d_v, which must also be a multiple of 64
+    assert call_out_proj(qwen(num_k_heads=1, num_v_heads=1, head_k_dim=32, head_v_dim=32), 2048) == UNSUPPORTED
+    assert call_in_proj(s, 2048, w_z=None) == NULL
+    assert call_out_proj(s, 2048, y=None) == NULL
+    assert call_in_proj(qwen(batch=0), 2048, **{n: None for n in ["x_norm", "qkv", "z", "dt_raw", "b_raw"]}) == OK
+    f = Fake()
+    assert call_in_proj(s, 2048, x_norm=ctypes.c_void_p(f().value + 8)) == ALIGN
+    assert call_in_proj(s, 2048, w_a=ctypes.c_void_p(f().value + 2)) == ALIGN
+    p = f()
+    assert call_in_proj(s, 2048, qkv=p, z=p) == ALIAS
+    q = f()
+    assert call_out_proj(s, 2048, gated=q, y=q) == ALIAS
+    assert call_in_proj(qwen(batch=65535 * 32 + 1), 2048) == SHAPE
