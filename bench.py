@@ -7,7 +7,8 @@ the Qwen3.5-style layer (H_k = 16, H_v = 32, d_k = d_v = 128, K = 4, bf16 activa
 fp32 state) at B = 512: its 1 GiB of state exceeds the 256 MB Infinity Cache, so the
 bandwidth figure is a cold-HBM one. 32 distinct steps of inputs are drawn and reused
 cyclically; the state keeps evolving. B = 1 and B = 64 are reported in "sweep", the
-B = 8 x T = 4096 multi-token call in "sequence".
+B = 8 x T = 4096 multi-token call in "sequence", speculative verification (B = 64,
+4 draft tokens) in "verify", the projections around the layer in "proj".
 
 Prints one JSON line. `value` = sequences x steps / second (seq-layer steps/s).
 The roofline figure uses algorithmic bytes (state read once and written once, every
@@ -36,7 +37,9 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN decode steps/s (seq·layer) at B=1/64/512 + achieved HBM GB/s vs peak"
 UNIT = "seq·layer steps/s"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_linear_causal_amd", "csrc", "gdn_kernels.hip")
+# sources the decode kernel is built from (the traffic record is keyed on them)
+KERNEL_SRCS = [os.path.join(ROOT, "gated_deltanet_linear_causal_amd", "csrc", f)
+               for f in ("gdn_kernels.hip", "gdn_device.h", "gdn_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdn_decode_fused_B512_traffic.txt")
 
 
@@ -53,7 +56,10 @@ def algorithmic_bytes(cfg, T=1) -> int:
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile():
@@ -166,6 +172,101 @@ def time_sequence(cfg, d, reps, torch, gdn):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def chunk_flops(cfg, C=32):
+    """Useful flops of the chunked form per chunk and v-head (d = d_k = d_v): K K^T and
+    Q K^T (2 C^2 d each), K H0 and Q H0 (2 C d^2 each), P Delta (2 C^2 d) and K^T E Delta
+    (2 C d^2). The kernel evaluates each product as three fp16 MFMAs (split operands)."""
+    d = cfg.head_k_dim
+    return 2 * (2 * C * C * d) + 2 * (2 * C * d * d) + 2 * C * C * d + 2 * C * d * d
+
+
+def time_events(fn, reps, torch, warmup=3):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def time_verify(cfg, T, reps, torch, gdn):
+    """gdn_decode_verify of T draft tokens per sequence, then gdn_decode_commit of all
+    T (the commit's worst case: every state rewritten)."""
+    from gated_deltanet_linear_causal_amd import inputs as I
+    c = cfg.with_(mode="sequence", steps=T)
+    _, d = build_inputs(c, T, torch)
+    s = gdn.make_shape(c.batch, c.num_k_heads, c.num_v_heads, c.head_k_dim, c.head_v_dim, c.conv_kernel,
+                       c.l2_eps, c.rms_eps, c.act_dtype, "f32")
+    out = torch.empty((c.batch, T, c.z_dim), dtype=torch.float32, device="cuda")
+    trail = torch.empty(gdn.gdn_verify_trail_bytes(s, T), dtype=torch.uint8, device="cuda")
+    acc = torch.full((c.batch,), T, dtype=torch.int32, device="cuda")
+
+    def verify(st):
+        gdn.gdn_decode_verify(s, T, d["conv_state"], d["state"], d["qkv"], d["conv_w"], d["a"], d["b"], d["z"],
+                              d["A_log"], d["dt_bias"], d["norm_w"], out, trail, stream=st)
+
+    def commit(st):
+        gdn.gdn_decode_commit(s, T, acc, d["conv_state"], d["state"], d["qkv"], trail, stream=st)
+
+    vsec = time_events(verify, reps, torch)
+    csec = time_events(commit, reps, torch)
+    B, Hk, Hv, dk, dv, K, C = c.batch, c.num_k_heads, c.num_v_heads, c.head_k_dim, c.head_v_dim, c.conv_kernel, c.channels
+    trail_b = 4 * B * T * (Hv * dv + Hk * dk + Hv)
+    vbytes = B * (Hv * dk * dv * 4 + (K - 1) * C * 2 + T * (C * 2 + Hv * dv * 2 + 2 * Hv * 2 + Hv * dv * 4)) + trail_b
+    cbytes = B * (2 * Hv * dk * dv * 4 + 2 * (K - 1) * C * 2 + min(T, K - 1) * C * 2) + trail_b
+    del d, out, trail
+    return {"workload": "B=%d, T=%d draft tokens: gdn_decode_verify, then gdn_decode_commit of all T" % (B, T),
+            "verify_us": round(vsec * 1e6, 2), "commit_us": round(csec * 1e6, 2),
+            "draft_tokens_per_s": round(B * T / vsec, 1),
+            "verify_GB_s": round(vbytes / vsec / 1e9, 1), "commit_GB_s": round(cbytes / csec / 1e9, 1),
+            "verify_algorithmic_bytes": vbytes, "commit_algorithmic_bytes": cbytes}
+
+
+def time_proj(cfg, B, reps, torch, gdn):
+    """gdn_in_proj and gdn_out_proj at batch B (hidden = inputs.HIDDEN), synthetic
+    bf16 weights; bytes = weights + x + y, flops = 2 B N K."""
+    import numpy as np
+    from gated_deltanet_linear_causal_amd import inputs as I
+    c = cfg.with_(batch=B)
+    H = I.HIDDEN
+    P = I.generate_projections(c, H)
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    w = {k: dv(v) for k, v in P.items()}
+    s = gdn.make_shape(B, c.num_k_heads, c.num_v_heads, c.head_k_dim, c.head_v_dim, c.conv_kernel,
+                       c.l2_eps, c.rms_eps, "bf16", "bf16")
+    C, Hv, zd = c.channels, c.num_v_heads, c.z_dim
+    qkv = torch.empty((B, C), dtype=torch.bfloat16, device="cuda")
+    z = torch.empty((B, zd), dtype=torch.bfloat16, device="cuda")
+    a = torch.empty((B, Hv), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty((B, Hv), dtype=torch.bfloat16, device="cuda")
+    gated = torch.randn((B, zd), device="cuda").to(torch.bfloat16)
+    y = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+
+    def inp(st):
+        gdn.gdn_in_proj(s, H, w["x_norm"], w["w_qkv"], w["w_z"], w["w_a"], w["w_b"], qkv, z, a, b, stream=st)
+
+    def outp(st):
+        gdn.gdn_out_proj(s, H, gated, w["w_out"], y, stream=st)
+
+    isec = time_events(inp, reps, torch)
+    osec = time_events(outp, reps, torch)
+    n_in = C + zd + 2 * Hv
+    ib = 2 * (n_in * H + B * H + B * n_in)
+    ob = 2 * (H * zd + B * zd + B * H)
+    res = {}
+    for name, sec, nb, fl in (("in_proj", isec, ib, 2 * B * n_in * H), ("out_proj", osec, ob, 2 * B * H * zd)):
+        res[name] = {"us": round(sec * 1e6, 2), "GB_s": round(nb / sec / 1e9, 1),
+                     "hbm_frac": round(nb / sec / 1e9 / HBM_PEAK_GBS, 4), "TFLOP_s": round(fl / sec / 1e12, 2),
+                     "mfma_frac": round(fl / sec / 1e12 / 2500.0, 4), "algorithmic_bytes": nb, "flops": fl}
+    del w, qkv, z, a, b, gated, y
+    return res
 
 
 def cpu_baseline(cfg, data, target_s=10.0):
@@ -329,10 +430,20 @@ def main():
         _, dd = build_inputs(c, c.steps, torch)
         ssec = time_sequence(c, dd, 2, torch, gdn)
         b = algorithmic_bytes(c, T=c.steps)
-        result["sequence"] = {"workload": "B=8 x T=4096 gdn_sequence", "ms": round(ssec * 1e3, 3),
-                              "tokens_per_s": round(c.batch * c.steps / ssec, 1),
-                              "GB_s": round(b / ssec / 1e9, 1), "hbm_frac": round(b / ssec / 1e9 / HBM_PEAK_GBS, 4)}
+        fl = chunk_flops(c) * ((c.steps + 31) // 32) * c.batch * c.num_v_heads
+        result["sequence"] = {"workload": "B=8 x T=4096 gdn_sequence (chunked MFMA form, 32-token chunks)",
+                              "ms": round(ssec * 1e3, 3), "tokens_per_s": round(c.batch * c.steps / ssec, 1),
+                              "GB_s": round(b / ssec / 1e9, 1), "hbm_frac": round(b / ssec / 1e9 / HBM_PEAK_GBS, 4),
+                              "useful_TFLOP_s": round(fl / ssec / 1e12, 2),
+                              "mfma_issued_TFLOP_s": round(3 * fl / ssec / 1e12, 2),
+                              "mfma_frac": round(3 * fl / ssec / 1e12 / 2500.0, 4)}
         del dd
+        torch.cuda.empty_cache()
+        result["verify"] = time_verify(I.config(2), 4, 50, torch, gdn)
+        torch.cuda.empty_cache()
+        result["proj"] = {"hidden": I.HIDDEN}
+        for B in (1, 64, 512):
+            result["proj"]["B%d" % B] = time_proj(I.config(2), B, 50, torch, gdn)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, data)

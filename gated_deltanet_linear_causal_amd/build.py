@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_kernels.hip", "gdn_chunked.hip", "gdn_proj.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_kernels.hip", "gdn_verify.hip", "gdn_chunked.hip", "gdn_proj.hip"]
 ARCH = "gfx950"
 
 
