@@ -27,7 +27,9 @@ __global__ __launch_bounds__((Layout<D, 1>::NT)) void gdn_verify_kernel(const Ke
   constexpr int kTM = kMaxVerifyTokens;
   constexpr int kRows = kMaxConvTaps - 1 + kTM;
   constexpr uint32_t kRowBytes = D * 4;
-  __shared__ __attribute__((aligned(16))) float s_x[kRows][NCH];  // K-1 conv-state rows, then T token rows
+  using raw_t = typename Act<BF>::raw_t;  // stored values, widened on use
+  __shared__ __attribute__((aligned(16))) raw_t s_x[kRows][NCH];  // K-1 conv-state rows, then T token rows
+  __shared__ __attribute__((aligned(16))) raw_t s_w[NCH * kMaxConvTaps];  // taps [NCH][K]
   __shared__ __attribute__((aligned(16))) float s_q[kTM][D];
   __shared__ __attribute__((aligned(16))) float s_k[kTM][D];
   __shared__ __attribute__((aligned(16))) float s_v[kTM][D];
@@ -36,8 +38,9 @@ __global__ __launch_bounds__((Layout<D, 1>::NT)) void gdn_verify_kernel(const Ke
   __shared__ float red[NW][3 * kTM];    // per-wave partial sums
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int b = blockIdx.x / a.Hv;
-  const int h = blockIdx.x - b * a.Hv;
+  const int bh = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x));  // (b, h), uniform
+  const int b = bh / a.Hv;
+  const int h = bh - b * a.Hv;
   const int g = h / a.G;
   const int cg = (t >> 6) * CGL + (t & (CGL - 1));
   const int rg = (t & 63) / CGL;
@@ -49,11 +52,56 @@ __global__ __launch_bounds__((Layout<D, 1>::NT)) void gdn_verify_kernel(const Ke
                  : (c < 2 * D ? static_cast<long>(a.Hk + g) * D + (c - D) : static_cast<long>(2 * a.Hk + h) * D + (c - 2 * D));
   };
 
-  // ---- A. conv inputs into LDS, then conv + SiLU of every (token, channel), gates
-  for (int c = t; c < NCH; c += NT) {
-    const long gc = chan(c);
-    for (int j = 0; j < K - 1; ++j) s_x[j][c] = Act<BF>::load(a.conv_state, (static_cast<long>(b) * (K - 1) + j) * C + gc);
-    for (int tok = 0; tok < T; ++tok) s_x[K - 1 + tok][c] = Act<BF>::load(a.qkv, b * a.qkv_bs + tok * a.qkv_ts + gc);
+  // ---- A. conv inputs and taps into LDS, then conv + SiLU of every (token, channel), gates
+  {
+    // 16-byte pieces of 8 consecutive unit channels (a segment's channels are
+    // consecutive in a qkv row and in conv1d_weight), every load issued before the
+    // first LDS store
+    constexpr int kPieces = NCH / 8;                                   // per row
+    constexpr int kXPer = (kRows * kPieces + NT - 1) / NT;
+    constexpr int kWChunks = NCH * kMaxConvTaps / 8;                   // taps, 8 per chunk
+    constexpr int kWPer = (kWChunks + NT - 1) / NT;
+    constexpr int kE = BF ? 1 : 2;                                     // 16-byte words per 8 elements
+    const int nrow = K - 1 + T, nw = NCH * K / 8;
+    u32x4 xr[kXPer][kE], wr[kWPer][kE];
+    auto ld8 = [&](const void* base, long elem, u32x4(&dst)[kE]) {
+#pragma unroll
+      for (int e = 0; e < kE; ++e)
+        dst[e] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + (elem * (BF ? 2 : 4)) + 16 * e);
+    };
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int it = t + i * NT, j = it / kPieces, pc = it - j * kPieces;
+      if (j < nrow) {
+        const long gc = chan(8 * pc);
+        if (j < K - 1)
+          ld8(a.conv_state, (static_cast<long>(b) * (K - 1) + j) * C + gc, xr[i]);
+        else
+          ld8(a.qkv, b * a.qkv_bs + (j - (K - 1)) * a.qkv_ts + gc, xr[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int it = t + i * NT;
+      if (it < nw) {
+        const int per_seg = D * K / 8, sg = it / per_seg, off = 8 * (it - sg * per_seg);
+        ld8(a.conv_w, chan(sg * D) * K + off, wr[i]);
+      }
+    }
+    auto put8 = [&](raw_t* dst, const u32x4(&src)[kE]) {  // 8 stored values, as they are
+#pragma unroll
+      for (int e = 0; e < kE; ++e) *reinterpret_cast<u32x4*>(dst + e * (16 / sizeof(raw_t))) = src[e];
+    };
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int it = t + i * NT, j = it / kPieces, pc = it - j * kPieces;
+      if (j < nrow) put8(&s_x[j][8 * pc], xr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int it = t + i * NT;
+      if (it < nw) put8(&s_w[8 * it], wr[i]);
+    }
   }
   if (t < T) {
     const long ab = b * a.ab_bs + t * a.ab_ts + h;
@@ -63,23 +111,19 @@ __global__ __launch_bounds__((Layout<D, 1>::NT)) void gdn_verify_kernel(const Ke
   // the state of head h (read only): issued after the small loads (vmcnt retires in
   // order), in flight during the conv and the norms
   const uint32_t voff = static_cast<uint32_t>(rg * R) * kRowBytes + static_cast<uint32_t>(cg) * 16u;
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.state + (static_cast<long>(b) * a.Hv + h) * (D * D), D * D * 4);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.state + static_cast<long>(bh) * (D * D), D * D * 4);
   float4 hreg[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) hreg[k] = buf_load4<false>(srs, voff, k * kRowBytes);
   __syncthreads();
   for (int c = t; c < NCH; c += NT) {
-    const long gc = chan(c);
-    float wt[kMaxConvTaps];
-#pragma unroll
-    for (int j = 0; j < kMaxConvTaps; ++j) wt[j] = j < K ? Act<BF>::load(a.conv_w, gc * K + j) : 0.0f;
     float(*dst)[D] = c < D ? s_q : (c < 2 * D ? s_k : s_v);
     const int e = c < D ? c : (c < 2 * D ? c - D : c - 2 * D);
     for (int tok = 0; tok < T; ++tok) {
       float u = 0.0f;
 #pragma unroll
       for (int j = 0; j < kMaxConvTaps; ++j)
-        if (j < K) u = fmaf(wt[j], s_x[tok + j][c], u);  // tap K-1 on the token itself
+        if (j < K) u = fmaf(Act<BF>::f(s_w[c * K + j]), Act<BF>::f(s_x[tok + j][c]), u);  // tap K-1 on the token itself
       dst[tok][e] = silu(u);
     }
   }
@@ -176,15 +220,16 @@ __global__ __launch_bounds__((Layout<D, 1>::NT)) void gdn_commit_kernel(const Ke
   constexpr int R = L::R, CGL = L::CGL;
   constexpr uint32_t kRowBytes = D * 4;
   const int t = threadIdx.x;
-  const int b = blockIdx.x / a.Hv;
-  const int h = blockIdx.x - b * a.Hv;
+  const int bh = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x));  // (b, h), uniform
+  const int b = bh / a.Hv;
+  const int h = bh - b * a.Hv;
   const int g = h / a.G;
   const int n = a.accepted[b];
   if (n < 1 || n > a.T) return;
   const int cg = (t >> 6) * CGL + (t & (CGL - 1));
   const int rg = (t & 63) / CGL;
   const uint32_t voff = static_cast<uint32_t>(rg * R) * kRowBytes + static_cast<uint32_t>(cg) * 16u;
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.state + (static_cast<long>(b) * a.Hv + h) * (D * D), D * D * 4);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.state + static_cast<long>(bh) * (D * D), D * D * 4);
   float4 hreg[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) hreg[k] = buf_load4<false>(srs, voff, k * kRowBytes);
