@@ -54,8 +54,10 @@ __device__ __forceinline__ int seg_of(const ProjArgs& p, long n) {
 
 // ----------------------------------------------------------------------------------
 // M <= MT rows: weight streaming. Dynamic LDS: X as MT x K bf16 (rows >= M are zero).
+// A wave takes NR output rows; each lane issues the loads of all its 16-byte pieces of
+// those rows (CU pieces per row at a time, K/512 in all) before the first product.
 // ----------------------------------------------------------------------------------
-template <int MT, int NR>
+template <int MT, int NR, int CU>
 __global__ __launch_bounds__(256) void gdn_proj_gemv(const ProjArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   const int K = p.K, K8 = K / 8;
@@ -83,20 +85,28 @@ __global__ __launch_bounds__(256) void gdn_proj_gemv(const ProjArgs p) {
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
-    for (int c = lane; c < K8; c += 64) {
-      u32x4 wv[NR];
+    for (int c0 = lane; c0 < K8; c0 += 64 * CU) {
+      u32x4 wv[CU][NR];
 #pragma unroll
-      for (int r = 0; r < NR; ++r) wv[r] = *reinterpret_cast<const u32x4*>(wr[r] + 8 * c);
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + static_cast<long>(m) * K + 8 * c);
+      for (int u = 0; u < CU; ++u)
 #pragma unroll
         for (int r = 0; r < NR; ++r)
+          if (c0 + 64 * u < K8) wv[u][r] = *reinterpret_cast<const u32x4*>(wr[r] + 8 * (c0 + 64 * u));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[r][m] = fmaf(lo_bf16(wv[r][e]), lo_bf16(xv[e]), acc[r][m]);
-            acc[r][m] = fmaf(hi_bf16(wv[r][e]), hi_bf16(xv[e]), acc[r][m]);
-          }
+      for (int u = 0; u < CU; ++u) {
+        const int c = c0 + 64 * u;
+        if (c >= K8) break;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + static_cast<long>(m) * K + 8 * c);
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[r][m] = fmaf(lo_bf16(wv[u][r][e]), lo_bf16(xv[e]), acc[r][m]);
+              acc[r][m] = fmaf(hi_bf16(wv[u][r][e]), hi_bf16(xv[e]), acc[r][m]);
+            }
+        }
       }
     }
 #pragma unroll
@@ -124,14 +134,17 @@ __global__ __launch_bounds__(256) void gdn_proj_gemv(const ProjArgs p) {
 
 // ----------------------------------------------------------------------------------
 // MFMA tiles. Grid: x = N-tiles of all segments (tile0 of each segment), y = M-tiles.
-// 4 waves as 2 x 2, each a (BM/2) x (BN/2) block of 16x16 accumulator tiles.
+// 4 waves as WM x WN, each a (BM/WM) x (BN/WN) block of 16x16 accumulator tiles; BK-deep
+// stages of X and W double-buffered in LDS (rows padded by 8 bf16).
 // ----------------------------------------------------------------------------------
-template <int BM, int BN>
+template <int BM, int BN, int BK, int WM, int WN>
 __global__ __launch_bounds__(256) void gdn_proj_mfma(const ProjArgs p) {
-  constexpr int BK = 64, LD = BK + 8;                 // LDS row stride 144 bytes
-  constexpr int TI = BM / 32, TJ = BN / 32;           // 16x16 tiles per wave
-  constexpr int XC = BM * BK / 8 / 256, WC = BN * BK / 8 / 256;  // 16-byte pieces per thread
-  static_assert(XC >= 1 && WC >= 1, "tile too small for 256 threads");
+  static_assert(WM * WN == 4, "4 waves");
+  constexpr int LD = BK + 8;
+  constexpr int TI = BM / WM / 16, TJ = BN / WN / 16;  // 16x16 tiles per wave
+  constexpr int PR = BK / 8;                          // 16-byte pieces per tile row
+  constexpr int XC = BM * PR / 256, WC = BN * PR / 256;  // pieces per thread
+  static_assert(XC >= 1 && WC >= 1 && TI >= 1 && TJ >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][LD];
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN][LD];
 
@@ -144,20 +157,20 @@ __global__ __launch_bounds__(256) void gdn_proj_mfma(const ProjArgs p) {
   const long m0 = static_cast<long>(blockIdx.y) * BM;
   const int K = p.K;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
 
-  // global -> register pieces: piece i of a tile is row i / 8, 8 bf16 at column 8 (i % 8)
+  // global -> register pieces: piece i of a tile is row i / PR, 8 bf16 at column 8 (i % PR)
   u32x4 xr[XC], wr_[WC];
   auto load = [&](int k0) {
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
-      const int i = t + 256 * c, row = i >> 3, col = 8 * (i & 7);
+      const int i = t + 256 * c, row = i / PR, col = 8 * (i % PR);
       const long m = m0 + row;
       xr[c] = m < p.M ? *reinterpret_cast<const u32x4*>(p.x + m * K + k0 + col) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int c = 0; c < WC; ++c) {
-      const int i = t + 256 * c, row = i >> 3, col = 8 * (i & 7);
+      const int i = t + 256 * c, row = i / PR, col = 8 * (i % PR);
       const long n = n0 + row;
       wr_[c] = n < s.n ? *reinterpret_cast<const u32x4*>(s.w + n * K + k0 + col) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -166,12 +179,12 @@ __global__ __launch_bounds__(256) void gdn_proj_mfma(const ProjArgs p) {
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
       const int i = t + 256 * c;
-      *reinterpret_cast<u32x4*>(&xs[buf][i >> 3][8 * (i & 7)]) = xr[c];
+      *reinterpret_cast<u32x4*>(&xs[buf][i / PR][8 * (i % PR)]) = xr[c];
     }
 #pragma unroll
     for (int c = 0; c < WC; ++c) {
       const int i = t + 256 * c;
-      *reinterpret_cast<u32x4*>(&ws[buf][i >> 3][8 * (i & 7)]) = wr_[c];
+      *reinterpret_cast<u32x4*>(&ws[buf][i / PR][8 * (i % PR)]) = wr_[c];
     }
   };
 
@@ -187,16 +200,16 @@ __global__ __launch_bounds__(256) void gdn_proj_mfma(const ProjArgs p) {
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * BK);  // next tile in flight during the products
+    if (kt + 1 < nk) load((kt + 1) * BK);  // next stage in flight during the products
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       bf16x8 a[TI], bb[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&xs[cur][wm * (BM / 2) + 16 * i + c16][32 * kk + 8 * q]);
+        a[i] = *reinterpret_cast<const bf16x8*>(&xs[cur][wm * (BM / WM) + 16 * i + c16][32 * kk + 8 * q]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        bb[j] = *reinterpret_cast<const bf16x8*>(&ws[cur][wn * (BN / 2) + 16 * j + c16][32 * kk + 8 * q]);
+        bb[j] = *reinterpret_cast<const bf16x8*>(&ws[cur][wn * (BN / WN) + 16 * j + c16][32 * kk + 8 * q]);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -212,13 +225,40 @@ __global__ __launch_bounds__(256) void gdn_proj_mfma(const ProjArgs p) {
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const long n = n0 + wn * (BN / 2) + 16 * j + c16;
+      const long n = n0 + wn * (BN / WN) + 16 * j + c16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const long m = m0 + wm * (BM / 2) + 16 * i + 4 * q + r;
+        const long m = m0 + wm * (BM / WM) + 16 * i + 4 * q + r;
         if (m < p.M && n < s.n) put(s, m, n, acc[i][j][r]);
       }
     }
+}
+
+template <int BM, int BN, int BK, int WM, int WN>
+hipError_t launch_mfma(ProjArgs& p, hipStream_t st) {
+  int tiles = 0;
+  for (int i = 0; i < p.nseg; ++i) {
+    p.seg[i].tile0 = tiles;
+    tiles += static_cast<int>((p.seg[i].n + BN - 1) / BN);
+  }
+  const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>((p.M + BM - 1) / BM));
+  gdn_proj_mfma<BM, BN, BK, WM, WN><<<grid, 256, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_gemv(const ProjArgs& p, hipStream_t st) {
+  // two rows per wave when there are many rows, else one (more waves in flight)
+  const size_t lds = static_cast<size_t>(MT) * p.K * 2;
+  if (p.rows >= 8192) {
+    const long tasks = (p.rows + 1) / 2;
+    const unsigned grid = static_cast<unsigned>(std::min<long>((tasks + 3) / 4, 1024));
+    gdn_proj_gemv<MT, 2, 4><<<grid, 256, lds, st>>>(p);
+  } else {
+    const unsigned grid = static_cast<unsigned>(std::min<long>((p.rows + 3) / 4, 1024));
+    gdn_proj_gemv<MT, 1, 8><<<grid, 256, lds, st>>>(p);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -230,35 +270,30 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
     rows += p.seg[i].n;
   }
   p.rows = rows;
-  if (p.M <= 8) {
-    constexpr int NR = 2;
-    const long groups = (rows + NR - 1) / NR;
-    const unsigned grid = static_cast<unsigned>(std::min<long>((groups + 3) / 4, 2048));
-    const size_t lds = (p.M <= 1 ? 1 : p.M <= 2 ? 2 : p.M <= 4 ? 4 : 8) * static_cast<size_t>(p.K) * 2;
-    if (p.M <= 1)
-      gdn_proj_gemv<1, NR><<<grid, 256, lds, st>>>(p);
-    else if (p.M <= 2)
-      gdn_proj_gemv<2, NR><<<grid, 256, lds, st>>>(p);
-    else if (p.M <= 4)
-      gdn_proj_gemv<4, NR><<<grid, 256, lds, st>>>(p);
-    else
-      gdn_proj_gemv<8, NR><<<grid, 256, lds, st>>>(p);
-    return hipGetLastError();
+  // weight streaming for one or two rows, and for up to 8 rows when there are too few
+  // output columns to give the MFMA tiles a full grid (X rows within the default LDS
+  // allowance of 64 KB)
+  const int mt = p.M <= 1 ? 1 : p.M <= 2 ? 2 : p.M <= 4 ? 4 : 8;
+  if ((p.M <= 2 || (p.M <= 8 && rows < 8192)) && static_cast<long>(mt) * p.K * 2 <= 65536) {
+    if (mt == 1) return launch_gemv<1>(p, st);
+    if (mt == 2) return launch_gemv<2>(p, st);
+    if (mt == 4) return launch_gemv<4>(p, st);
+    return launch_gemv<8>(p, st);
   }
-  // 32 x 32 tiles up to M = 64 (more workgroups for the weight stream), 64 x 64 above
-  const bool small = p.M <= 64;
-  const int BM = small ? 32 : 64, BN = small ? 32 : 64;
-  int tiles = 0;
-  for (int i = 0; i < p.nseg; ++i) {
-    p.seg[i].tile0 = tiles;
-    tiles += static_cast<int>((p.seg[i].n + BN - 1) / BN);
-  }
-  const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>((p.M + BM - 1) / BM));
-  if (small)
-    gdn_proj_mfma<32, 32><<<grid, 256, 0, st>>>(p);
-  else
-    gdn_proj_mfma<64, 64><<<grid, 256, 0, st>>>(p);
-  return hipGetLastError();
+  // MFMA: the largest tile that still gives every CU a workgroup (the weight stream and
+  // the LDS reads per MFMA both favour large tiles; a grid below 256 workgroups leaves
+  // CUs idle), else 32 x 32 tiles with 256-deep stages for more bytes in flight
+  auto tiles = [&](int bm, int bn) {
+    long n = 0;
+    for (int i = 0; i < p.nseg; ++i) n += (p.seg[i].n + bn - 1) / bn;
+    return n * ((p.M + bm - 1) / bm);
+  };
+  if (tiles(128, 128) >= 256) return launch_mfma<128, 128, 64, 2, 2>(p, st);
+  if (tiles(64, 64) >= 256) return launch_mfma<64, 64, 64, 2, 2>(p, st);
+  // 32 x 32 tiles: 64-deep stages keep 8 workgroups per CU resident when the grid is
+  // large; a small grid needs the deeper stages for bytes in flight
+  if (tiles(32, 32) < 512 && p.K % 256 == 0) return launch_mfma<32, 32, 256, 2, 2>(p, st);
+  return launch_mfma<32, 32, 64, 2, 2>(p, st);
 }
 
 }  // namespace gdn
