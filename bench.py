@@ -369,7 +369,7 @@ def main():
         summarize(args.summarize)
         return 0
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the GDN core shards "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the GDN core shards "
               "by sequence and k-head with no exchange; see the design notes). Run with --gpus 1.",
               file=sys.stderr)
         return 2

@@ -15,18 +15,20 @@
 // Work unit: one workgroup (4 waves) per (sequence, v-head), looping over chunks.
 // The 128x128 state lives in MFMA accumulators for the whole sequence: wave w owns
 // columns 32w .. 32w+31 (8 x 2 tiles of 16x16). An accumulator tile, lane l holding
-// rows 4(l/16)+r, column l%16, is exactly the B-operand layout of the 16x16x32 bf16
+// rows 4(l/16)+r, column l%16, is exactly the B-operand layout of the 16x16x32 f16
 // MFMA when the contraction index of each 32-block is ordered (4q..4q+3, 16+4q..
 // 16+4q+3) for lane group q: two stacked accumulator tiles feed B directly, and the
 // A operand reads the same permuted columns from LDS (two 8-byte reads).
 // Precision: every operand is split into two fp16 halves (x = hi + lo, 22 significant
-// bits) and each product is evaluated as hi*hi + hi*lo + lo*hi with fp32 accumulation
-// (the three MFMAs of an accumulator are issued apart, interleaved with independent ones)
-// (~2^-21 relative per product). A bf16 split (8 + 8 bits) measured ~1e-4 relative
+// bits) and each product is evaluated as hi*hi + hi*lo + lo*hi with fp32 accumulation,
+// ~2^-21 relative per product; the three MFMAs of an accumulator are issued apart,
+// interleaved with independent ones. A bf16 split (8 + 8 bits) measured ~1e-4 relative
 // error on the outputs, too coarse for the fp32 recurrence. Operands must stay below
 // the fp16 range (6.5e4); the normalised q, k, the state and delta of this layer are
 // orders of magnitude smaller.
 // The (I + A) solve is an fp32 forward substitution on VALU, one lane per column.
+// With bf16 activations, waves 2-3 prefetch the next chunk's conv inputs, z rows and
+// gates into LDS while waves 0-1 run the solve.
 //
 // The conv state is only read here; a separate epilogue launch writes the rolled
 // state afterwards (two workgroups of a k-head read the same Q/K conv columns).
