@@ -192,6 +192,14 @@ __device__ __forceinline__ float raw_f32(uint32_t v) {
 
 // silu with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an IEEE divide
 __device__ __forceinline__ float silu(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
+// log2(e) silu(u) from u2 = log2(e) u: u2 / (1 + 2^-u2). The conv weights are scaled by
+// log2(e) once, so the exponent needs no multiply; the factor log2(e) then cancels in
+// the L2 norms of q and k (whose epsilon is scaled by log2(e)^2) and is taken out of v
+// where v enters the right-hand side of the solve.
+__device__ __forceinline__ float silu_l2e(float u2) {
+  return u2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u2));
+}
+constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
 
 // Cross-lane adds inside a row of 16 lanes via DPP (no LDS traffic).
 template <int CTRL>
@@ -252,27 +260,29 @@ __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float 
 // x = hi + lo in fp16, both rounded to nearest: hi = fp16(x), lo = fp16(x - hi)
 // (x - hi is exact in fp32). 11 + 11 significant bits: |x - hi - lo| <= 2^-22 |x|
 // for normal values, and <= 2^-25 absolute in the fp16 subnormal range.
-__device__ __forceinline__ void split1(float x, uint32_t& hi, uint32_t& lo) {
+// `one` is 1.0f held opaque to the optimiser: x * one - hi is then a single
+// v_fma_mix_f32 reading the fp16 hi directly (exact, like the subtraction it replaces)
+// instead of a conversion back to fp32 followed by a subtraction.
+__device__ __forceinline__ void split1(float x, uint32_t& hi, uint32_t& lo, float one) {
   const _Float16 h = static_cast<_Float16>(x);
-  const _Float16 r = static_cast<_Float16>(x - static_cast<float>(h));
+  const _Float16 r = static_cast<_Float16>(fmaf(x, one, -static_cast<float>(h)));
   hi = __builtin_bit_cast(uint16_t, h);
   lo = __builtin_bit_cast(uint16_t, r);
 }
 // two fp32 -> packed fp16 pairs (hi0 | hi1 << 16), (lo0 | lo1 << 16), same rounding as
 // split1 (v_cvt_pk_f16_f32 rounds to nearest even)
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo, float one) {
   const f32x2 x = {x0, x1};
   const f16x2 h = __builtin_convertvector(x, f16x2);
-  const f32x2 back = __builtin_convertvector(h, f32x2);
-  const f32x2 res = {x0 - back[0], x1 - back[1]};
+  const f32x2 res = {fmaf(x0, one, -static_cast<float>(h[0])), fmaf(x1, one, -static_cast<float>(h[1]))};
   hi = __builtin_bit_cast(uint32_t, h);
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(res, f16x2));
 }
 // four fp32 -> (hi pair, hi pair), (lo pair, lo pair)
-__device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo) {
+__device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo, float one) {
   uint32_t h0, h1, l0, l1;
-  split2(x[0], x[1], h0, l0);
-  split2(x[2], x[3], h1, l1);
+  split2(x[0], x[1], h0, l0, one);
+  split2(x[2], x[3], h1, l1, one);
   hi[0] = h0;
   hi[1] = h1;
   lo[0] = l0;
@@ -299,10 +309,10 @@ __device__ __forceinline__ u32x4 frag(const uint16_t* plane, int ld, int row, in
 
 // B-operand fragment from two stacked accumulator-layout tiles (rows 0..15, 16..31 of
 // a 32-row block), split into hi and lo.
-__device__ __forceinline__ void bfrag(f32x4 top, f32x4 bottom, u32x4& hi, u32x4& lo) {
+__device__ __forceinline__ void bfrag(f32x4 top, f32x4 bottom, u32x4& hi, u32x4& lo, float one) {
   u32x2 h0, l0, h1, l1;
-  split4(top, h0, l0);
-  split4(bottom, h1, l1);
+  split4(top, h0, l0, one);
+  split4(bottom, h1, l1, one);
   hi[0] = h0[0];
   hi[1] = h0[1];
   hi[2] = h1[0];
@@ -313,9 +323,9 @@ __device__ __forceinline__ void bfrag(f32x4 top, f32x4 bottom, u32x4& hi, u32x4&
   lo[3] = l1[1];
 }
 
-__device__ __forceinline__ void put_split(uint16_t* hi_plane, uint16_t* lo_plane, int idx, float x) {
+__device__ __forceinline__ void put_split(uint16_t* hi_plane, uint16_t* lo_plane, int idx, float x, float one) {
   uint32_t h, l;
-  split1(x, h, l);
+  split1(x, h, l, one);
   hi_plane[idx] = static_cast<uint16_t>(h);
   lo_plane[idx] = static_cast<uint16_t>(l);
 }
@@ -366,7 +376,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     for (int e = 0; e < kCW; ++e) {
       const long gc = unit_channel(c0 + e);
 #pragma unroll
-      for (int j = 0; j < kTaps; ++j) wt[i][e][j] = raw_f32<BF>(load_raw<BF>(a.conv_w, gc * kTaps + j));
+      for (int j = 0; j < kTaps; ++j) wt[i][e][j] = kLog2e * raw_f32<BF>(load_raw<BF>(a.conv_w, gc * kTaps + j));
     }
   }
   float win[2][kTaps - 1];  // fp32: the channel's last three inputs
@@ -400,6 +410,8 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     // lane-dependent LDS addresses are recomputed instead of held across the loop
     int tid_ = tid;
     asm volatile("" : "+v"(tid_));
+    float one = 1.0f;
+    asm volatile("" : "+s"(one));
     const int tid = tid_;
     const int w = tid >> 6, l = tid & 63, q = l >> 4, c16 = l & 15;
 
@@ -425,8 +437,9 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
             u0 = fmaf(wt[i][0][j], xl[e + j], u0);
             u1 = fmaf(wt[i][1][j], xh[e + j], u1);
           }
-          const bool live = t8 + e < nt;
-          *reinterpret_cast<f32x2*>(dst + (t8 + e) * ld) = f32x2{live ? silu(u0) : 0.0f, live ? silu(u1) : 0.0f};
+          // tokens past the end (last chunk) repeat the last input row: finite values
+          // whose beta is 0, so their delta rows are exactly 0 and they change nothing
+          *reinterpret_cast<f32x2*>(dst + (t8 + e) * ld) = f32x2{silu_l2e(u0), silu_l2e(u1)};
         }
       }
     } else {
@@ -449,7 +462,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
             uu = fmaf(wt[m][0][1], win[m][1], uu);
             uu = fmaf(wt[m][0][2], win[m][2], uu);
             uu = fmaf(wt[m][0][3], xf, uu);
-            const float val = (t < nt) ? silu(uu) : 0.0f;
+            const float val = (t < nt) ? silu_l2e(uu) : 0.0f;
             if (m == 0)
               sm.u.raw[t][tid] = val;
             else
@@ -475,6 +488,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     {
       constexpr int kTW = kC / 4;
       const int tb = w * kTW;
+      const float l2_eps = a.l2_eps * (kLog2e * kLog2e);  // q, k carry the factor log2(e)
       float2 qv[kTW], kv[kTW];
       float ss[2 * kTW];
 #pragma unroll
@@ -496,19 +510,19 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
       for (int i = 0; i < 2 * kTW; ++i) ss[i] += dpp<0x140>(ss[i]);
 #pragma unroll
-      for (int i = 0; i < 2 * kTW; ++i) ss[i] = __builtin_amdgcn_rsqf(rows_total(ss[i]) + a.l2_eps);
+      for (int i = 0; i < 2 * kTW; ++i) ss[i] = __builtin_amdgcn_rsqf(rows_total(ss[i]) + l2_eps);
       float kn[2][kTW];  // normalised k of channels 2l, 2l+1
 #pragma unroll
       for (int tt = 0; tt < kTW; ++tt) {
         const int t = tb + tt;
         const float rq = ss[2 * tt], rk = ss[2 * tt + 1];
         uint32_t h, lo;
-        split2(qv[tt].x * rq * kUp, qv[tt].y * rq * kUp, h, lo);
+        split2(qv[tt].x * rq * kUp, qv[tt].y * rq * kUp, h, lo, one);
         *reinterpret_cast<uint32_t*>(&sm.q_hi[t][2 * l]) = h;
         *reinterpret_cast<uint32_t*>(&sm.q_lo[t][2 * l]) = lo;
         kn[0][tt] = kv[tt].x * rk;
         kn[1][tt] = kv[tt].y * rk;
-        split2(kn[0][tt] * kUp, kn[1][tt] * kUp, h, lo);
+        split2(kn[0][tt] * kUp, kn[1][tt] * kUp, h, lo, one);
         *reinterpret_cast<uint32_t*>(&sm.k_hi[t][2 * l]) = h;
         *reinterpret_cast<uint32_t*>(&sm.k_lo[t][2 * l]) = lo;
       }
@@ -518,7 +532,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           uint32_t h, lo;
-          split2(kn[c][2 * e], kn[c][2 * e + 1], h, lo);
+          split2(kn[c][2 * e], kn[c][2 * e + 1], h, lo, one);
           hv[e] = h;
           lv[e] = lo;
         }
@@ -568,7 +582,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         // kk and qk carry the 2^15 x 2^15 operand scale
         const float av = -(bt[r] * e * (kk[r] * (kDown * kDown)));
         sm.u.s.at[s][t] = (s < t) ? av : 0.0f;
-        put_split(&sm.u.s.p_hi[0][0], &sm.u.s.p_lo[0][0], t * kPLd + s, e * (qk[r] * kDown));  // = 2^15 P
+        put_split(&sm.u.s.p_hi[0][0], &sm.u.s.p_lo[0][0], t * kPLd + s, e * (qk[r] * kDown), one);  // = 2^15 P
       }
     }
 
@@ -599,7 +613,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         if (kb + 1 < 4) load_fq(kb + 1, fq[(kb + 1) & 1]);
         u32x4 hb_hi[2], hb_lo[2];
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) bfrag(hacc[2 * kb][jt], hacc[2 * kb + 1][jt], hb_hi[jt], hb_lo[jt]);
+        for (int jt = 0; jt < 2; ++jt) bfrag(hacc[2 * kb][jt], hacc[2 * kb + 1][jt], hb_hi[jt], hb_lo[jt], one);
         // hi*hi, hi*lo, lo*hi of all eight accumulators in turn (independent neighbours)
 #pragma unroll
         for (int part = 0; part < 3; ++part)
@@ -615,6 +629,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
       }
     }
     // rhs[t][j] = beta_t (v_t[j] - gamma_t (K H0)[t][j]);  O starts as gamma_t (Q H0)[t][j]
+    // (v is stored as log2(e) v)
     f32x4 oacc[2][2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -627,7 +642,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
           const int j = 32 * w + 16 * jt + c16;
-          sm.u.s.x[t4 + r][j] = bt[r] * (sm.v[t4 + r][j] - gam * (kh[tt][jt][r] * kDown));
+          sm.u.s.x[t4 + r][j] = (bt[r] * kLn2) * (sm.v[t4 + r][j] - (gam * (kDown * kLog2e)) * kh[tt][jt][r]);
           oacc[tt][jt][r] = gam * (qh[tt][jt][r] * kDown);
         }
       }
@@ -703,8 +718,8 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
           top2[r] = __expf(gC - g0[r]) * top[r];
           bot2[r] = __expf(gC - g1[r]) * bot[r];
         }
-        bfrag(top, bot, dh[jt], dl[jt]);
-        bfrag(top2, bot2, eh[jt], el[jt]);
+        bfrag(top, bot, dh[jt], dl[jt], one);
+        bfrag(top2, bot2, eh[jt], el[jt], one);
       }
       f32x4 pd[2][2] = {};  // 2^15 P Delta
 #pragma unroll
