@@ -206,6 +206,18 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
+// v_permlane32_swap: lanes 32-63 of a trade places with lanes 0-31 of b (afterwards a
+// holds a[0..31], b[0..31] and b holds a[32..63], b[32..63]). v_permlane16_swap: the
+// odd rows of 16 lanes of a trade places with the even rows of b. Written as inline
+// asm with both registers read and written: the compiler's builtins for these return
+// one register for both results. Two wait states before the swap cover a VALU write
+// of either operand just before it.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_rows(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
 // sum over the 16 lanes of each row (every lane of the row gets it)
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
@@ -214,15 +226,6 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0x140>(v);  // row_mirror
   return v;
 }
-// total over the wave of a value already summed within each row of 16 lanes
-__device__ __forceinline__ float rows_total(float v) {
-  const int iv = __builtin_bit_cast(int, v);
-  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)) +
-          __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16))) +
-         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
-          __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48)));
-}
-
 template <bool BF>
 __device__ __forceinline__ void chunk_gate_inputs(const KernelArgs& a, int b, int h, int ch, int lane, float& dt,
                                                   float& br) {
@@ -501,16 +504,28 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         ss[2 * tt] = qv[tt].x * qv[tt].x + qv[tt].y * qv[tt].y;
         ss[2 * tt + 1] = kv[tt].x * kv[tt].x + kv[tt].y * kv[tt].y;
       }
+      // The 16 sums over the wave, transposed: each exchange step halves the values a
+      // lane carries while doubling the lanes each covers. After the 32-lane swaps value
+      // i (i < 8) lives in lanes 0-31 and value i + 8 in lanes 32-63, each summed over
+      // lanes l and l ^ 32; after the 16-lane swaps register j of row r holds value
+      // j + 4 r summed over l, l ^ 16, l ^ 32, l ^ 48; a row sum completes it.
+      float h8[kTW];
 #pragma unroll
-      for (int i = 0; i < 2 * kTW; ++i) ss[i] += dpp<0xB1>(ss[i]);
+      for (int i = 0; i < kTW; ++i) {
+        float x0 = ss[i], x1 = ss[i + kTW];
+        swap_halves(x0, x1);
+        h8[i] = x0 + x1;
+      }
+      float h4[kTW / 2];
 #pragma unroll
-      for (int i = 0; i < 2 * kTW; ++i) ss[i] += dpp<0x4E>(ss[i]);
+      for (int j = 0; j < kTW / 2; ++j) {
+        float x0 = h8[j], x1 = h8[j + kTW / 2];
+        swap_rows(x0, x1);
+        h4[j] = __builtin_amdgcn_rsqf(row16_sum(x0 + x1) + l2_eps);
+      }
 #pragma unroll
-      for (int i = 0; i < 2 * kTW; ++i) ss[i] += dpp<0x141>(ss[i]);
-#pragma unroll
-      for (int i = 0; i < 2 * kTW; ++i) ss[i] += dpp<0x140>(ss[i]);
-#pragma unroll
-      for (int i = 0; i < 2 * kTW; ++i) ss[i] = __builtin_amdgcn_rsqf(rows_total(ss[i]) + l2_eps);
+      for (int i = 0; i < 2 * kTW; ++i)
+        ss[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, h4[i % 4]), 16 * (i / 4)));
       float kn[2][kTW];  // normalised k of channels 2l, 2l+1
 #pragma unroll
       for (int tt = 0; tt < kTW; ++tt) {
