@@ -8,7 +8,9 @@
 // M <= 8 (decode at small batch) is weight-streaming: each wave takes NR output rows
 // at a time, every lane reads 16-byte pieces of the rows (coalesced, K contiguous) and
 // multiplies them with the M rows of X held in LDS; a wave reduction finishes each dot
-// product. The bound is HBM: every weight byte is read once.
+// product. The bound is HBM: every weight byte is read once. Up to 32 rows with few
+// output columns use a skinny MFMA kernel that splits K over the waves of a workgroup
+// (see gdn_proj_skinny).
 // Larger M uses MFMA (v_mfma_f32_16x16x32_bf16) on BM x BN tiles of Y, BK = 64, X and W
 // tiles double-buffered in LDS. Operand fragments are 8 consecutive k per lane (a
 // 16-byte LDS read) for both X and W: the product pairs A and B register slots of the
@@ -234,6 +236,117 @@ __global__ __launch_bounds__(256) void gdn_proj_mfma(const ProjArgs p) {
     }
 }
 
+// ----------------------------------------------------------------------------------
+// Skinny MFMA (M <= 16 TI): the weight stream with matrix cores. A workgroup of KW waves
+// takes one BN = 16 TJ wide tile of outputs for all M rows; wave w covers k in
+// [w K / KW, (w + 1) K / KW), and the KW partial tiles are summed through LDS at the end.
+// Operands go from memory straight into MFMA fragments (no LDS staging): per 64-deep
+// k-block, lane group q holds k0 + 16 q .. k0 + 16 q + 15 of its row (two 16-byte
+// loads, one per MFMA step), so the four lane groups read a row's 128 bytes at once; A
+// (X, small and reused from cache) and B (W, streamed once) use the same k order, which
+// leaves every dot product unchanged. D k-blocks are in flight in registers. Rows of X
+// past M and rows of W past the segment end are clamped to valid rows: they only feed
+// outputs that are not stored.
+// ----------------------------------------------------------------------------------
+template <int TI, int TJ, int KW, int D>
+__global__ __launch_bounds__(64 * KW) void gdn_proj_skinny(const ProjArgs p) {
+  constexpr int BM = 16 * TI, BN = 16 * TJ, NT = 64 * KW;
+  static_assert(KW * BM * BN * 4 <= 65536, "reduction buffer");
+  __shared__ float red[KW][BM * BN];
+
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProjSegs; ++i)
+    if (i < p.nseg && static_cast<int>(blockIdx.x) >= p.seg[i].tile0) si = i;
+  const ProjSeg& s = p.seg[si];
+  const long n0 = static_cast<long>(blockIdx.x - s.tile0) * BN;
+  const int K = p.K;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
+  const int kw = K / KW, nkb = kw / 64;
+  const long k0 = static_cast<long>(w) * kw + 16 * q;
+
+  const uint16_t* xp[TI];
+  const uint16_t* wp[TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) xp[i] = p.x + static_cast<long>(min(16 * i + c16, p.M - 1)) * K + k0;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) wp[j] = s.w + min(n0 + 16 * j + c16, s.n - 1) * K + k0;
+
+  u32x4 xa[D][TI][2], wb[D][TJ][2];
+  auto load = [&](int kb, int sl) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) wb[sl][j][e] = *reinterpret_cast<const u32x4*>(wp[j] + 64 * kb + 8 * e);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) xa[sl][i][e] = *reinterpret_cast<const u32x4*>(xp[i] + 64 * kb + 8 * e);
+  };
+  f32x4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (i < nkb) load(i, i);
+  // k-block kb sits in register slot kb % D; unrolled by D so that slots are constants
+  for (int kb0 = 0; kb0 < nkb; kb0 += D) {
+#pragma unroll
+    for (int sl = 0; sl < D; ++sl) {
+      const int kb = kb0 + sl;
+      if (kb >= nkb) break;
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[sl][i][e]),
+                                                                __builtin_bit_cast(bf16x8, wb[sl][j][e]), acc[i][j], 0, 0,
+                                                                0);
+      if (kb + D < nkb) load(kb + D, sl);
+    }
+  }
+  // accumulator tile (i, j): lane holds rows 16 i + 4 q + r, column 16 j + c16
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[w][(16 * i + 4 * q + r) * BN + 16 * j + c16] = acc[i][j][r];
+  __syncthreads();
+  for (int e = t; e < BM * BN; e += NT) {
+    float v = 0.0f;
+#pragma unroll
+    for (int u = 0; u < KW; ++u) v += red[u][e];
+    const int m = e / BN;
+    const long n = n0 + (e - m * BN);
+    if (m < p.M && n < s.n) put(s, m, n, v);
+  }
+}
+
+template <int TI, int TJ, int KW>
+hipError_t launch_skinny(ProjArgs& p, hipStream_t st) {
+  int tiles = 0;
+  for (int i = 0; i < p.nseg; ++i) {
+    p.seg[i].tile0 = tiles;
+    tiles += static_cast<int>((p.seg[i].n + 16 * TJ - 1) / (16 * TJ));
+  }
+  gdn_proj_skinny<TI, TJ, KW, 3><<<tiles, 64 * KW, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+// TI from the row count (16 rows per accumulator tile)
+template <int TJ, int KW>
+hipError_t launch_skinny_m(ProjArgs& p, hipStream_t st) {
+  if (p.M <= 16) return launch_skinny<1, TJ, KW>(p, st);
+  if (p.M <= 32) return launch_skinny<2, TJ, KW>(p, st);
+  if (p.M <= 48) return launch_skinny<3, TJ, KW>(p, st);
+  return launch_skinny<4, TJ, KW>(p, st);
+}
+
 template <int BM, int BN, int BK, int WM, int WN>
 hipError_t launch_mfma(ProjArgs& p, hipStream_t st) {
   int tiles = 0;
@@ -270,6 +383,14 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
     rows += p.seg[i].n;
   }
   p.rows = rows;
+  // Few output columns and a long K (the out_proj shape) at 3..32 rows: the skinny MFMA
+  // kernel, K split over 8 waves, one 16-column tile per workgroup. Measured at hidden =
+  // 2048, K = 4096: 7.5 / 9.6 / 13.4 us at 4 / 16 / 32 rows, against 8.3 / 15.4 / 15.5
+  // with the weight-streaming and tiled paths.
+  if (p.M >= 3 && p.M <= 32 && rows <= 4096 && p.K % 512 == 0) return launch_skinny_m<1, 8>(p, st);
+  // 33..64 rows and many columns (the in_proj shape): one 64-row tile, so the weights
+  // stream once (32-row tiles read them twice); 19.8 against 21.6 us at 64 rows.
+  if (p.M > 32 && p.M <= 64 && rows >= 8192 && p.K % 256 == 0) return launch_mfma<64, 64, 256, 2, 2>(p, st);
   // weight streaming for one or two rows, and for up to 8 rows when there are too few
   // output columns to give the MFMA tiles a full grid (X rows within the default LDS
   // allowance of 64 KB)

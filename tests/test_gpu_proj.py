@@ -8,9 +8,11 @@ Tolerance: the kernels accumulate in fp32 and round once to the output dtype.
 * fp32 outputs: 1e-5 absolute + 1e-5 relative. The weights are scaled by
   1/sqrt(fan_in), so outputs are O(1) and the fp32 sum of K <= 4096 products has an
   error of order sqrt(K) 2^-24, a few 1e-7.
-Shapes cover both kernels (rows B <= 8 stream the weights; larger B uses MFMA tiles
-of 32 x 32 up to B = 64 and 64 x 64 above), ragged row and column tiles (the H_v-wide
-a/b segments are narrower than a tile) and the Qwen3.5-style sizes.
+Shapes cover every kernel: weight streaming (B <= 8, or B <= 2), the skinny MFMA
+kernel (3..32 rows, few output columns: out_proj at B = 3 and 20, in_proj at hidden
+512), 64 x 64 tiles for 33..64 rows (in_proj at B = 40 and 64), 32 x 32 tiles and
+larger tiles above; ragged row and column tiles (the H_v-wide a/b segments are narrower
+than a tile) and the Qwen3.5-style sizes.
 """
 
 import numpy as np
@@ -58,6 +60,8 @@ CASES = [
     (3, 16, 32, 128, 2048, None),
     (8, 2, 4, 64, 512, None),
     (9, 2, 4, 64, 512, None),
+    (20, 16, 32, 128, 2048, None),
+    (40, 16, 32, 128, 2048, None),
     (64, 16, 32, 128, 2048, None),
     (100, 2, 6, 64, 256, None),
     (512, 16, 32, 128, 2048, [0, 1, 63, 64, 255, 300, 511]),
