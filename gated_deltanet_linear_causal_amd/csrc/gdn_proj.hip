@@ -347,6 +347,125 @@ hipError_t launch_skinny_m(ProjArgs& p, hipStream_t st) {
   return launch_skinny<4, TJ, KW>(p, st);
 }
 
+// ----------------------------------------------------------------------------------
+// Pipelined MFMA tiles for many rows (compute-bound). BM x BN tile per workgroup of 4
+// waves (2 x 2); 64-deep stages in a ring of S LDS slots, filled by direct-to-LDS DMA
+// (global_load_lds_dwordx4: 64 lanes x 16 bytes into 1 KB of consecutive LDS), so S - 1
+// stages of loads are in flight without registers. A stage holds BM rows of X and BN
+// rows of W, 128 bytes (eight 16-byte cells) each; cell c of row r is stored at
+// position c ^ (r & 7), so the eight rows that one fragment read touches per LDS cycle
+// hit eight different bank groups. One DMA instruction fills 8 rows: lane i writes
+// position i & 7 of row i >> 3 and so fetches cell (i & 7) ^ (i >> 3) of that row.
+// Per stage: wait until this wave's DMA of the stage has landed (the memory counter,
+// S - 2 later stages may still be in flight), an LDS-only barrier, then the DMA of
+// stage + S - 1 into the slot every wave finished reading before the barrier, then the
+// products. No LDS store is issued in the loop, so nothing there waits for the DMA.
+// Rows past M or the segment end are clamped to valid rows; they feed only outputs
+// that are not stored.
+// ----------------------------------------------------------------------------------
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// NI DMA instructions of a stage: 16 bytes per lane from src[i] + off into 1 KB blocks
+// of LDS at dst + 512 i elements (a device function: the builtin has no host form)
+template <int NI>
+__device__ __forceinline__ void pipe_issue(const uint16_t* const (&src)[NI], long off, uint16_t* dst) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) __builtin_amdgcn_global_load_lds(src[i] + off, dst + 512 * i, 16, 0, 0);
+}
+
+template <int BM, int BN, int S>
+__global__ __launch_bounds__(256) void gdn_proj_pipe(const ProjArgs p) {
+  constexpr int R = BM + BN;            // rows per stage
+  constexpr int NI = R / 8 / 4;         // DMA instructions per wave per stage
+  constexpr int TI = BM / 2 / 16, TJ = BN / 2 / 16;
+  static_assert(R % 32 == 0 && TI >= 1 && TJ >= 1, "tile shape");
+  static_assert((S - 2) * NI < 64, "memory counter range");
+  __shared__ __attribute__((aligned(16))) uint16_t ring[S][R][64];
+
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProjSegs; ++i)
+    if (i < p.nseg && static_cast<int>(blockIdx.x) >= p.seg[i].tile0) si = i;
+  const ProjSeg& s = p.seg[si];
+  const long n0 = static_cast<long>(blockIdx.x - s.tile0) * BN;
+  const long m0 = static_cast<long>(blockIdx.y) * BM;
+  const int K = p.K;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
+  const int wm = w >> 1, wn = w & 1;
+
+  // this lane's DMA sources: instruction i of wave w fills rows 8 (NI w + i) .. + 7
+  const uint16_t* src[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = 8 * (NI * w + i) + (l >> 3), cell = (l & 7) ^ (l >> 3);
+    src[i] = r < BM ? p.x + min(m0 + r, static_cast<long>(p.M) - 1) * K + 8 * cell
+                    : s.w + min(n0 + (r - BM), s.n - 1) * K + 8 * cell;
+  }
+  uint16_t* const ring0 = &ring[0][0][0] + 512 * NI * w;  // this wave's blocks of slot 0
+
+  f32x4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nk = K / 64;
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i)
+    if (i < nk) pipe_issue<NI>(src, 64L * i, ring0 + i * (R * 64));
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + S - 2 < nk)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * NI));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    if (kt + S - 1 < nk) pipe_issue<NI>(src, 64L * (kt + S - 1), ring0 + ((kt + S - 1) % S) * (R * 64));
+    const uint16_t* st = &ring[kt % S][0][0];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 a[TI], bb[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int r = wm * (BM / 2) + 16 * i + c16;
+        a[i] = *reinterpret_cast<const bf16x8*>(st + 64 * r + 8 * ((4 * kk + q) ^ (r & 7)));
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int r = BM + wn * (BN / 2) + 16 * j + c16;
+        bb[j] = *reinterpret_cast<const bf16x8*>(st + 64 * r + 8 * ((4 * kk + q) ^ (r & 7)));
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // accumulator tile (i, j): lane holds rows 4q + r, column c16
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const long n = n0 + wn * (BN / 2) + 16 * j + c16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const long m = m0 + wm * (BM / 2) + 16 * i + 4 * q + r;
+        if (m < p.M && n < s.n) put(s, m, n, acc[i][j][r]);
+      }
+    }
+}
+
+template <int BM, int BN, int S>
+hipError_t launch_pipe(ProjArgs& p, hipStream_t st) {
+  int tiles = 0;
+  for (int i = 0; i < p.nseg; ++i) {
+    p.seg[i].tile0 = tiles;
+    tiles += static_cast<int>((p.seg[i].n + BN - 1) / BN);
+  }
+  const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>((p.M + BM - 1) / BM));
+  gdn_proj_pipe<BM, BN, S><<<grid, 256, 0, st>>>(p);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int BK, int WM, int WN>
 hipError_t launch_mfma(ProjArgs& p, hipStream_t st) {
   int tiles = 0;
@@ -410,7 +529,11 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
     return n * ((p.M + bm - 1) / bm);
   };
   if (tiles(128, 128) >= 256) return launch_mfma<128, 128, 64, 2, 2>(p, st);
-  if (tiles(64, 64) >= 256) return launch_mfma<64, 64, 64, 2, 2>(p, st);
+  // 64 x 64 tiles: the DMA-fed ring of 4 stages (64 KB of LDS, two workgroups per CU).
+  // out_proj at 512 / 1024 rows: 44.4 / 50.4 -> 25.7 / 31.1 us; in_proj at 128 rows:
+  // 28.4 -> 23.9 us. (A 128 x 128 ring needs 128 KB, one workgroup per CU, and lost to
+  // the register-staged kernel above.)
+  if (tiles(64, 64) >= 256) return launch_pipe<64, 64, 4>(p, st);
   // 32 x 32 tiles: 64-deep stages keep 8 workgroups per CU resident when the grid is
   // large; a small grid needs the deeper stages for bytes in flight
   if (tiles(32, 32) < 512 && p.K % 256 == 0) return launch_mfma<32, 32, 256, 2, 2>(p, st);
