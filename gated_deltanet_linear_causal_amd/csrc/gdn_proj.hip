@@ -348,8 +348,8 @@ hipError_t launch_skinny_m(ProjArgs& p, hipStream_t st) {
 }
 
 // ----------------------------------------------------------------------------------
-// Pipelined MFMA tiles for many rows (compute-bound). BM x BN tile per workgroup of 4
-// waves (2 x 2); 64-deep stages in a ring of S LDS slots, filled by direct-to-LDS DMA
+// Pipelined MFMA tiles for many rows (compute-bound). BM x BN tile per workgroup of
+// WM x WN waves; 64-deep stages in a ring of S LDS slots, filled by direct-to-LDS DMA
 // (global_load_lds_dwordx4: 64 lanes x 16 bytes into 1 KB of consecutive LDS), so S - 1
 // stages of loads are in flight without registers. A stage holds BM rows of X and BN
 // rows of W, 128 bytes (eight 16-byte cells) each; cell c of row r is stored at
@@ -373,12 +373,13 @@ __device__ __forceinline__ void pipe_issue(const uint16_t* const (&src)[NI], lon
   for (int i = 0; i < NI; ++i) __builtin_amdgcn_global_load_lds(src[i] + off, dst + 512 * i, 16, 0, 0);
 }
 
-template <int BM, int BN, int S>
-__global__ __launch_bounds__(256) void gdn_proj_pipe(const ProjArgs p) {
+template <int BM, int BN, int S, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) {
+  constexpr int NW = WM * WN;           // waves
   constexpr int R = BM + BN;            // rows per stage
-  constexpr int NI = R / 8 / 4;         // DMA instructions per wave per stage
-  constexpr int TI = BM / 2 / 16, TJ = BN / 2 / 16;
-  static_assert(R % 32 == 0 && TI >= 1 && TJ >= 1, "tile shape");
+  constexpr int NI = R / 8 / NW;        // DMA instructions per wave per stage
+  constexpr int TI = BM / WM / 16, TJ = BN / WN / 16;
+  static_assert(R % (8 * NW) == 0 && TI >= 1 && TJ >= 1, "tile shape");
   static_assert((S - 2) * NI < 64, "memory counter range");
   __shared__ __attribute__((aligned(16))) uint16_t ring[S][R][64];
 
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(256) void gdn_proj_pipe(const ProjArgs p) {
   const long m0 = static_cast<long>(blockIdx.y) * BM;
   const int K = p.K;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
 
   // this lane's DMA sources: instruction i of wave w fills rows 8 (NI w + i) .. + 7
   const uint16_t* src[NI];
@@ -426,12 +427,12 @@ __global__ __launch_bounds__(256) void gdn_proj_pipe(const ProjArgs p) {
       bf16x8 a[TI], bb[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const int r = wm * (BM / 2) + 16 * i + c16;
+        const int r = wm * (BM / WM) + 16 * i + c16;
         a[i] = *reinterpret_cast<const bf16x8*>(st + 64 * r + 8 * ((4 * kk + q) ^ (r & 7)));
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const int r = BM + wn * (BN / 2) + 16 * j + c16;
+        const int r = BM + wn * (BN / WN) + 16 * j + c16;
         bb[j] = *reinterpret_cast<const bf16x8*>(st + 64 * r + 8 * ((4 * kk + q) ^ (r & 7)));
       }
 #pragma unroll
@@ -445,16 +446,16 @@ __global__ __launch_bounds__(256) void gdn_proj_pipe(const ProjArgs p) {
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const long n = n0 + wn * (BN / 2) + 16 * j + c16;
+      const long n = n0 + wn * (BN / WN) + 16 * j + c16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const long m = m0 + wm * (BM / 2) + 16 * i + 4 * q + r;
+        const long m = m0 + wm * (BM / WM) + 16 * i + 4 * q + r;
         if (m < p.M && n < s.n) put(s, m, n, acc[i][j][r]);
       }
     }
 }
 
-template <int BM, int BN, int S>
+template <int BM, int BN, int S, int WM = 2, int WN = 2>
 hipError_t launch_pipe(ProjArgs& p, hipStream_t st) {
   int tiles = 0;
   for (int i = 0; i < p.nseg; ++i) {
@@ -462,7 +463,7 @@ hipError_t launch_pipe(ProjArgs& p, hipStream_t st) {
     tiles += static_cast<int>((p.seg[i].n + BN - 1) / BN);
   }
   const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>((p.M + BM - 1) / BM));
-  gdn_proj_pipe<BM, BN, S><<<grid, 256, 0, st>>>(p);
+  gdn_proj_pipe<BM, BN, S, WM, WN><<<grid, 64 * WM * WN, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -528,6 +529,10 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
     for (int i = 0; i < p.nseg; ++i) n += (p.seg[i].n + bn - 1) / bn;
     return n * ((p.M + bm - 1) / bm);
   };
+  // many rows (in_proj at 512+): 256 x 128 tiles of 8 waves on a 3-stage DMA ring (144 KB
+  // of LDS, one workgroup of two waves per SIMD per CU): 61.0 / 118.4 -> 47.8 / 95.6 us at
+  // 512 / 1024 rows
+  if (tiles(256, 128) >= 128) return launch_pipe<256, 128, 3, 4, 2>(p, st);
   if (tiles(128, 128) >= 256) return launch_mfma<128, 128, 64, 2, 2>(p, st);
   // 64 x 64 tiles: the DMA-fed ring of 4 stages (64 KB of LDS, two workgroups per CU).
   // out_proj at 512 / 1024 rows: 44.4 / 50.4 -> 25.7 / 31.1 us; in_proj at 128 rows:
