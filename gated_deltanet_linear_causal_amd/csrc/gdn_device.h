@@ -3,8 +3,6 @@
 // state, gate and norm arithmetic, the lane layout of a state pass and the delta rule.
 #pragma once
 
-#include <type_traits>
-
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -115,10 +113,58 @@ __device__ __forceinline__ float4 fma4(float4 a, float s, float4 c) {
   return make_float4(fmaf(a.x, s, c.x), fmaf(a.y, s, c.y), fmaf(a.z, s, c.z), fmaf(a.w, s, c.w));
 }
 
+// v + (v of lane ^ M), computed on the VALU instead of through the LDS crossbar
+// (ds_bpermute): every lane gets exactly the value of v + __shfl_xor(v, M) (the same
+// two operands; fp addition is commutative). M = 1, 2: DPP quad permutations; 4: quad
+// mirror then half-row mirror; 8: row rotate by 8; 16, 32: v_permlane16_swap /
+// v_permlane32_swap of two copies of v, after which the two registers hold v and its
+// partner in some order. The swaps are inline asm with both registers read and written
+// (the compiler's builtins return one register for both results), after two wait states.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+template <int M>
+__device__ __forceinline__ float xor_add(float v) {
+  if constexpr (M == 1) {
+    return v + dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return v + dpp_mov<0x4E>(v);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    return v + dpp_mov<0x141>(dpp_mov<0x1B>(v));  // quad_perm [3,2,1,0], then row_half_mirror
+  } else if constexpr (M == 8) {
+    return v + dpp_mov<0x128>(v);  // row_ror:8
+  } else if constexpr (M == 16) {
+    float a = v, b = v;
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return a + b;
+  } else {
+    static_assert(M == 32, "lane mask");
+    float a = v, b = v;
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return a + b;
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void xor_round(float4& m, float4& pq) {
+  m.x = xor_add<M>(m.x);
+  m.y = xor_add<M>(m.y);
+  m.z = xor_add<M>(m.z);
+  m.w = xor_add<M>(m.w);
+  pq.x = xor_add<M>(pq.x);
+  pq.y = xor_add<M>(pq.y);
+  pq.z = xor_add<M>(pq.z);
+  pq.w = xor_add<M>(pq.w);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v = xor_add<32>(v);
+  v = xor_add<16>(v);
+  v = xor_add<8>(v);
+  v = xor_add<4>(v);
+  v = xor_add<2>(v);
+  return xor_add<1>(v);
 }
 
 // Sum of NV values over the whole workgroup; every lane gets the same totals (same
@@ -185,17 +231,13 @@ __device__ __forceinline__ float4 delta_rule(float4 (&hreg)[R], const float* kr,
     pq = fma4(hreg[4 * k4 + 2], qq.z, pq);
     pq = fma4(hreg[4 * k4 + 3], qq.w, pq);
   }
-#pragma unroll
-  for (int msk = CGL; msk < 64; msk <<= 1) {
-    m.x += __shfl_xor(m.x, msk, 64);
-    m.y += __shfl_xor(m.y, msk, 64);
-    m.z += __shfl_xor(m.z, msk, 64);
-    m.w += __shfl_xor(m.w, msk, 64);
-    pq.x += __shfl_xor(pq.x, msk, 64);
-    pq.y += __shfl_xor(pq.y, msk, 64);
-    pq.z += __shfl_xor(pq.z, msk, 64);
-    pq.w += __shfl_xor(pq.w, msk, 64);
-  }
+  // reduce over the row groups: lanes l ^ CGL, l ^ 2 CGL, ... up to l ^ 32
+  if constexpr (CGL <= 1) xor_round<1>(m, pq);
+  if constexpr (CGL <= 2) xor_round<2>(m, pq);
+  if constexpr (CGL <= 4) xor_round<4>(m, pq);
+  if constexpr (CGL <= 8) xor_round<8>(m, pq);
+  if constexpr (CGL <= 16) xor_round<16>(m, pq);
+  xor_round<32>(m, pq);
   const float4 delta = beta * (v4 - alpha * m);
   if (delta_out) *delta_out = delta;
   // keep k out of registers across the shuffles: re-read it from LDS
