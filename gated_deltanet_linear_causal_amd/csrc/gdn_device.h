@@ -189,9 +189,10 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float* red) {
 }
 
 // Lane layout of the state pass for head dim D and P heads per pass.
-template <int D, int P>
+// RR > 0 overrides the rows per lane (fewer rows: more lanes per head, fewer VGPRs).
+template <int D, int P, int RR = 0>
 struct Layout {
-  static constexpr int R = (D == 128) ? 32 : (D == 64 ? 16 : 4);  // rows per lane
+  static constexpr int R = RR > 0 ? RR : ((D == 128) ? 32 : (D == 64 ? 16 : 4));  // rows per lane
   static constexpr int CG = D / 4;                                 // float4 column groups
   static constexpr int RG = D / R;                                 // row groups
   static constexpr int LPH = CG * RG;                              // lanes per head
@@ -213,7 +214,7 @@ template <int D, int P, bool STORE, bool STREAM, int R>
 __device__ __forceinline__ float4 delta_rule(float4 (&hreg)[R], const float* kr, const float* qr, float4 v4,
                                              float alpha, float beta, float kq, __amdgpu_buffer_rsrc_t srs,
                                              uint32_t voff, uint32_t soff, float4* delta_out = nullptr) {
-  using L = Layout<D, P>;
+  using L = Layout<D, P, R>;
   static_assert(R == L::R, "rows per lane");
   constexpr int CGL = L::CGL;
   constexpr uint32_t kRowBytes = D * 4;

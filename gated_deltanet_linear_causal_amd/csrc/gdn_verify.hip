@@ -19,9 +19,14 @@ namespace {
 // (B) the T delta-rule steps on the VGPR-resident state with no barrier between them,
 // (C) the per-head RMSNorm and the outputs of all T tokens (one block reduction).
 // ----------------------------------------------------------------------------------
+// d = 128 uses 16 state rows per lane (4 waves per head, 64 state VGPRs): the per-token
+// work per lane halves and more workgroups stay resident.
+template <int D>
+using VerifyLayout = Layout<D, 1, D == 128 ? 16 : 0>;
+
 template <int D, bool BF>
-__global__ __launch_bounds__((Layout<D, 1>::NT)) void gdn_verify_kernel(const KernelArgs a) {
-  using L = Layout<D, 1>;
+__global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const KernelArgs a) {
+  using L = VerifyLayout<D>;
   constexpr int NT = L::NT, R = L::R, CGL = L::CGL, NW = L::NW;
   constexpr int NCH = 3 * D;
   constexpr int kTM = kMaxVerifyTokens;
@@ -280,9 +285,9 @@ template <int D>
 hipError_t launch_verify_d(const KernelArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv));
   if (a.act_bf16)
-    gdn_verify_kernel<D, true><<<grid, Layout<D, 1>::NT, 0, s>>>(a);
+    gdn_verify_kernel<D, true><<<grid, VerifyLayout<D>::NT, 0, s>>>(a);
   else
-    gdn_verify_kernel<D, false><<<grid, Layout<D, 1>::NT, 0, s>>>(a);
+    gdn_verify_kernel<D, false><<<grid, VerifyLayout<D>::NT, 0, s>>>(a);
   return hipGetLastError();
 }
 
