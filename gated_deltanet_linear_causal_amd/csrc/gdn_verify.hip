@@ -57,6 +57,11 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
                  : (c < 2 * D ? static_cast<long>(a.Hk + g) * D + (c - D) : static_cast<long>(2 * a.Hk + h) * D + (c - 2 * D));
   };
 
+  const uint32_t voff = static_cast<uint32_t>(rg * R) * kRowBytes + static_cast<uint32_t>(cg) * 16u;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.state + static_cast<long>(bh) * (D * D), D * D * 4);
+  float4 hreg[R];
+  raw_t gdt = 0, gbr = 0;  // raw gate inputs of token t (t < T), converted where used
+
   // ---- A. conv inputs and taps into LDS, then conv + SiLU of every (token, channel), gates
   {
     // 16-byte pieces of 8 consecutive unit channels (a segment's channels are
@@ -74,25 +79,35 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
       for (int e = 0; e < kE; ++e)
         dst[e] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + (elem * (BF ? 2 : 4)) + 16 * e);
     };
+    // Loads are unconditional, with indices clamped to valid rows (only the LDS stores
+    // below are conditional): a load inside a branch is waited for where the branch
+    // joins, which would put each load's latency in series.
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
-      const int it = t + i * NT, j = it / kPieces, pc = it - j * kPieces;
-      if (j < nrow) {
-        const long gc = chan(8 * pc);
-        if (j < K - 1)
-          ld8(a.conv_state, (static_cast<long>(b) * (K - 1) + j) * C + gc, xr[i]);
-        else
-          ld8(a.qkv, b * a.qkv_bs + (j - (K - 1)) * a.qkv_ts + gc, xr[i]);
-      }
+      const int it = min(t + i * NT, nrow * kPieces - 1), j = it / kPieces, pc = it - j * kPieces;
+      const long gc = chan(8 * pc);
+      const bool from_state = j < K - 1;
+      const void* base = from_state ? a.conv_state : a.qkv;
+      const long elem = from_state ? (static_cast<long>(b) * (K - 1) + j) * C + gc
+                                   : b * a.qkv_bs + (j - (K - 1)) * a.qkv_ts + gc;
+      ld8(base, elem, xr[i]);
     }
 #pragma unroll
     for (int i = 0; i < kWPer; ++i) {
-      const int it = t + i * NT;
-      if (it < nw) {
-        const int per_seg = D * K / 8, sg = it / per_seg, off = 8 * (it - sg * per_seg);
-        ld8(a.conv_w, chan(sg * D) * K + off, wr[i]);
-      }
+      const int it = min(t + i * NT, nw - 1);
+      const int per_seg = D * K / 8, sg = it / per_seg, off = 8 * (it - sg * per_seg);
+      ld8(a.conv_w, chan(sg * D) * K + off, wr[i]);
     }
+    // the gate inputs and then the state of head h (read only) go out before the first
+    // LDS store waits for the loads above, so all three latencies overlap; the state is
+    // issued last (vmcnt retires in order) and stays in flight during the conv and norms
+    {
+      const long ab = b * a.ab_bs + min(t, T - 1) * a.ab_ts + h;  // T >= 1
+      gdt = Act<BF>::raw(a.dt_raw, ab);
+      gbr = Act<BF>::raw(a.b_raw, ab);
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) hreg[k] = buf_load4<false>(srs, voff, k * kRowBytes);
     auto put8 = [&](raw_t* dst, const u32x4(&src)[kE]) {  // 8 stored values, as they are
 #pragma unroll
       for (int e = 0; e < kE; ++e) *reinterpret_cast<u32x4*>(dst + e * (16 / sizeof(raw_t))) = src[e];
@@ -109,17 +124,9 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
     }
   }
   if (t < T) {
-    const long ab = b * a.ab_bs + t * a.ab_ts + h;
-    s_gate[0][t] = gate_alpha(Act<BF>::load(a.dt_raw, ab), a.dt_bias[h], a.A_log[h]);
-    s_gate[1][t] = gate_beta(Act<BF>::load(a.b_raw, ab));
+    s_gate[0][t] = gate_alpha(Act<BF>::f(gdt), a.dt_bias[h], a.A_log[h]);
+    s_gate[1][t] = gate_beta(Act<BF>::f(gbr));
   }
-  // the state of head h (read only): issued after the small loads (vmcnt retires in
-  // order), in flight during the conv and the norms
-  const uint32_t voff = static_cast<uint32_t>(rg * R) * kRowBytes + static_cast<uint32_t>(cg) * 16u;
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.state + static_cast<long>(bh) * (D * D), D * D * 4);
-  float4 hreg[R];
-#pragma unroll
-  for (int k = 0; k < R; ++k) hreg[k] = buf_load4<false>(srs, voff, k * kRowBytes);
   __syncthreads();
   for (int c = t; c < NCH; c += NT) {
     float(*dst)[D] = c < D ? s_q : (c < 2 * D ? s_k : s_v);
