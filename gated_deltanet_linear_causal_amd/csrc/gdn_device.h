@@ -30,16 +30,21 @@ struct Act {
   __device__ static __forceinline__ void put(void* p, long i, raw_t v) { static_cast<raw_t*>(p)[i] = v; }
   __device__ static __forceinline__ float f(raw_t v) { return BF ? bf16_to_f32(v) : __uint_as_float(v); }
   __device__ static __forceinline__ float load(const void* p, long i) { return f(raw(p, i)); }
-  // 4 consecutive elements (8-byte aligned for bf16, 16-byte for fp32)
-  __device__ static __forceinline__ float4 load4(const void* p, long i) {
-    if constexpr (BF) {
-      const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+  // 4 consecutive elements (8-byte aligned for bf16, 16-byte for fp32): raw4 loads the
+  // stored words, cvt4 widens them where they are used (a conversion right after a load
+  // makes the wave wait for the load there)
+  using raw4_t = typename std::conditional<BF, uint2, float4>::type;
+  __device__ static __forceinline__ raw4_t raw4(const void* p, long i) {
+    return *reinterpret_cast<const raw4_t*>(static_cast<const raw_t*>(p) + i);
+  }
+  __device__ static __forceinline__ float4 cvt4(raw4_t w) {
+    if constexpr (BF)
       return make_float4(bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xffffu),
                          bf16_to_f32(w.y >> 16));
-    } else {
-      return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-    }
+    else
+      return w;
   }
+  __device__ static __forceinline__ float4 load4(const void* p, long i) { return cvt4(raw4(p, i)); }
 };
 
 __device__ __forceinline__ void store_out4(void* p, long i, float4 v, bool bf16) {

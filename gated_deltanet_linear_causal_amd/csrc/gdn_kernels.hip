@@ -182,7 +182,8 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_fast(const Kernel
     cr.load_taps_all(a.conv_w);
   }
   float dt = 0.0f, braw = 0.0f, A_log = 0.0f, dt_bias = 0.0f;
-  float4 z4 = f4(0.0f), w4 = f4(0.0f);
+  typename Act<BF>::raw4_t z_raw{};
+  float4 w4 = f4(0.0f);
   if constexpr (MODE != kModeConv) {
     dt = Act<BF>::load(a.dt_raw, b * a.ab_bs + h);
     braw = Act<BF>::load(a.b_raw, b * a.ab_bs + h);
@@ -190,10 +191,11 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_fast(const Kernel
     dt_bias = a.dt_bias[h];
   }
   if constexpr (MODE == kModeFused) {
-    if (rg == 0) {
-      z4 = Act<BF>::load4(a.z, b * a.z_bs + static_cast<long>(h) * D + 4 * cg);
-      w4 = *reinterpret_cast<const float4*>(a.norm_w + 4 * cg);
-    }
+    // every lane loads (the output lanes are row group 0; the others repeat their
+    // addresses): a load inside a branch is waited for at the join, which would hold
+    // the state loads below until all small loads had returned
+    z_raw = Act<BF>::raw4(a.z, b * a.z_bs + static_cast<long>(h) * D + 4 * cg);
+    w4 = *reinterpret_cast<const float4*>(a.norm_w + 4 * cg);
   }
 
   // ---- 2. the state (the step's whole cost), P heads of k-head g
@@ -271,7 +273,8 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_fast(const Kernel
     } else {
       const float r = head_rms_scale<D, P>(o, rg == 0, ph, hred, a.rms_eps);
       if (rg == 0)
-        store_out4(a.out, b * a.out_bs + static_cast<long>(h) * D + 4 * cg, gated(o, r, w4, z4), a.out_bf16 != 0);
+        store_out4(a.out, b * a.out_bs + static_cast<long>(h) * D + 4 * cg, gated(o, r, w4, Act<BF>::cvt4(z_raw)),
+                   a.out_bf16 != 0);
     }
   }
 }
@@ -368,12 +371,12 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_generic(const Ker
       const int hl = pass * P + ph;
       const int h = g * G + hl;
       const uint32_t soff = static_cast<uint32_t>(pass * P) * kHeadBytes;
-      float4 z4 = f4(0.0f), w4 = f4(0.0f);
-      if constexpr (MODE == kModeFused)
-        if (rg == 0) {
-          z4 = Act<BF>::load4(a.z, b * a.z_bs + static_cast<long>(h) * D + 4 * cg);
-          w4 = *reinterpret_cast<const float4*>(a.norm_w + 4 * cg);
-        }
+      typename Act<BF>::raw4_t z_raw{};  // loaded by every lane, widened where used
+      float4 w4 = f4(0.0f);
+      if constexpr (MODE == kModeFused) {
+        z_raw = Act<BF>::raw4(a.z, b * a.z_bs + static_cast<long>(h) * D + 4 * cg);
+        w4 = *reinterpret_cast<const float4*>(a.norm_w + 4 * cg);
+      }
       const float alpha = gate_alpha(Act<BF>::load(a.dt_raw, b * a.ab_bs + h), a.dt_bias[h], a.A_log[h]);
       const float beta = gate_beta(Act<BF>::load(a.b_raw, b * a.ab_bs + h));
       float4 hreg[R];
@@ -387,7 +390,8 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_generic(const Ker
       } else {
         const float r = head_rms_scale<D, P>(o, rg == 0, ph, hred, a.rms_eps);
         if (rg == 0)
-          store_out4(a.out, b * a.out_bs + static_cast<long>(h) * D + 4 * cg, gated(o, r, w4, z4), a.out_bf16 != 0);
+          store_out4(a.out, b * a.out_bs + static_cast<long>(h) * D + 4 * cg, gated(o, r, w4, Act<BF>::cvt4(z_raw)),
+                     a.out_bf16 != 0);
         if (pass + 1 < passes) __syncthreads();  // hred is rewritten by the next pass
       }
     }
@@ -431,11 +435,8 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_seq_kernel(const Kerne
   const long ab0 = b * a.ab_bs + h;
   float dt = Act<BF>::load(a.dt_raw, ab0), braw = Act<BF>::load(a.b_raw, ab0);
   const long z0 = b * a.z_bs + static_cast<long>(h) * D + 4 * cg;
-  float4 z4 = f4(0.0f), w4 = f4(0.0f);
-  if (rg == 0) {
-    z4 = Act<BF>::load4(a.z, z0);
-    w4 = *reinterpret_cast<const float4*>(a.norm_w + 4 * cg);
-  }
+  typename Act<BF>::raw4_t z_raw = Act<BF>::raw4(a.z, z0);  // every lane: no wait at a branch join
+  const float4 w4 = *reinterpret_cast<const float4*>(a.norm_w + 4 * cg);
   const float A_log = a.A_log[h], dt_bias = a.dt_bias[h];
 
   const uint32_t voff = static_cast<uint32_t>(ph) * kHeadBytes + static_cast<uint32_t>(rg * R) * kRowBytes +
@@ -451,13 +452,13 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_seq_kernel(const Kerne
     cr.roll();
     const float alpha = gate_alpha(dt, dt_bias, A_log);
     const float beta = gate_beta(braw);
-    const float4 zc = z4;
+    const float4 zc = Act<BF>::cvt4(z_raw);
     // prefetch the next token's inputs
     if (tok + 1 < a.T) {
       cr.load_x(a.qkv, b * a.qkv_bs + (tok + 1) * a.qkv_ts);
       dt = Act<BF>::load(a.dt_raw, ab0 + (tok + 1) * a.ab_ts);
       braw = Act<BF>::load(a.b_raw, ab0 + (tok + 1) * a.ab_ts);
-      if (rg == 0) z4 = Act<BF>::load4(a.z, z0 + (tok + 1) * a.z_ts);
+      z_raw = Act<BF>::raw4(a.z, z0 + (tok + 1) * a.z_ts);
     }
     __syncthreads();
     float s3[3] = {0.0f, 0.0f, 0.0f};
