@@ -26,9 +26,9 @@
 // error on the outputs, too coarse for the fp32 recurrence. Operands must stay below
 // the fp16 range (6.5e4); the normalised q, k, the state and delta of this layer are
 // orders of magnitude smaller.
-// The (I + A) solve is an fp32 forward substitution on VALU, one lane per column.
-// With bf16 activations, waves 2-3 prefetch the next chunk's conv inputs, z rows and
-// gates into LDS while waves 0-1 run the solve.
+// The (I + A) solve is an fp32 forward substitution on VALU, two lanes per column.
+// With bf16 activations, the next chunk's conv inputs, z rows and gate inputs are
+// loaded while it runs and stored to LDS after it.
 //
 // The conv state is only read here; a separate epilogue launch writes the rolled
 // state afterwards (two workgroups of a k-head read the same Q/K conv columns).
@@ -74,8 +74,8 @@ constexpr int kTaps = 4;             // conv taps (K)
 // chunk can be formed from LDS alone.
 template <bool BF>
 struct Staging {
-  uint32_t x[kC + kTaps - 1][kPairs + 4];  // two bf16 channels per word
-  uint32_t z[2][kC][kD / 2 + 4];           // z rows of this v-head, double-buffered by chunk parity
+  alignas(16) uint32_t x[kC + kTaps - 1][kPairs + 4];  // two bf16 channels per word
+  alignas(16) uint32_t z[2][kC][kD / 2 + 4];           // z rows of this v-head, double-buffered by chunk parity
 };
 template <>
 struct Staging<false> {};
@@ -88,7 +88,7 @@ struct alignas(16) ChunkSmem {
   union {
     float raw[kC][kRawLd];  // silu(conv) of q (0..127) and k (128..255) before the L2 norm (steps 1-2)
     struct {
-      alignas(16) float at[kC][kALd];  // -A transposed: at[s][t] = -A[t][s], zero for s >= t (steps 3-4)
+      alignas(16) float at[kC][kALd];  // -A transposed, at[s][16 (t & 1) + t / 2] = -A[t][s], zero for s >= t (steps 3-4)
       float x[kC][kXLd];    // right-hand side, then Delta (steps 3-5)
       uint16_t p_hi[kC][kPLd], p_lo[kC][kPLd];  // 2^15 P (steps 3-5)
     } s;
@@ -110,67 +110,92 @@ __device__ __forceinline__ void chunk_gate_inputs(const KernelArgs& a, int b, in
 __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float br, float A_exp, float dt_bias,
                                             float* g_out, float* beta_out);
 
-// Prefetch chunk `ch` (bf16 activations): conv inputs and z rows into LDS, and the
-// chunk's gates. Done by NW waves, the calling one being number WV among them. Every
-// load is a wave-uniform row address plus the lane's dword, so a row of 64 dwords is
-// one coalesced 256-byte access. Rows of tokens past T (last chunk) repeat the last
-// token: the conv outputs and the outputs of such tokens are masked, so their values
-// are never used. With `first`, rows 0..2 come from the conv state; otherwise the last
-// wave first moves the previous chunk's last three rows there (it is the wave that
-// overwrites them, and a wave's LDS accesses complete in order).
-template <int NW, int WV>
-__device__ __forceinline__ void stage_chunk(ChunkSmem<true>& sm, const KernelArgs& a, int b, int g, int h, int ch,
-                                            int lane, bool first, float A_exp, float dt_bias) {
-  Staging<true>& st = sm.st;
+// Prefetch of chunk `ch` (bf16 activations) by the four waves, wave `wv` (wave-uniform)
+// taking tokens 8 wv .. 8 wv + 7: conv inputs and z rows, and (wave 0) the gates. The
+// global loads go to registers first (stage_load) and the LDS stores follow later
+// (stage_store), so that the loads are in flight during the work in between. A row
+// segment is 64 dwords (256 bytes); one 16-byte load per lane covers four rows, lanes
+// 16 r .. 16 r + 15 taking row r, so a wave's 32 rows take 8 loads. Rows of tokens past
+// T (last chunk) repeat the last token: the conv outputs and the outputs of such tokens
+// are masked, so their values are never used.
+struct StageRegs {
+  u32x4 xv[6];   // conv inputs: segment k / 2 (q, k, v) of token 8 wv + 4 (k % 2) + lane / 16
+  u32x4 zv[2];   // z row of token 8 wv + 4 k + lane / 16
+  float dt, br;  // gate inputs of token `lane` (used by wave 0)
+};
+
+__device__ __forceinline__ int seg_offset(int sg, int g, int h, int hk) {  // dword offset of a conv segment
+  return sg == 0 ? g * (kD / 2) : (sg == 1 ? (hk + g) * (kD / 2) : (2 * hk + h) * (kD / 2));
+}
+
+// Buffer resource over `bytes` bytes from `base` (raw dwords; word 3 = 0x00020000 is the
+// raw-dword format of the gfx9 family): the base lives in SGPRs and each lane supplies a
+// 32-bit byte offset, so a load needs no 64-bit address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ void stage_load(const KernelArgs& a, int b, int g, int h, int ch, int lane, int wv,
+                                           StageRegs& r) {
   const int T = a.T, t0 = ch * kC, nt = min(kC, T - t0);
-  // Row strides and segment offsets in dwords, opaque to the optimiser so that the
-  // per-row offsets are recomputed here (a few scalar ops) instead of being hoisted
-  // out of the chunk loop into registers.
+  // Row strides and segment offsets in dwords, opaque to the optimiser so that they are
+  // recomputed here (a few scalar ops) instead of being held across the chunk loop.
   int cw = a.C / 2, zw = a.Hv * (kD / 2), hk = a.Hk;
   asm volatile("" : "+s"(cw), "+s"(zw), "+s"(hk));
-  // conv rows: (token t, segment s) with s = 0 q, 1 k of k-head g, 2 v of v-head h
-  constexpr int kXPer = 3 * kC / NW, kZPer = kC / NW;
-  float dt = 0.0f, br = 0.0f;  // gate inputs, loaded first (the gate math then overlaps the other loads)
-  if (WV == 0) chunk_gate_inputs<true>(a, b, h, ch, lane, dt, br);
-  const uint32_t* xb = reinterpret_cast<const uint32_t*>(a.qkv) + (static_cast<long>(b) * T + t0) * cw + lane;
-  const uint32_t* zb = reinterpret_cast<const uint32_t*>(a.z) + (static_cast<long>(b) * T + t0) * zw + h * (kD / 2) + lane;
-  const int so[3] = {g * (kD / 2), (hk + g) * (kD / 2), (2 * hk + h) * (kD / 2)};
-  uint32_t xv[kXPer], zv[kZPer];
+  chunk_gate_inputs<true>(a, b, h, ch, lane, r.dt, r.br);
+  const uint32_t* xb = reinterpret_cast<const uint32_t*>(a.qkv) + (static_cast<long>(b) * T + t0) * cw;
+  const uint32_t* zb = reinterpret_cast<const uint32_t*>(a.z) + (static_cast<long>(b) * T + t0) * zw + h * (kD / 2);
+  const __amdgpu_buffer_rsrc_t xr = rows_rsrc(xb, static_cast<uint32_t>(nt * cw) * 4u);
+  const __amdgpu_buffer_rsrc_t zr = rows_rsrc(zb, static_cast<uint32_t>(nt * zw) * 4u);
+  const int col = 16 * (lane & 15);  // byte offset of the lane's 4 dwords in a segment
 #pragma unroll
-  for (int i = 0; i < kXPer; ++i) {
-    const int r = WV * kXPer + i, t = r / 3, sg = r - 3 * t;
-    xv[i] = xb[min(t, nt - 1) * cw + so[sg]];
-  }
+  for (int half = 0; half < 2; ++half) {
+    const int t = min(8 * wv + 4 * half + (lane >> 4), nt - 1);
 #pragma unroll
-  for (int i = 0; i < kZPer; ++i) {
-    const int t = WV * kZPer + i;
-    zv[i] = zb[min(t, nt - 1) * zw];
+    for (int sg = 0; sg < 3; ++sg)
+      r.xv[2 * sg + half] = __builtin_amdgcn_raw_buffer_load_b128(xr, 4 * (t * cw + seg_offset(sg, g, h, hk)) + col, 0, 0);
+    r.zv[half] = __builtin_amdgcn_raw_buffer_load_b128(zr, 4 * t * zw + col, 0, 0);
   }
+}
+
+// With `first`, rows 0..2 of the staged conv inputs come from the conv state; otherwise
+// wave 3 first moves the previous chunk's last three rows there (it is the wave that
+// overwrites them, and a wave's LDS accesses complete in order).
+__device__ __forceinline__ void stage_store(ChunkSmem<true>& sm, const KernelArgs& a, int b, int g, int h, int ch,
+                                            int lane, int wv, bool first, float A_exp, float dt_bias,
+                                            const StageRegs& r) {
+  Staging<true>& st = sm.st;
   constexpr int kHist = (kTaps - 1) * 3;  // history rows x segments
   if (first) {
     // conv state rows 0..2 ([B][K-1][C], same channel layout as a qkv row)
-    const uint32_t* cb = reinterpret_cast<const uint32_t*>(a.conv_state) + static_cast<long>(b) * (kTaps - 1) * cw + lane;
+    int cw = a.C / 2, hk = a.Hk;
+    asm volatile("" : "+s"(cw), "+s"(hk));
+    const uint32_t* cb = reinterpret_cast<const uint32_t*>(a.conv_state) + static_cast<long>(b) * (kTaps - 1) * cw;
 #pragma unroll
-    for (int r = WV; r < kHist; r += NW) {
-      const int j = r / 3, sg = r - 3 * j;
-      st.x[j][sg * (kD / 2) + lane] = cb[j * cw + so[sg]];
+    for (int k = 0; k < (kHist + 3) / 4; ++k) {
+      const int rr = wv + 4 * k;
+      if (rr < kHist) {
+        const int j = rr / 3, sg = rr - 3 * j;
+        st.x[j][sg * (kD / 2) + lane] = cb[j * cw + seg_offset(sg, g, h, hk) + lane];
+      }
     }
-  } else if (WV == NW - 1) {
+  } else if (wv == 3) {
     uint32_t hist[kHist];
 #pragma unroll
-    for (int r = 0; r < kHist; ++r) hist[r] = st.x[kC + r / 3][(r % 3) * (kD / 2) + lane];
+    for (int rr = 0; rr < kHist; ++rr) hist[rr] = st.x[kC + rr / 3][(rr % 3) * (kD / 2) + lane];
 #pragma unroll
-    for (int r = 0; r < kHist; ++r) st.x[r / 3][(r % 3) * (kD / 2) + lane] = hist[r];
+    for (int rr = 0; rr < kHist; ++rr) st.x[rr / 3][(rr % 3) * (kD / 2) + lane] = hist[rr];
   }
-  if (WV == 0) chunk_gates(a.T - t0, lane, dt, br, A_exp, dt_bias, sm.g[ch & 1], sm.beta[ch & 1]);
+  if (wv == 0) chunk_gates(a.T - ch * kC, lane, r.dt, r.br, A_exp, dt_bias, sm.g[ch & 1], sm.beta[ch & 1]);
 #pragma unroll
-  for (int i = 0; i < kXPer; ++i) {
-    const int r = WV * kXPer + i, t = r / 3, sg = r - 3 * t;
-    st.x[kTaps - 1 + t][sg * (kD / 2) + lane] = xv[i];
+  for (int half = 0; half < 2; ++half) {
+    const int t = 8 * wv + 4 * half + (lane >> 4);
+#pragma unroll
+    for (int sg = 0; sg < 3; ++sg)
+      *reinterpret_cast<u32x4*>(&st.x[kTaps - 1 + t][sg * (kD / 2) + 4 * (lane & 15)]) = r.xv[2 * sg + half];
+    *reinterpret_cast<u32x4*>(&st.z[ch & 1][t][4 * (lane & 15)]) = r.zv[half];
   }
-  const int par = ch & 1;
-#pragma unroll
-  for (int i = 0; i < kZPer; ++i) st.z[par][WV * kZPer + i][lane] = zv[i];
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t u) { return __uint_as_float(u << 16); }
@@ -229,12 +254,11 @@ __device__ __forceinline__ float row16_sum(float v) {
 template <bool BF>
 __device__ __forceinline__ void chunk_gate_inputs(const KernelArgs& a, int b, int h, int ch, int lane, float& dt,
                                                   float& br) {
+  // lanes past the end read the last token (the gates mask them)
   const int t0 = ch * kC;
-  if (lane < min(kC, a.T - t0)) {
-    const long ai = (static_cast<long>(b) * a.T + t0 + lane) * a.Hv + h;
-    dt = raw_f32<BF>(load_raw<BF>(a.dt_raw, ai));
-    br = raw_f32<BF>(load_raw<BF>(a.b_raw, ai));
-  }
+  const long ai = (static_cast<long>(b) * a.T + t0 + min(lane, min(kC, a.T - t0) - 1)) * a.Hv + h;
+  dt = raw_f32<BF>(load_raw<BF>(a.dt_raw, ai));
+  br = raw_f32<BF>(load_raw<BF>(a.b_raw, ai));
 }
 
 __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float br, float A_exp, float dt_bias,
@@ -396,12 +420,10 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
   const int nchunks = (T + kC - 1) / kC;
   if constexpr (BF) {
     if (nchunks > 0) {
-      switch (__builtin_amdgcn_readfirstlane(w)) {
-        case 0: stage_chunk<4, 0>(sm, a, b, g, h, 0, l, true, A_exp, dt_bias); break;
-        case 1: stage_chunk<4, 1>(sm, a, b, g, h, 0, l, true, A_exp, dt_bias); break;
-        case 2: stage_chunk<4, 2>(sm, a, b, g, h, 0, l, true, A_exp, dt_bias); break;
-        default: stage_chunk<4, 3>(sm, a, b, g, h, 0, l, true, A_exp, dt_bias); break;
-      }
+      const int wv = __builtin_amdgcn_readfirstlane(w);
+      StageRegs sr;
+      stage_load(a, b, g, h, 0, l, wv, sr);
+      stage_store(sm, a, b, g, h, 0, l, wv, true, A_exp, dt_bias, sr);
     }
     __syncthreads();
   }
@@ -485,6 +507,13 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
       }
     }
     __syncthreads();
+
+    // The next chunk's inputs (bf16 activations) are loaded here and stored to LDS after
+    // the solve: phases 2 and 3 cover the loads' latency.
+    const int wv = __builtin_amdgcn_readfirstlane(w);
+    [[maybe_unused]] StageRegs sr;
+    const int chn = min(ch + 1, nchunks - 1);
+    if constexpr (BF) stage_load(a, b, g, h, chn, l, wv, sr);
 
     // ---- 2. L2 norms of q and k; split planes [t][i] and [i][t]. Wave w takes tokens
     // 8w .. 8w+7, lane l channels 2l and 2l+1; the 16 reductions run side by side.
@@ -596,7 +625,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         const float e = (s <= t) ? ex : 0.0f;
         // kk and qk carry the 2^15 x 2^15 operand scale
         const float av = -(bt[r] * e * (kk[r] * (kDown * kDown)));
-        sm.u.s.at[s][t] = (s < t) ? av : 0.0f;
+        sm.u.s.at[s][16 * (t & 1) + (t >> 1)] = (s < t) ? av : 0.0f;
         put_split(&sm.u.s.p_hi[0][0], &sm.u.s.p_lo[0][0], t * kPLd + s, e * (qk[r] * kDown), one);  // = 2^15 P
       }
     }
@@ -664,41 +693,45 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     }
     __syncthreads();
 
-    // ---- 4. forward substitution (I + A) Delta = rhs, one lane per column j, in
-    // right-looking order: once delta_s is final it is eliminated from every later row,
-    // so the updates of different rows are independent.
-    if (tid < kD) {
-      float d[kC];
+    // ---- 4. forward substitution (I + A) Delta = rhs in right-looking order: once
+    // delta_s is final it is eliminated from every later row, so the updates of different
+    // rows are independent. Two lanes per column j (all four waves): lane parity p holds
+    // the rows t = 2i + p; at step s the lane holding row s passes delta_s to its partner
+    // by DPP. With bf16 activations the next chunk's inputs are stored to LDS afterwards.
+    {
+      const int j = 32 * w + (l >> 1), p = l & 1;
+      float d[kC / 2];
 #pragma unroll
-      for (int t = 0; t < kC; ++t) d[t] = sm.u.s.x[t][tid];
-      // rows of -A^T are read two rows ahead of their use
-      f32x4 ring[3][kC / 4];
-      auto fetch = [&](int s_, f32x4(&dst)[kC / 4]) {
+      for (int i = 0; i < kC / 2; ++i) d[i] = sm.u.s.x[2 * i + p][j];
+      // rows of -A^T (this lane's parity) are read two rows ahead of their use; at step s
+      // the rows i >= lo(s) are updated (for s even and p = 0 that includes row s itself,
+      // whose coefficient is 0)
+      auto lo = [](int s_) { return (s_ & 1) ? (s_ >> 1) + 1 : (s_ >> 1); };
+      constexpr int kAhead = 2;
+      f32x4 ring[kAhead + 1][kC / 8];
+      auto fetch = [&](int s_, f32x4(&dst)[kC / 8]) {
 #pragma unroll
-        for (int t4 = (s_ + 1) / 4; t4 < kC / 4; ++t4) dst[t4] = *reinterpret_cast<const f32x4*>(&sm.u.s.at[s_][4 * t4]);
+        for (int i4 = lo(s_) / 4; i4 < kC / 8; ++i4) dst[i4] = *reinterpret_cast<const f32x4*>(&sm.u.s.at[s_][16 * p + 4 * i4]);
       };
-      fetch(0, ring[0]);
-      fetch(1, ring[1]);
+#pragma unroll
+      for (int s = 0; s < kAhead; ++s) fetch(s, ring[s]);
 #pragma unroll
       for (int s = 0; s < kC - 1; ++s) {
-        if (s + 2 < kC - 1) fetch(s + 2, ring[(s + 2) % 3]);
+        if (s + kAhead < kC - 1) fetch(s + kAhead, ring[(s + kAhead) % (kAhead + 1)]);
+        // quad_perm [0,0,2,2] (even lane of the pair) or [1,1,3,3] (odd lane)
+        const float ds = (s & 1) ? dpp<0xF5>(d[s >> 1]) : dpp<0xA0>(d[s >> 1]);
 #pragma unroll
-        for (int t4 = (s + 1) / 4; t4 < kC / 4; ++t4) {
-          const f32x4 m = ring[s % 3][t4];
+        for (int i4 = lo(s) / 4; i4 < kC / 8; ++i4) {
+          const f32x4 m = ring[s % (kAhead + 1)][i4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (4 * t4 + e > s) d[4 * t4 + e] = fmaf(m[e], d[s], d[4 * t4 + e]);
+            if (4 * i4 + e >= lo(s)) d[4 * i4 + e] = fmaf(m[e], ds, d[4 * i4 + e]);
         }
       }
 #pragma unroll
-      for (int t = 0; t < kC; ++t) sm.u.s.x[t][tid] = d[t];
-    } else if constexpr (BF) {
-      // waves 2-3 prefetch the next chunk's inputs meanwhile
-      if (ch + 1 < nchunks) {
-        if (__builtin_amdgcn_readfirstlane(w) == 2)
-          stage_chunk<2, 0>(sm, a, b, g, h, ch + 1, l, false, A_exp, dt_bias);
-        else
-          stage_chunk<2, 1>(sm, a, b, g, h, ch + 1, l, false, A_exp, dt_bias);
+      for (int i = 0; i < kC / 2; ++i) sm.u.s.x[2 * i + p][j] = d[i];
+      if constexpr (BF) {
+        if (ch + 1 < nchunks) stage_store(sm, a, b, g, h, ch + 1, l, wv, false, A_exp, dt_bias, sr);
       }
     }
     __syncthreads();
