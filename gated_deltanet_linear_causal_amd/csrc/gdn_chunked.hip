@@ -439,6 +439,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     asm volatile("" : "+s"(one));
     const int tid = tid_;
     const int w = tid >> 6, l = tid & 63, q = l >> 4, c16 = l & 15;
+    const int hw = __builtin_amdgcn_readfirstlane(w) >> 1;  // row block of the wave's K K^T / Q K^T tile
 
     // ---- 1. conv + SiLU of this chunk's tokens (and, fp32, the gates)
     if constexpr (BF) {
@@ -586,34 +587,68 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     }
     __syncthreads();
 
-    // ---- 3a. K K^T and Q K^T (32 x 32): wave w computes tile (w/2, w%2) of each
-    {
-      const int tt = w >> 1, st = w & 1;
-      u32x4 fr[kD / 32][6];  // all operand fragments read before the first product
+    // ---- 3. K K^T and Q K^T (32 x 32), K H0 and Q H0 (this wave's columns) on MFMA, in
+    // one pass over the K and Q fragments. Wave w computes tile (w/2, w%2) of K K^T and
+    // Q K^T (tile (0, 1) lies above the diagonal: all its entries are masked). The wave
+    // holds its fragments with its own row block first, slot lt holding row block
+    // lt ^ hw (hw = w / 2), so the A operand of its K K^T / Q K^T tile is always slot 0;
+    // the accumulators of K H0, Q H0 and O follow the same slots.
+    f32x4 kh[2][2], qh[2][2];
 #pragma unroll
-      for (int kb = 0; kb < kD / 32; ++kb) {
-        fr[kb][0] = frag(&sm.k_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        fr[kb][1] = frag(&sm.k_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        fr[kb][2] = frag(&sm.q_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        fr[kb][3] = frag(&sm.q_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        fr[kb][4] = frag(&sm.k_hi[0][0], kQKLd, 16 * st + c16, 32 * kb, q);
-        fr[kb][5] = frag(&sm.k_lo[0][0], kQKLd, 16 * st + c16, 32 * kb, q);
+    for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        kh[lt][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        qh[lt][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
-      // four independent accumulators (K K^T and Q K^T, even and odd blocks) so that
-      // consecutive MFMAs never wait on each other's result
-      f32x4 kk2[2] = {}, qk2[2] = {};
+    // two accumulators each for K K^T and Q K^T (even and odd blocks), so that the three
+    // MFMAs of one are issued apart
+    f32x4 kk2[2] = {}, qk2[2] = {};
+    {
+      const bool same = (w & 1) == hw;  // B operand (K rows of block w % 2) in slot 0, else slot 1
+      // K and Q fragments of block kb + 1 are read while block kb is multiplied
+      u32x4 fq[2][2][4];
+      auto load_fq = [&](int kb, u32x4(&dst)[2][4]) {
 #pragma unroll
-      for (int kb = 0; kb < kD / 32; ++kb) {
+        for (int lt = 0; lt < 2; ++lt) {
+          const int row = 16 * (lt ^ hw) + c16;
+          dst[lt][0] = frag(&sm.k_hi[0][0], kQKLd, row, 32 * kb, q);
+          dst[lt][1] = frag(&sm.k_lo[0][0], kQKLd, row, 32 * kb, q);
+          dst[lt][2] = frag(&sm.q_hi[0][0], kQKLd, row, 32 * kb, q);
+          dst[lt][3] = frag(&sm.q_lo[0][0], kQKLd, row, 32 * kb, q);
+        }
+      };
+      load_fq(0, fq[0]);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb + 1 < 4) load_fq(kb + 1, fq[(kb + 1) & 1]);
+        const u32x4(&f0)[4] = fq[kb & 1][0];
+        const u32x4 bkh = same ? fq[kb & 1][0][0] : fq[kb & 1][1][0];
+        const u32x4 bkl = same ? fq[kb & 1][0][1] : fq[kb & 1][1][1];
+        u32x4 hb_hi[2], hb_lo[2];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) bfrag(hacc[2 * kb][jt], hacc[2 * kb + 1][jt], hb_hi[jt], hb_lo[jt], one);
+        // hi*hi, hi*lo, lo*hi of all ten accumulators in turn (independent neighbours)
 #pragma unroll
         for (int part = 0; part < 3; ++part) {
-          const u32x4 ka = part == 2 ? fr[kb][1] : fr[kb][0], qa = part == 2 ? fr[kb][3] : fr[kb][2];
-          const u32x4 bb = part == 1 ? fr[kb][5] : fr[kb][4];
-          kk2[kb & 1] = mfma(ka, bb, kk2[kb & 1]);
-          qk2[kb & 1] = mfma(qa, bb, qk2[kb & 1]);
+          kk2[kb & 1] = mfma(part == 2 ? f0[1] : f0[0], part == 1 ? bkl : bkh, kk2[kb & 1]);
+          qk2[kb & 1] = mfma(part == 2 ? f0[3] : f0[2], part == 1 ? bkl : bkh, qk2[kb & 1]);
+#pragma unroll
+          for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+              const u32x4(&f)[4] = fq[kb & 1][lt];
+              const u32x4 bb = part == 1 ? hb_lo[jt] : hb_hi[jt];
+              kh[lt][jt] = mfma(part == 2 ? f[1] : f[0], bb, kh[lt][jt]);
+              qh[lt][jt] = mfma(part == 2 ? f[3] : f[2], bb, qh[lt][jt]);
+            }
         }
       }
+    }
+    // A and P of tile (w / 2, w % 2)
+    {
       const f32x4 kk = kk2[0] + kk2[1], qk = qk2[0] + qk2[1];
-      const int t4 = 16 * tt + 4 * q, s = 16 * st + c16;
+      const int t4 = 16 * hw + 4 * q, s = 16 * (w & 1) + c16;
       const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
       const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
       const float gs = sm.g[par][s];
@@ -630,54 +665,12 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
       }
     }
 
-    // ---- 3b. K H0 and Q H0 for this wave's columns; right-hand side of the solve
-    f32x4 kh[2][2], qh[2][2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        kh[tt][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        qh[tt][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
-    {
-      // K and Q fragments of block kb + 1 are read while block kb is multiplied
-      u32x4 fq[2][2][4];
-      auto load_fq = [&](int kb, u32x4(&dst)[2][4]) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          dst[tt][0] = frag(&sm.k_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-          dst[tt][1] = frag(&sm.k_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-          dst[tt][2] = frag(&sm.q_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-          dst[tt][3] = frag(&sm.q_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-        }
-      };
-      load_fq(0, fq[0]);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (kb + 1 < 4) load_fq(kb + 1, fq[(kb + 1) & 1]);
-        u32x4 hb_hi[2], hb_lo[2];
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) bfrag(hacc[2 * kb][jt], hacc[2 * kb + 1][jt], hb_hi[jt], hb_lo[jt], one);
-        // hi*hi, hi*lo, lo*hi of all eight accumulators in turn (independent neighbours)
-#pragma unroll
-        for (int part = 0; part < 3; ++part)
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-              const u32x4(&f)[4] = fq[kb & 1][tt];
-              const u32x4 bb = part == 1 ? hb_lo[jt] : hb_hi[jt];
-              kh[tt][jt] = mfma(part == 2 ? f[1] : f[0], bb, kh[tt][jt]);
-              qh[tt][jt] = mfma(part == 2 ? f[3] : f[2], bb, qh[tt][jt]);
-            }
-      }
-    }
     // rhs[t][j] = beta_t (v_t[j] - gamma_t (K H0)[t][j]);  O starts as gamma_t (Q H0)[t][j]
     // (v is stored as log2(e) v)
-    f32x4 oacc[2][2];
+    f32x4 oacc[2][2];  // slot lt: rows of block lt ^ hw
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int t4 = 16 * tt + 4 * q;
+      const int t4 = 16 * (tt ^ hw) + 4 * q;
       const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
       const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
 #pragma unroll
@@ -742,8 +735,8 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
       u32x4 ph[2], pl[2], kth[8], ktl[8];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        ph[tt] = frag(&sm.u.s.p_hi[0][0], kPLd, 16 * tt + c16, 0, q);
-        pl[tt] = frag(&sm.u.s.p_lo[0][0], kPLd, 16 * tt + c16, 0, q);
+        ph[tt] = frag(&sm.u.s.p_hi[0][0], kPLd, 16 * (tt ^ hw) + c16, 0, q);  // slot order, as oacc
+        pl[tt] = frag(&sm.u.s.p_lo[0][0], kPLd, 16 * (tt ^ hw) + c16, 0, q);
       }
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
@@ -813,7 +806,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         }
         if (c16 == 0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sm.ss[16 * tt + 4 * q + r][w] = s4[r];
+          for (int r = 0; r < 4; ++r) sm.ss[16 * (tt ^ hw) + 4 * q + r][w] = s4[r];
         }
       }
       __syncthreads();
@@ -826,7 +819,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = 16 * tt + 4 * q + r;
+          const int t = 16 * (tt ^ hw) + 4 * q + r;
           sv[tt][r] = *reinterpret_cast<const f32x4*>(&sm.ss[t][0]);
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
@@ -855,7 +848,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int t = 16 * tt + 4 * q + r;
+            const int t = 16 * (tt ^ hw) + 4 * q + r;
             if (full || t < nt) {
 #pragma unroll
               for (int jt = 0; jt < 2; ++jt) outp[row0 + t * zrow + 32 * w + 16 * jt + c16] = cvt(y[tt][r][jt]);
