@@ -357,6 +357,32 @@ __device__ __forceinline__ void put_split(uint16_t* hi_plane, uint16_t* lo_plane
   lo_plane[idx] = static_cast<uint16_t>(l);
 }
 
+// The 16 outputs of a lane (rows 16 (tt ^ hw) + 4q + r, columns 32w + 16jt + c16) as
+// buffer stores at byte offset vo (the lane's row 4q and column) plus the row offset;
+// bf16 outputs are rounded to nearest even.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_rows(const float (&y)[2][4][2], __amdgpu_buffer_rsrc_t ors, int vo, int hw,
+                                           int zr) {
+  constexpr int esz = OUT_BF16 ? 2 : 4;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ro = vo + (16 * (tt ^ hw) + r) * zr * esz;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const float x = y[tt][r][jt];
+        if constexpr (OUT_BF16) {
+          uint32_t u = __float_as_uint(x);
+          u += 0x7fffu + ((u >> 16) & 1u);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(u >> 16), ors, ro + 16 * esz * jt, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), ors, ro + 16 * esz * jt, 0, 0);
+        }
+      }
+    }
+}
+
 template <bool BF>
 __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
   __shared__ ChunkSmem<BF> sm;
@@ -841,29 +867,20 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) y[tt][r][jt] = oacc[tt][jt][r] * rsd * rr * nw[jt] * silu(zz[tt][r][jt]);
         }
-      // rows past the end of the sequence (last chunk only) are not written
-      auto emit = [&](auto* outp, auto cvt) {
-        const bool full = nt == kC;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * (tt ^ hw) + 4 * q + r;
-            if (full || t < nt) {
-#pragma unroll
-              for (int jt = 0; jt < 2; ++jt) outp[row0 + t * zrow + 32 * w + 16 * jt + c16] = cvt(y[tt][r][jt]);
-            }
-          }
-      };
-      if (a.out_bf16) {
-        emit(static_cast<uint16_t*>(a.out), [](float x) {  // round to nearest even
-          uint32_t u = __float_as_uint(x);
-          u += 0x7fffu + ((u >> 16) & 1u);
-          return static_cast<uint16_t>(u >> 16);
-        });
-      } else {
-        emit(static_cast<float*>(a.out), [](float x) { return x; });
-      }
+      // The chunk's nt output rows form one buffer resource: rows past the end of the
+      // sequence (last chunk) fall outside it and are not written (hardware range check).
+      // The lane's part of the byte offset (row 4q, column 32w + c16) is fixed; the row
+      // block and r are wave-uniform.
+      const int esz = a.out_bf16 ? 2 : 4;
+      const int zr = a.Hv * kD;  // elements per token row
+      const __amdgpu_buffer_rsrc_t ors = rows_rsrc(
+          static_cast<char*>(a.out) + ((static_cast<long>(b) * T + t0) * zr + static_cast<long>(h) * kD) * esz,
+          static_cast<uint32_t>(nt * zr * esz));
+      const int vo = (4 * q * zr + 32 * w + c16) * esz;
+      if (a.out_bf16)
+        store_rows<true>(y, ors, vo, hw, zr);
+      else
+        store_rows<false>(y, ors, vo, hw, zr);
     }
     __syncthreads();  // LDS is rewritten by the next chunk
   }

@@ -298,6 +298,33 @@ def test_chunked_bf16_output():
     GC.compare("chunk bf16-out state", GC.host_f64(dv.state), r_st, "bf16")
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_chunked_ragged_tail_writes_nothing_past_end(out_dtype):
+    """The last chunk of a sequence (T = 45: 13 tokens) writes its T rows only: the
+    output sits at the start of a larger buffer whose tail, where rows 45..63 of the
+    last sequence would land, must keep its sentinel."""
+    B, T = 2, 45
+    cfg = cfg_of("chunk_tail", B, 2, 4, 128, 4, "bf16", steps=T, mode="sequence")
+    data = I.generate(cfg)
+    dv = GC.DeviceInputs(cfg, data)
+    s = GC.shape_for(cfg, out_dtype=out_dtype)
+    n = B * T * cfg.z_dim
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    buf = torch.full((n + 32 * cfg.z_dim,), float("nan"), dtype=tdt, device="cuda")
+    out = buf[:n].view(B, T, cfg.z_dim)
+    gdn.gdn_sequence(s, T, dv.conv_state, dv.state, dv.qkv, dv.conv_w, dv.a, dv.b, dv.z, dv.A_log,
+                     dv.dt_bias, dv.norm_w, out)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[n:]).all(), "rows past the end of the last sequence were written"
+    assert torch.isfinite(out).all()
+    r_out, _, _ = GC.oracle_sequence(cfg, data)
+    if out_dtype == "f32":
+        GC.compare("chunk tail out", GC.host_f64(out), r_out, "bf16")
+    else:
+        err = np.abs(GC.host_f64(out) - r_out) - (2.0 ** -7 * np.abs(r_out) + 1e-5)
+        assert np.all(err <= 0), err.max()
+
+
 def test_chunked_resume_across_chunk_boundaries():
     """Splitting a sequence at points that are not chunk multiples changes only the
     rounding: the pieces agree with the whole within the parity tolerance, and the
