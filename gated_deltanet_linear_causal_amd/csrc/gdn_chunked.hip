@@ -734,18 +734,30 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
       };
 #pragma unroll
       for (int s = 0; s < kAhead; ++s) fetch(s, ring[s]);
+      // delta_s from the lane holding row s: quad_perm [0,0,2,2] (even lane of the pair)
+      // or [1,1,3,3] (odd lane)
+      float ds = dpp<0xA0>(d[0]);
 #pragma unroll
       for (int s = 0; s < kC - 1; ++s) {
         if (s + kAhead < kC - 1) fetch(s + kAhead, ring[(s + kAhead) % (kAhead + 1)]);
-        // quad_perm [0,0,2,2] (even lane of the pair) or [1,1,3,3] (odd lane)
-        const float ds = (s & 1) ? dpp<0xF5>(d[s >> 1]) : dpp<0xA0>(d[s >> 1]);
+        const f32x4(&m)[kC / 8] = ring[s % (kAhead + 1)];
+        // the next pivot row (s + 1, slot (s + 1) / 2, always updated at step s) first, so
+        // that its hand-off overlaps the other updates of this step
+        // (two more updates separate it from the DPP read of its result); scheduling
+        // barriers keep the next step's updates, which wait for the hand-off, behind this
+        // step's
+        const int in = (s + 1) >> 1;
+        d[in] = fmaf(m[in >> 2][in & 3], ds, d[in]);
 #pragma unroll
-        for (int i4 = lo(s) / 4; i4 < kC / 8; ++i4) {
-          const f32x4 m = ring[s % (kAhead + 1)][i4];
+        for (int i = in + 1; i < min(in + 3, kC / 2); ++i) d[i] = fmaf(m[i >> 2][i & 3], ds, d[i]);
+        float dn = 0.0f;
+        if (s + 1 < kC - 1) dn = ((s + 1) & 1) ? dpp<0xF5>(d[in]) : dpp<0xA0>(d[in]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * i4 + e >= lo(s)) d[4 * i4 + e] = fmaf(m[e], ds, d[4 * i4 + e]);
-        }
+        for (int i = lo(s); i < kC / 2; ++i)
+          if (i < in || i >= in + 3) d[i] = fmaf(m[i >> 2][i & 3], ds, d[i]);
+        __builtin_amdgcn_sched_barrier(0);
+        ds = dn;
       }
 #pragma unroll
       for (int i = 0; i < kC / 2; ++i) sm.u.s.x[2 * i + p][j] = d[i];
