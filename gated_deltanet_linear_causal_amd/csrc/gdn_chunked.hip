@@ -630,30 +630,77 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     // two accumulators each for K K^T and Q K^T (even and odd blocks), so that the three
     // MFMAs of one are issued apart
     f32x4 kk2[2] = {}, qk2[2] = {};
+    // Factors of the epilogues, formed before the products so that their LDS reads and
+    // exponentials overlap the MFMAs. Tile (w/2, w%2), rows t = 16 hw + 4q + r, column
+    // s = 16 (w % 2) + c16: ea = -beta_t exp(g_t - g_s) 2^-30 for s < t, else 0 (A from
+    // 2^30 k_t.k_s), eb = exp(g_t - g_s) 2^-15 for s <= t, else 0 (2^15 P from 2^30 q_t.k_s).
+    // Rows of slot lt (t = 16 (lt ^ hw) + 4q + r), column j: rhs = c1v + c3 (2^15 K H0) with
+    // c1v = beta_t ln2 v_t[j] (v is stored as log2(e) v), c3 = -beta_t ln2 gamma_t 2^-15
+    // log2(e); O starts as c4 (2^15 Q H0), c4 = gamma_t 2^-15.
+    float ea[4], eb[4];
+    {
+      const int t4 = 16 * hw + 4 * q, s = 16 * (w & 1) + c16;
+      const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
+      const float gs = sm.g[par][s];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t4 + r;
+        // exp(g_t - g_s) <= 1 for s <= t; the other entries are masked (argument clamped)
+        const float e = (s <= t) ? __expf(fminf(gt[r] - gs, 0.0f)) : 0.0f;
+        ea[r] = (s < t) ? -(bt[r] * e * (kDown * kDown)) : 0.0f;
+        eb[r] = e * kDown;
+      }
+    }
+    float c1v[2][4][2], c3[2][4], c4[2][4];
+#pragma unroll
+    for (int lt = 0; lt < 2; ++lt) {
+      const int t4 = 16 * (lt ^ hw) + 4 * q;
+      const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gam = __expf(gt[r]), c1 = bt[r] * kLn2;
+        c3[lt][r] = -c1 * (gam * (kDown * kLog2e));
+        c4[lt][r] = gam * kDown;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) c1v[lt][r][jt] = c1 * sm.v[t4 + r][32 * w + 16 * jt + c16];
+      }
+    }
     {
       const bool same = (w & 1) == hw;  // B operand (K rows of block w % 2) in slot 0, else slot 1
-      // K and Q fragments of block kb + 1 are read while block kb is multiplied
+      // Operands of block kb: K and Q fragments fq[kb & 1] (8: slot lt, plane k_hi, k_lo,
+      // q_hi, q_lo) and the split state hb*[kb & 1] (8 pairs: column tile jt, rows
+      // 32 kb + 4q + {0,1 | 2,3} and 16 + ...). Those of block kb + 1 are produced one
+      // slice at a time between the MFMAs of block kb, each slice with two MFMAs behind
+      // a scheduling barrier, so that the loads and splits issue while the matrix core
+      // works instead of before it.
       u32x4 fq[2][2][4];
-      auto load_fq = [&](int kb, u32x4(&dst)[2][4]) {
-#pragma unroll
-        for (int lt = 0; lt < 2; ++lt) {
-          const int row = 16 * (lt ^ hw) + c16;
-          dst[lt][0] = frag(&sm.k_hi[0][0], kQKLd, row, 32 * kb, q);
-          dst[lt][1] = frag(&sm.k_lo[0][0], kQKLd, row, 32 * kb, q);
-          dst[lt][2] = frag(&sm.q_hi[0][0], kQKLd, row, 32 * kb, q);
-          dst[lt][3] = frag(&sm.q_lo[0][0], kQKLd, row, 32 * kb, q);
-        }
+      u32x4 hbh[2][2], hbl[2][2];
+      auto frag_slice = [&](int kb, int k, u32x4(&dst)[2][4]) {
+        const int lt = k >> 2, pl = k & 3;
+        const uint16_t* plane = pl == 0 ? &sm.k_hi[0][0] : (pl == 1 ? &sm.k_lo[0][0] : (pl == 2 ? &sm.q_hi[0][0] : &sm.q_lo[0][0]));
+        dst[lt][pl] = frag(plane, kQKLd, 16 * (lt ^ hw) + c16, 32 * kb, q);
       };
-      load_fq(0, fq[0]);
+      auto split_slice = [&](int kb, int k, u32x4(&hh)[2], u32x4(&hl)[2]) {
+        const int jt = k >> 2, e = k & 3;
+        const f32x4 src = e < 2 ? hacc[2 * kb][jt] : hacc[2 * kb + 1][jt];
+        uint32_t h_, l_;
+        split2(src[2 * (e & 1)], src[2 * (e & 1) + 1], h_, l_, one);
+        hh[jt][e] = h_;
+        hl[jt][e] = l_;
+      };
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        frag_slice(0, k, fq[0]);
+        split_slice(0, k, hbh[0], hbl[0]);
+      }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        if (kb + 1 < 4) load_fq(kb + 1, fq[(kb + 1) & 1]);
-        const u32x4(&f0)[4] = fq[kb & 1][0];
-        const u32x4 bkh = same ? fq[kb & 1][0][0] : fq[kb & 1][1][0];
-        const u32x4 bkl = same ? fq[kb & 1][0][1] : fq[kb & 1][1][1];
-        u32x4 hb_hi[2], hb_lo[2];
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) bfrag(hacc[2 * kb][jt], hacc[2 * kb + 1][jt], hb_hi[jt], hb_lo[jt], one);
+        const int cb = kb & 1, nb = cb ^ 1;
+        const u32x4(&f0)[4] = fq[cb][0];
+        const u32x4 bkh = same ? fq[cb][0][0] : fq[cb][1][0];
+        const u32x4 bkl = same ? fq[cb][0][1] : fq[cb][1][1];
         // hi*hi, hi*lo, lo*hi of all ten accumulators in turn (independent neighbours)
 #pragma unroll
         for (int part = 0; part < 3; ++part) {
@@ -663,10 +710,16 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
           for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
-              const u32x4(&f)[4] = fq[kb & 1][lt];
-              const u32x4 bb = part == 1 ? hb_lo[jt] : hb_hi[jt];
+              const u32x4(&f)[4] = fq[cb][lt];
+              const u32x4 bb = part == 1 ? hbl[cb][jt] : hbh[cb][jt];
               kh[lt][jt] = mfma(part == 2 ? f[1] : f[0], bb, kh[lt][jt]);
               qh[lt][jt] = mfma(part == 2 ? f[3] : f[2], bb, qh[lt][jt]);
+              const int k = 4 * part + 2 * lt + jt;
+              if (kb + 1 < 4 && k < 8) {
+                frag_slice(kb + 1, k, fq[nb]);
+                split_slice(kb + 1, k, hbh[nb], hbl[nb]);
+              }
+              __builtin_amdgcn_sched_barrier(0);
             }
         }
       }
@@ -675,40 +728,26 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     {
       const f32x4 kk = kk2[0] + kk2[1], qk = qk2[0] + qk2[1];
       const int t4 = 16 * hw + 4 * q, s = 16 * (w & 1) + c16;
-      const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
-      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
-      const float gs = sm.g[par][s];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = t4 + r;
-        // exp(g_t - g_s) <= 1 for s <= t; the other entries are masked (argument clamped)
-        const float ex = __expf(fminf(gt[r] - gs, 0.0f));
-        const float e = (s <= t) ? ex : 0.0f;
-        // kk and qk carry the 2^15 x 2^15 operand scale
-        const float av = -(bt[r] * e * (kk[r] * (kDown * kDown)));
-        sm.u.s.at[s][16 * (t & 1) + (t >> 1)] = (s < t) ? av : 0.0f;
-        put_split(&sm.u.s.p_hi[0][0], &sm.u.s.p_lo[0][0], t * kPLd + s, e * (qk[r] * kDown), one);  // = 2^15 P
+        sm.u.s.at[s][16 * (t & 1) + (t >> 1)] = ea[r] * kk[r];
+        put_split(&sm.u.s.p_hi[0][0], &sm.u.s.p_lo[0][0], t * kPLd + s, eb[r] * qk[r], one);  // = 2^15 P
       }
     }
 
     // rhs[t][j] = beta_t (v_t[j] - gamma_t (K H0)[t][j]);  O starts as gamma_t (Q H0)[t][j]
-    // (v is stored as log2(e) v)
     f32x4 oacc[2][2];  // slot lt: rows of block lt ^ hw
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t4 = 16 * (tt ^ hw) + 4 * q;
-      const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
-      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float gam = __expf(gt[r]);
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
-          const int j = 32 * w + 16 * jt + c16;
-          sm.u.s.x[t4 + r][j] = (bt[r] * kLn2) * (sm.v[t4 + r][j] - (gam * (kDown * kLog2e)) * kh[tt][jt][r]);
-          oacc[tt][jt][r] = gam * (qh[tt][jt][r] * kDown);
+          sm.u.s.x[t4 + r][32 * w + 16 * jt + c16] = fmaf(c3[tt][r], kh[tt][jt][r], c1v[tt][r][jt]);
+          oacc[tt][jt][r] = c4[tt][r] * qh[tt][jt][r];
         }
-      }
     }
     __syncthreads();
 
