@@ -163,7 +163,7 @@ def time_sequence(cfg, d, reps, torch, gdn):
         gdn.gdn_sequence(s, cfg.steps, d["conv_state"], d["state"], d["qkv"], d["conv_w"], d["a"], d["b"], d["z"],
                          d["A_log"], d["dt_bias"], d["norm_w"], out, workspace=ws, stream=stream)
 
-    for _ in range(3):  # untimed: the clock settles over the first few calls
+    for _ in range(10):  # untimed: the clock settles over the first few calls
         run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -429,7 +429,7 @@ def main():
         result["roofline"]["copy_GB_s"] = round(copy_bandwidth(torch), 1)
         c = I.config(4)
         _, dd = build_inputs(c, c.steps, torch)
-        ssec = time_sequence(c, dd, 5, torch, gdn)
+        ssec = time_sequence(c, dd, 20, torch, gdn)
         b = algorithmic_bytes(c, T=c.steps)
         fl = chunk_flops(c) * ((c.steps + 31) // 32) * c.batch * c.num_v_heads
         result["sequence"] = {"workload": "B=8 x T=4096 gdn_sequence (chunked MFMA form, 32-token chunks)",
