@@ -100,6 +100,8 @@ __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t vo
 // ----------------------------------------------------------------------------------
 
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+// the same with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an IEEE divide
+__device__ __forceinline__ float silu_rcp(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
 
 __device__ __forceinline__ float softplus(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
 
@@ -170,6 +172,36 @@ __device__ __forceinline__ float wave_sum(float v) {
   v = xor_add<4>(v);
   v = xor_add<2>(v);
   return xor_add<1>(v);
+}
+
+// Wave sums of N values at once (N a multiple of 4), transposed: each exchange step
+// halves the registers a lane carries while doubling the lanes each covers. After the
+// 32-lane swaps register i < N/2 holds value i (lanes 0-31) or value i + N/2 (lanes
+// 32-63), summed over lanes l and l ^ 32; after the 16-lane swaps register j < N/4 of
+// row r (16 lanes) holds value j + (N/4)(r & 1) + (N/2)(r >> 1), summed over l, l ^ 16,
+// l ^ 32, l ^ 48; a DPP row sum completes it. out[j] is that total on every lane of row
+// r. N/2 + N/4 swaps and N adds replace N wave sums (6N exchanges and adds).
+template <int N>
+__device__ __forceinline__ void wave_sums_t(const float (&v)[N], float (&out)[N / 4]) {
+  static_assert(N % 4 == 0, "N");
+  float h[N / 2];
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    float x0 = v[i], x1 = v[i + N / 2];
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x0), "+v"(x1));
+    h[i] = x0 + x1;
+  }
+#pragma unroll
+  for (int j = 0; j < N / 4; ++j) {
+    float x0 = h[j], x1 = h[j + N / 4];
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x0), "+v"(x1));
+    float r = x0 + x1;
+    r = xor_add<1>(r);
+    r = xor_add<2>(r);
+    r += dpp_mov<0x141>(r);  // row_half_mirror: the other quad of the half-row
+    r += dpp_mov<0x140>(r);  // row_mirror: the other half of the row
+    out[j] = r;
+  }
 }
 
 // Sum of NV values over the whole workgroup; every lane gets the same totals (same
@@ -281,9 +313,11 @@ __device__ __forceinline__ float head_rms_scale(float4 o, bool holder, int ph, f
 }
 
 // norm_weight and the silu(z) gate of steps 8-11
+template <bool RCP = false>
 __device__ __forceinline__ float4 gated(float4 o, float r, float4 w4, float4 z4) {
-  return make_float4(o.x * r * w4.x * silu(z4.x), o.y * r * w4.y * silu(z4.y), o.z * r * w4.z * silu(z4.z),
-                     o.w * r * w4.w * silu(z4.w));
+  auto sl = [](float x) { return RCP ? silu_rcp(x) : silu(x); };
+  return make_float4(o.x * r * w4.x * sl(z4.x), o.y * r * w4.y * sl(z4.y), o.z * r * w4.z * sl(z4.z),
+                     o.w * r * w4.w * sl(z4.w));
 }
 }  // namespace
 }  // namespace gdn

@@ -39,6 +39,7 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   __shared__ __attribute__((aligned(16))) float s_k[kTM][D];
   __shared__ __attribute__((aligned(16))) float s_v[kTM][D];
   __shared__ __attribute__((aligned(16))) float s_o[kTM][D];  // readouts, for the RMSNorm of phase C
+  __shared__ __attribute__((aligned(16))) raw_t s_z[kTM][D];  // z rows of the tokens, staged in phase A
   __shared__ float s_gate[3][kTM];      // alpha, beta, k.q per token
   __shared__ float red[NW][3 * kTM];    // per-wave partial sums
 
@@ -72,8 +73,9 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
     constexpr int kWChunks = NCH * kMaxConvTaps / 8;                   // taps, 8 per chunk
     constexpr int kWPer = (kWChunks + NT - 1) / NT;
     constexpr int kE = BF ? 1 : 2;                                     // 16-byte words per 8 elements
-    const int nrow = K - 1 + T, nw = NCH * K / 8;
-    u32x4 xr[kXPer][kE], wr[kWPer][kE];
+    constexpr int kZPer = (kTM * D / 8 + NT - 1) / NT;                 // z pieces
+    const int nrow = K - 1 + T, nw = NCH * K / 8, nz = T * (D / 8);
+    u32x4 xr[kXPer][kE], wr[kWPer][kE], zr[kZPer][kE];
     auto ld8 = [&](const void* base, long elem, u32x4(&dst)[kE]) {
 #pragma unroll
       for (int e = 0; e < kE; ++e)
@@ -97,6 +99,11 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
       const int it = min(t + i * NT, nw - 1);
       const int per_seg = D * K / 8, sg = it / per_seg, off = 8 * (it - sg * per_seg);
       ld8(a.conv_w, chan(sg * D) * K + off, wr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kZPer; ++i) {
+      const int it = min(t + i * NT, nz - 1), tok = it / (D / 8), pc = it - tok * (D / 8);
+      ld8(a.z, b * a.z_bs + tok * a.z_ts + static_cast<long>(h) * D + 8 * pc, zr[i]);
     }
     // the gate inputs and then the state of head h (read only) go out before the first
     // LDS store waits for the loads above, so all three latencies overlap; the state is
@@ -122,6 +129,11 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
       const int it = t + i * NT;
       if (it < nw) put8(&s_w[8 * it], wr[i]);
     }
+#pragma unroll
+    for (int i = 0; i < kZPer; ++i) {
+      const int it = t + i * NT, tok = it / (D / 8), pc = it - tok * (D / 8);
+      if (it < nz) put8(&s_z[tok][8 * pc], zr[i]);
+    }
   }
   if (t < T) {
     s_gate[0][t] = gate_alpha(Act<BF>::f(gdt), a.dt_bias[h], a.A_log[h]);
@@ -131,12 +143,27 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   for (int c = t; c < NCH; c += NT) {
     float(*dst)[D] = c < D ? s_q : (c < 2 * D ? s_k : s_v);
     const int e = c < D ? c : (c < 2 * D ? c - D : c - 2 * D);
-    for (int tok = 0; tok < T; ++tok) {
-      float u = 0.0f;
+    if (K == 4) {
+      // the common width: taps in registers and a sliding window of the last three
+      // inputs, so each input is read from LDS once
+      const float w0 = Act<BF>::f(s_w[4 * c]), w1 = Act<BF>::f(s_w[4 * c + 1]), w2 = Act<BF>::f(s_w[4 * c + 2]),
+                  w3 = Act<BF>::f(s_w[4 * c + 3]);
+      float x0 = Act<BF>::f(s_x[0][c]), x1 = Act<BF>::f(s_x[1][c]), x2 = Act<BF>::f(s_x[2][c]);
+      for (int tok = 0; tok < T; ++tok) {
+        const float x3 = Act<BF>::f(s_x[tok + 3][c]);  // tap 3 on the token itself
+        dst[tok][e] = silu_rcp(fmaf(w3, x3, fmaf(w2, x2, fmaf(w1, x1, w0 * x0))));
+        x0 = x1;
+        x1 = x2;
+        x2 = x3;
+      }
+    } else {
+      for (int tok = 0; tok < T; ++tok) {
+        float u = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kMaxConvTaps; ++j)
-        if (j < K) u = fmaf(Act<BF>::f(s_w[c * K + j]), Act<BF>::f(s_x[tok + j][c]), u);  // tap K-1 on the token itself
-      dst[tok][e] = silu(u);
+        for (int j = 0; j < kMaxConvTaps; ++j)
+          if (j < K) u = fmaf(Act<BF>::f(s_w[c * K + j]), Act<BF>::f(s_x[tok + j][c]), u);  // tap K-1 on the token itself
+        dst[tok][e] = silu_rcp(u);
+      }
     }
   }
   __syncthreads();
@@ -153,11 +180,15 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
         s3[3 * tok + 1] = fmaf(k, k, s3[3 * tok + 1]);
         s3[3 * tok + 2] = fmaf(q, k, s3[3 * tok + 2]);
       }
+  {
+    float s6[3 * kTM / 4];  // row r holds sum j + 6 (r & 1) + 12 (r >> 1) in register j
+    wave_sums_t<3 * kTM>(s3, s6);
+    if ((lane & 15) == 0) {
+      const int r = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < 3 * kTM; ++i) s3[i] = wave_sum(s3[i]);
-  if (lane == 0)
-#pragma unroll
-    for (int i = 0; i < 3 * kTM; ++i) red[wv][i] = s3[i];
+      for (int j = 0; j < 3 * kTM / 4; ++j) red[wv][j + (3 * kTM / 4) * (r & 1) + (3 * kTM / 2) * (r >> 1)] = s6[j];
+    }
+  }
   __syncthreads();
   const long bt0 = static_cast<long>(b) * T;
   for (int tok = 0; tok < T; ++tok) {
@@ -168,13 +199,17 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
       sk += red[w][3 * tok + 1];
       sqk += red[w][3 * tok + 2];
     }
-    const float rq = 1.0f / sqrtf(sq + a.l2_eps), rk = 1.0f / sqrtf(sk + a.l2_eps);
+    const float rq = __builtin_amdgcn_rsqf(sq + a.l2_eps), rk = __builtin_amdgcn_rsqf(sk + a.l2_eps);
     if (t == 0) s_gate[2][tok] = sqk * rq * rk;
-    for (int i = t; i < D; i += NT) {
-      const float kn = s_k[tok][i] * rk;
-      s_q[tok][i] *= rq;
-      s_k[tok][i] = kn;
-      if (h % a.G == 0) a.trail_k[((bt0 + tok) * a.Hk + g) * D + i] = kn;
+    // elements 0..D-1 scale q, D..2D-1 scale k (and record it in the trail)
+    for (int i = t; i < 2 * D; i += NT) {
+      if (i < D) {
+        s_q[tok][i] *= rq;
+      } else {
+        const float kn = s_k[tok][i - D] * rk;
+        s_k[tok][i - D] = kn;
+        if (h % a.G == 0) a.trail_k[((bt0 + tok) * a.Hk + g) * D + (i - D)] = kn;
+      }
     }
   }
   __syncthreads();
@@ -202,11 +237,17 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
       const float4 o = *reinterpret_cast<const float4*>(&s_o[tok][4 * cg]);
       v = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
     }
-    ss[tok] = wave_sum(v);
+    ss[tok] = v;
   }
-  if (lane == 0)
+  {
+    float s2[kTM / 4];  // row r holds token j + 2 (r & 1) + 4 (r >> 1) in register j
+    wave_sums_t<kTM>(ss, s2);
+    if ((lane & 15) == 0) {
+      const int r = lane >> 4;
 #pragma unroll
-    for (int tok = 0; tok < kTM; ++tok) red[wv][tok] = ss[tok];
+      for (int j = 0; j < kTM / 4; ++j) red[wv][j + (kTM / 4) * (r & 1) + (kTM / 2) * (r >> 1)] = s2[j];
+    }
+  }
   __syncthreads();
   if (rg == 0) {
     const float4 w4 = *reinterpret_cast<const float4*>(a.norm_w + 4 * cg);
@@ -215,10 +256,11 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
       float tot = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) tot += red[w][tok];
-      const float r = 1.0f / sqrtf(tot / static_cast<float>(D) + a.rms_eps);
-      const float4 z4 = Act<BF>::load4(a.z, b * a.z_bs + tok * a.z_ts + static_cast<long>(h) * D + 4 * cg);
+      const float r = __builtin_amdgcn_rsqf(tot / static_cast<float>(D) + a.rms_eps);
+      const float4 z4 = Act<BF>::load4(&s_z[tok][0], 4 * cg);
       const float4 o = *reinterpret_cast<const float4*>(&s_o[tok][4 * cg]);
-      store_out4(a.out, b * a.out_bs + tok * a.out_ts + static_cast<long>(h) * D + 4 * cg, gated(o, r, w4, z4), obf);
+      store_out4(a.out, b * a.out_bs + tok * a.out_ts + static_cast<long>(h) * D + 4 * cg, gated<true>(o, r, w4, z4),
+                 obf);
     }
   }
 }
