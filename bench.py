@@ -6,7 +6,8 @@ readout, gated RMSNorm) over the whole batch, inputs resident in HBM. The worklo
 the Qwen3.5-style layer (H_k = 16, H_v = 32, d_k = d_v = 128, K = 4, bf16 activations,
 fp32 state) at B = 512: its 1 GiB of state exceeds the 256 MB Infinity Cache, so the
 bandwidth figure is a cold-HBM one. 32 distinct steps of inputs are drawn and reused
-cyclically; the state keeps evolving. B = 1 and B = 64 are reported in "sweep", the
+cyclically; the state keeps evolving. B = 1 and B = 64 are reported in "sweep" (each
+step called from the host, and 64 steps captured in one HIP graph and replayed), the
 B = 8 x T = 4096 multi-token call in "sequence", speculative verification (B = 64,
 4 draft tokens) in "verify", the projections around the layer in "proj".
 
@@ -116,6 +117,44 @@ def time_decode(cfg, d, steps, warmup, torch, gdn):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / 1e3 / steps
+
+
+def time_decode_graph(cfg, d, steps, torch, gdn, replays=5):
+    """Average seconds per gdn_decode_layer step when `steps` consecutive steps are
+    captured in one HIP graph and replayed: the device time of a step without the
+    host's per-call launch cost (which bounds small batches when called one by one)."""
+    s = gdn.make_shape(cfg.batch, cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim,
+                       cfg.conv_kernel, cfg.l2_eps, cfg.rms_eps, cfg.act_dtype, "f32")
+    nin = d["qkv"].shape[0]
+    out = torch.empty((cfg.batch, cfg.z_dim), dtype=torch.float32, device="cuda")
+
+    def step(i, st):
+        j = i % nin
+        gdn.gdn_decode_layer(s, d["conv_state"], d["state"], d["qkv"][j], d["conv_w"], d["a"][j], d["b"][j],
+                             d["z"][j], d["A_log"], d["dt_bias"], d["norm_w"], out, stream=st)
+
+    side = torch.cuda.Stream()  # warm-up off the default stream before capture
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(4):
+            step(i, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        for i in range(steps):
+            step(i, st)
+    g.replay()  # untimed
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / 1e3 / (replays * steps)
 
 
 def time_pooled(cfg, d, pool, steps, warmup, torch, gdn):
@@ -421,8 +460,11 @@ def main():
             _, dd = build_inputs(c, 32, torch)
             ssec = time_decode(c, dd, max(args.steps, 200), args.warmup, torch, gdn)
             b = algorithmic_bytes(c)
+            gsec = time_decode_graph(c, dd, 64, torch, gdn)
             sweep["B%d" % c.batch] = {"steps_per_s": round(c.batch / ssec, 1), "us_per_step": round(ssec * 1e6, 2),
-                                      "GB_s": round(b / ssec / 1e9, 1), "frac": round(b / ssec / 1e9 / HBM_PEAK_GBS, 4)}
+                                      "GB_s": round(b / ssec / 1e9, 1), "frac": round(b / ssec / 1e9 / HBM_PEAK_GBS, 4),
+                                      "graph_us_per_step": round(gsec * 1e6, 2),
+                                      "graph_GB_s": round(b / gsec / 1e9, 1)}
             del dd
         result["sweep"] = sweep
         torch.cuda.empty_cache()

@@ -340,3 +340,41 @@ def test_chunked_resume_across_chunk_boundaries():
     GC.compare("chunk resume out", GC.host_f64(out_b), GC.host_f64(out_a), "bf16")
     GC.compare("chunk resume state", GC.host_f64(b.state), GC.host_f64(a.state), "bf16")
     assert torch.equal(a.conv_state, b.conv_state)
+
+
+def test_decode_steps_replayed_from_a_hip_graph():
+    """Four decode steps captured in one HIP graph (the launches go to the capturing
+    stream) and replayed three times, with eager work (state resets, copies) and
+    synchronisations between the replays: every replay reproduces the eager steps bit for
+    bit (outputs, recurrent state, conv state). Also checks the eager steps against the
+    oracle, so the graph path is pinned to the same reference."""
+    cfg = I.config(1).with_(batch=3, steps=4)
+    data = I.generate(cfg)
+    d = GC.DeviceInputs(cfg, data)
+    st0, cs0 = d.state.clone(), d.conv_state.clone()
+    eager = GC.gpu_decode(cfg, d, cfg.steps)
+    st_e, cs_e = d.state.clone(), d.conv_state.clone()
+    r_out, _, _ = GC.oracle_decode(cfg, data, cfg.steps)
+    GC.compare("graph eager out", GC.host_f64(eager), r_out, "bf16")
+
+    s = GC.shape_for(cfg)
+    outs = torch.empty_like(eager)
+    d.state.copy_(st0)
+    d.conv_state.copy_(cs0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        for t in range(cfg.steps):
+            gdn.gdn_decode_layer(s, d.conv_state, d.state, d.qkv[t], d.conv_w, d.a[t], d.b[t], d.z[t], d.A_log,
+                                 d.dt_bias, d.norm_w, outs[t], stream=st)
+    for rep in range(3):
+        d.state.copy_(st0)
+        d.conv_state.copy_(cs0)
+        outs.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs, eager), "replay %d: outputs differ from the eager steps" % rep
+        assert torch.equal(d.state, st_e), "replay %d: state differs" % rep
+        assert torch.equal(d.conv_state, cs_e), "replay %d: conv state differs" % rep
