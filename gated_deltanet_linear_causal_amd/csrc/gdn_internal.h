@@ -79,6 +79,7 @@ struct ProjArgs {
   const uint16_t* x;  // [M][K] bf16
   int nseg;
   long rows;          // sum of the segments' n (set by launch_proj)
+  int ntiles, mblocks;  // column tiles and row blocks of a tiled launch (set by its launcher)
   ProjSeg seg[kMaxProjSegs];
 };
 hipError_t launch_proj(ProjArgs p, hipStream_t stream);

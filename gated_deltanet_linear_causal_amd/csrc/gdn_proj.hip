@@ -383,13 +383,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
   static_assert((S - 2) * NI < 64, "memory counter range");
   __shared__ __attribute__((aligned(16))) uint16_t ring[S][R][64];
 
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by id, so XCD x takes
+  // the column tiles nt = x, x + 8, ..., each with all its row blocks in a row. The
+  // weight tile then comes from HBM once per column tile and the row blocks of the
+  // activations are read by one XCD's workgroups, from its L2.
+  const int id = static_cast<int>(blockIdx.x), xcd = id & 7, k = id >> 3, nmb = p.mblocks;
+  const int nt = (k / nmb) * 8 + xcd;
+  if (nt >= p.ntiles) return;
   int si = 0;
 #pragma unroll
   for (int i = 1; i < kMaxProjSegs; ++i)
-    if (i < p.nseg && static_cast<int>(blockIdx.x) >= p.seg[i].tile0) si = i;
+    if (i < p.nseg && nt >= p.seg[i].tile0) si = i;
   const ProjSeg& s = p.seg[si];
-  const long n0 = static_cast<long>(blockIdx.x - s.tile0) * BN;
-  const long m0 = static_cast<long>(blockIdx.y) * BM;
+  const long n0 = static_cast<long>(nt - s.tile0) * BN;
+  const long m0 = static_cast<long>(k % nmb) * BM;
   const int K = p.K;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
   const int wm = w / WN, wn = w % WN;
@@ -462,7 +469,10 @@ hipError_t launch_pipe(ProjArgs& p, hipStream_t st) {
     p.seg[i].tile0 = tiles;
     tiles += static_cast<int>((p.seg[i].n + BN - 1) / BN);
   }
-  const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>((p.M + BM - 1) / BM));
+  p.ntiles = tiles;
+  p.mblocks = static_cast<int>((p.M + BM - 1) / BM);
+  // one workgroup per (column tile, row block), column tiles rounded up to a multiple of 8
+  const dim3 grid(static_cast<unsigned>(((tiles + 7) / 8) * 8 * p.mblocks));
   gdn_proj_pipe<BM, BN, S, WM, WN><<<grid, 64 * WM * WN, 0, st>>>(p);
   return hipGetLastError();
 }
