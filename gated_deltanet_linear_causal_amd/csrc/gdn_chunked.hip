@@ -719,7 +719,9 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
                 frag_slice(kb + 1, k, fq[nb]);
                 split_slice(kb + 1, k, hbh[nb], hbl[nb]);
               }
-              __builtin_amdgcn_sched_barrier(0);
+              // (the last block has no fences: the epilogues below may start among its
+              // MFMAs once the products they read are final)
+              if (kb + 1 < 4) __builtin_amdgcn_sched_barrier(0);
             }
         }
       }
