@@ -32,10 +32,9 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 
 // Round to nearest even; NaN stays NaN (quiet).
 __device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16, qnan = (u >> 16) | 0x40u;
+  return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? qnan : rne);
 }
 
 __device__ __forceinline__ void put(const ProjSeg& s, long m, long n, float v) {
@@ -79,7 +78,7 @@ __global__ __launch_bounds__(256) void gdn_proj_gemv(const ProjArgs p) {
     for (int r = 0; r < NR; ++r) {
       const long n = r0 + r;
       live[r] = n < p.rows;
-      const ProjSeg& s = p.seg[seg_of(p, live[r] ? n : r0)];
+      const ProjSeg s = p.seg[seg_of(p, live[r] ? n : r0)];
       wr[r] = s.w + (live[r] ? n - s.row0 : 0) * static_cast<long>(K);
     }
     float acc[NR][MT];
@@ -125,7 +124,7 @@ __global__ __launch_bounds__(256) void gdn_proj_gemv(const ProjArgs p) {
       for (int r = 0; r < NR; ++r) {
         if (!live[r]) continue;
         const long n = r0 + r;
-        const ProjSeg& s = p.seg[seg_of(p, n)];
+        const ProjSeg s = p.seg[seg_of(p, n)];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
           if (m < p.M) put(s, m, n - s.row0, acc[r][m]);
@@ -154,7 +153,7 @@ __global__ __launch_bounds__(256) void gdn_proj_mfma(const ProjArgs p) {
 #pragma unroll
   for (int i = 1; i < kMaxProjSegs; ++i)
     if (i < p.nseg && static_cast<int>(blockIdx.x) >= p.seg[i].tile0) si = i;
-  const ProjSeg& s = p.seg[si];
+  const ProjSeg s = p.seg[si];
   const long n0 = static_cast<long>(blockIdx.x - s.tile0) * BN;
   const long m0 = static_cast<long>(blockIdx.y) * BM;
   const int K = p.K;
@@ -258,7 +257,7 @@ __global__ __launch_bounds__(64 * KW) void gdn_proj_skinny(const ProjArgs p) {
 #pragma unroll
   for (int i = 1; i < kMaxProjSegs; ++i)
     if (i < p.nseg && static_cast<int>(blockIdx.x) >= p.seg[i].tile0) si = i;
-  const ProjSeg& s = p.seg[si];
+  const ProjSeg s = p.seg[si];
   const long n0 = static_cast<long>(blockIdx.x - s.tile0) * BN;
   const int K = p.K;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
@@ -394,7 +393,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
 #pragma unroll
   for (int i = 1; i < kMaxProjSegs; ++i)
     if (i < p.nseg && nt >= p.seg[i].tile0) si = i;
-  const ProjSeg& s = p.seg[si];
+  const ProjSeg s = p.seg[si];
   const long n0 = static_cast<long>(nt - s.tile0) * BN;
   const long m0 = static_cast<long>(k % nmb) * BM;
   const int K = p.K;
@@ -418,16 +417,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int nk = K / 64;
+  auto issue = [&](int j) { pipe_issue<NI>(src, 64L * j, ring0 + (j % S) * (R * 64)); };
 #pragma unroll
   for (int i = 0; i < S - 1; ++i)
-    if (i < nk) pipe_issue<NI>(src, 64L * i, ring0 + i * (R * 64));
+    if (i < nk) issue(i);
   for (int kt = 0; kt < nk; ++kt) {
+    // this wave's DMA of stage kt has landed once at most the S - 2 later stages are
+    // outstanding (the memory counter drains in issue order)
     if (kt + S - 2 < nk)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * NI));
     else
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();
-    if (kt + S - 1 < nk) pipe_issue<NI>(src, 64L * (kt + S - 1), ring0 + ((kt + S - 1) % S) * (R * 64));
+    if (kt + S - 1 < nk) issue(kt + S - 1);
     const uint16_t* st = &ring[kt % S][0][0];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -448,18 +450,47 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
         for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
     }
   }
-  // accumulator tile (i, j): lane holds rows 4q + r, column c16
+  // The tile leaves through LDS: the ring is free once every wave is past its last
+  // products, so the accumulators go there as an fp32 BM x BN tile (lane: rows 4q + r,
+  // column c16 of each 16 x 16 block), and the tile is stored row-wise in 16-byte pieces.
+  __syncthreads();
+  float* const tile = reinterpret_cast<float*>(&ring[0][0][0]);
+  constexpr int TS = BN + 4;  // row stride in floats
+  static_assert(BM * TS * 4 <= S * R * 128, "output tile fits the ring");
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const long n = n0 + wn * (BN / WN) + 16 * j + c16;
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const long m = m0 + wm * (BM / WM) + 16 * i + 4 * q + r;
-        if (m < p.M && n < s.n) put(s, m, n, acc[i][j][r]);
+      for (int r = 0; r < 4; ++r)
+        tile[(wm * (BM / WM) + 16 * i + 4 * q + r) * TS + wn * (BN / WN) + 16 * j + c16] = acc[i][j][r];
+  __syncthreads();
+  // E output elements per 16-byte piece; a piece is stored whole when its columns are in
+  // range and the segment's rows keep it 16-byte aligned, else element by element
+  const int E = s.y_bf16 ? 8 : 4;
+  const bool vec = (s.n % E) == 0 && (reinterpret_cast<uintptr_t>(s.y) & 15) == 0;
+  const int pieces = BN / E;
+  for (int e = t; e < BM * pieces; e += 64 * NW) {
+    const int row = e / pieces, c0 = (e % pieces) * E;
+    const long m = m0 + row, n = n0 + c0;
+    if (m >= p.M || n >= s.n) continue;
+    const float* v = tile + row * TS + c0;
+    if (vec && n + E <= s.n) {
+      u32x4 o;
+      if (s.y_bf16) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          o[h] = static_cast<uint32_t>(to_bf16(v[2 * h])) | (static_cast<uint32_t>(to_bf16(v[2 * h + 1])) << 16);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(s.y) + m * s.n + n) = o;
+      } else {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) o[h] = __float_as_uint(v[h]);
+        *reinterpret_cast<u32x4*>(static_cast<float*>(s.y) + m * s.n + n) = o;
       }
+    } else {
+      for (int h = 0; h < E && n + h < s.n; ++h) put(s, m, n + h, v[h]);
     }
+  }
 }
 
 template <int BM, int BN, int S, int WM = 2, int WN = 2>
