@@ -11,10 +11,12 @@ Tolerance: the kernels accumulate in fp32 and round once to the output dtype.
 Shapes cover every kernel: weight streaming (B <= 8, or B <= 2), the skinny MFMA
 kernel (3..32 rows, few output columns: out_proj at B = 3 and 20, in_proj at hidden
 512), 64 x 64 tiles for 33..64 rows (in_proj at B = 40 and 64), 32 x 32 tiles (B = 100),
-the DMA-fed 64 x 64 ring (in_proj at B = 128, out_proj at B = 512 and 600, the latter
-with a ragged last row tile) and 128 x 128 tiles (in_proj at B = 512 and 600); ragged
-row and column tiles (the H_v-wide a/b segments are narrower than a tile) and the
-Qwen3.5-style sizes.
+the DMA-fed 64 x 64 ring (in_proj at B = 128, out_proj at B = 512, 600 and 1024, the
+600 with a ragged last row tile) and the 256 x 128 ring (in_proj at B = 512, 600 and
+1024); ragged row and column tiles (the H_v-wide a/b segments are narrower than a tile)
+and the Qwen3.5-style sizes. The ring kernels store their tiles in 16-byte pieces; a
+segment whose width is not a multiple of 8 bf16 values (the a/b segments of the H_v = 20
+layer at B = 1024) is stored element by element.
 """
 
 import numpy as np
@@ -69,6 +71,7 @@ CASES = [
     (128, 16, 32, 128, 2048, [0, 1, 15, 63, 64, 100, 127]),
     (600, 16, 32, 128, 2048, [0, 63, 64, 511, 512, 575, 576, 599]),
     (512, 16, 32, 128, 2048, [0, 1, 63, 64, 255, 300, 511]),
+    (1024, 4, 20, 128, 2048, [0, 1, 255, 256, 511, 767, 1000, 1023]),
 ]
 
 
