@@ -378,3 +378,37 @@ def test_decode_steps_replayed_from_a_hip_graph():
         assert torch.equal(outs, eager), "replay %d: outputs differ from the eager steps" % rep
         assert torch.equal(d.state, st_e), "replay %d: state differs" % rep
         assert torch.equal(d.conv_state, cs_e), "replay %d: conv state differs" % rep
+
+
+def test_decode_state_beyond_4GiB():
+    """B = 2200 of the Qwen3.5-style layer: the 4.3 GiB recurrent state puts the slices of
+    sequences 1024 and up past 2^31 bytes and those of 2048 and up past 2^32, on the
+    streamed (non-temporal) decode path. Inputs are drawn on the device from a seeded
+    generator (a host copy of the whole state would be 4.3 GiB); the sampled sequences
+    are copied back and recomputed by the oracle."""
+    from oracle import oracle as O
+    cfg = I.config(3).with_(batch=2200)
+    params = I.generate(I.config(3).with_(batch=1), steps=1)
+    B, Hv, d, C, zd = cfg.batch, cfg.num_v_heads, cfg.head_v_dim, cfg.channels, cfg.z_dim
+    print("case decode B=%d state %.2f GiB" % (B, B * Hv * d * d * 4 / 2 ** 30), flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2200)
+    state = torch.empty((B, Hv, d, d), dtype=torch.float32, device="cuda").normal_(0.0, 0.02, generator=g)
+    rnd = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda").normal_(generator=g).to(torch.bfloat16)
+    conv_state, qkv, z, a, b = rnd(B, cfg.conv_kernel - 1, C), rnd(B, C), rnd(B, zd), rnd(B, Hv), rnd(B, Hv)
+    out = torch.full((B, zd), float("nan"), dtype=torch.float32, device="cuda")
+    idx = np.array([0, 1, 1023, 1024, 2047, 2048, 2199])
+    sel = torch.as_tensor(idx, device="cuda")
+    h = lambda t: GC.host_f64(t[sel])
+    st, cs = h(state), h(conv_state)
+    q_h, z_h, a_h, b_h = h(qkv), h(z), h(a), h(b)
+    gdn.gdn_decode_layer(GC.shape_for(cfg), conv_state, state, qkv, GC.dev(params["conv_w"], "bf16"), a, b, z,
+                         GC.dev(params["A_log"], "f32"), GC.dev(params["dt_bias"], "f32"),
+                         GC.dev(params["norm_w"], "f32"), out)
+    torch.cuda.synchronize()
+    r_out = O.decode_step(O.shape_of(cfg, batch=len(idx)), cs, st, q_h, I.widen(params["conv_w"], "bf16"), a_h, b_h,
+                          z_h, params["A_log"], params["dt_bias"], params["norm_w"])
+    GC.compare("B2200 out", h(out), r_out, "bf16")
+    GC.compare("B2200 state", h(state), st, "bf16")
+    np.testing.assert_array_equal(GC.host_bits(conv_state[sel]), GC.conv_state_bits_expected(cs, "bf16"))
+    assert not torch.isnan(out).any().item()
