@@ -26,6 +26,9 @@
 // error on the outputs, too coarse for the fp32 recurrence. Operands must stay below
 // the fp16 range (6.5e4); the normalised q, k, the state and delta of this layer are
 // orders of magnitude smaller.
+// The running sums g_t are kept in fp64: in a strongly decaying head g reaches -1e3
+// and beyond within a chunk, where an fp32 sum would carry ~1e-4 absolute error into
+// every exp(g_t - g_s); each difference is formed in fp64 and only then rounded.
 // The (I + A) solve is an fp32 forward substitution on VALU, two lanes per column.
 // With bf16 activations, the next chunk's conv inputs, z rows and gate inputs are
 // loaded while it runs and stored to LDS after it.
@@ -94,7 +97,7 @@ struct alignas(16) ChunkSmem {
     } s;
   } u;
   float v[kC][kXLd];        // silu(conv) of v
-  alignas(16) float g[2][kC];  // running sum of log(alpha) inside the chunk, by chunk parity
+  alignas(16) double g[2][kC];  // running sum of log(alpha) inside the chunk (fp64), by chunk parity
   alignas(16) float beta[2][kC];
   alignas(16) float ss[kC][4];  // per-wave partial sums of o^2
   Staging<BF> st;
@@ -108,7 +111,7 @@ template <bool BF>
 __device__ __forceinline__ void chunk_gate_inputs(const KernelArgs& a, int b, int h, int ch, int lane, float& dt,
                                                   float& br);
 __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float br, float A_exp, float dt_bias,
-                                            float* g_out, float* beta_out);
+                                            double* g_out, float* beta_out);
 
 // Prefetch of chunk `ch` (bf16 activations) by the four waves, wave `wv` (wave-uniform)
 // taking tokens 8 wv .. 8 wv + 7: conv inputs and z rows, and (wave 0) the gates. The
@@ -231,6 +234,23 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
+// the same move for an fp64 value, one DPP per half (a lane shifted in from outside
+// the row reads +0.0 in both halves)
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+  const u32x2 w = __builtin_bit_cast(u32x2, v);
+  u32x2 r;
+  r[0] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(w[0]), CTRL, 0xf, 0xf, true));
+  r[1] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(w[1]), CTRL, 0xf, 0xf, true));
+  return __builtin_bit_cast(double, r);
+}
+__device__ __forceinline__ double readlane64(double v, int lane) {
+  const u32x2 w = __builtin_bit_cast(u32x2, v);
+  u32x2 r;
+  r[0] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(w[0]), lane));
+  r[1] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(w[1]), lane));
+  return __builtin_bit_cast(double, r);
+}
 // v_permlane32_swap: lanes 32-63 of a trade places with lanes 0-31 of b (afterwards a
 // holds a[0..31], b[0..31] and b holds a[32..63], b[32..63]). v_permlane16_swap: the
 // odd rows of 16 lanes of a trade places with the even rows of b. Written as inline
@@ -262,7 +282,7 @@ __device__ __forceinline__ void chunk_gate_inputs(const KernelArgs& a, int b, in
 }
 
 __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float br, float A_exp, float dt_bias,
-                                            float* g_out, float* beta_out) {
+                                            double* g_out, float* beta_out) {
   float la = 0.0f, bt = 0.0f;
   if (lane < min(kC, left)) {
     // softplus(x) = max(x, 0) + log(1 + exp(-|x|)); the log's argument lies in (1, 2]
@@ -270,16 +290,17 @@ __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float 
     la = -A_exp * (fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))));
     bt = __builtin_amdgcn_rcpf(1.0f + __expf(-br));
   }
-  // inclusive scan over lanes 0..31: within each row of 16 lanes by DPP row shifts
-  // (lanes shifted in from outside the row read 0), then row 1 adds row 0's total
-  la += dpp<0x111>(la);  // row_shr:1
-  la += dpp<0x112>(la);  // row_shr:2
-  la += dpp<0x114>(la);  // row_shr:4
-  la += dpp<0x118>(la);  // row_shr:8
-  const float row0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), 15));
-  if (lane >= 16) la += row0;
+  // inclusive scan in fp64 over lanes 0..31: within each row of 16 lanes by DPP row
+  // shifts (lanes shifted in from outside the row read 0), then row 1 adds row 0's total
+  double g = la;
+  g += dpp64<0x111>(g);  // row_shr:1
+  g += dpp64<0x112>(g);  // row_shr:2
+  g += dpp64<0x114>(g);  // row_shr:4
+  g += dpp64<0x118>(g);  // row_shr:8
+  const double row0 = readlane64(g, 15);
+  if (lane >= 16) g += row0;
   if (lane < kC) {
-    g_out[lane] = la;
+    g_out[lane] = g;
     beta_out[lane] = bt;
   }
 }
@@ -640,14 +661,14 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     float ea[4], eb[4];
     {
       const int t4 = 16 * hw + 4 * q, s = 16 * (w & 1) + c16;
-      const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
+      const double* gt = &sm.g[par][t4];
       const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
-      const float gs = sm.g[par][s];
+      const double gs = sm.g[par][s];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = t4 + r;
         // exp(g_t - g_s) <= 1 for s <= t; the other entries are masked (argument clamped)
-        const float e = (s <= t) ? __expf(fminf(gt[r] - gs, 0.0f)) : 0.0f;
+        const float e = (s <= t) ? __expf(fminf(static_cast<float>(gt[r] - gs), 0.0f)) : 0.0f;
         ea[r] = (s < t) ? -(bt[r] * e * (kDown * kDown)) : 0.0f;
         eb[r] = e * kDown;
       }
@@ -656,11 +677,11 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
     for (int lt = 0; lt < 2; ++lt) {
       const int t4 = 16 * (lt ^ hw) + 4 * q;
-      const f32x4 gt = *reinterpret_cast<const f32x4*>(&sm.g[par][t4]);
+      const double* gt = &sm.g[par][t4];
       const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float gam = __expf(gt[r]), c1 = bt[r] * kLn2;
+        const float gam = __expf(static_cast<float>(gt[r])), c1 = bt[r] * kLn2;
         c3[lt][r] = -c1 * (gam * (kDown * kLog2e));
         c4[lt][r] = gam * kDown;
 #pragma unroll
@@ -822,10 +843,10 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         kth[it] = frag(&sm.kt_hi[0][0], kKTLd, 16 * it + c16, 0, q);
         ktl[it] = frag(&sm.kt_lo[0][0], kKTLd, 16 * it + c16, 0, q);
       }
-      const float gC = sm.g[par][kC - 1];
-      const float gamC = __expf(gC);
-      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.g[par][4 * q]);
-      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.g[par][16 + 4 * q]);
+      const double gC = sm.g[par][kC - 1];
+      const float gamC = __expf(static_cast<float>(gC));
+      const double* g0 = &sm.g[par][4 * q];
+      const double* g1 = &sm.g[par][16 + 4 * q];
       u32x4 dh[2], dl[2], eh[2], el[2];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
@@ -835,8 +856,8 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         for (int r = 0; r < 4; ++r) {
           top[r] = sm.u.s.x[4 * q + r][j];
           bot[r] = sm.u.s.x[16 + 4 * q + r][j];
-          top2[r] = __expf(gC - g0[r]) * top[r];
-          bot2[r] = __expf(gC - g1[r]) * bot[r];
+          top2[r] = __expf(static_cast<float>(gC - g0[r])) * top[r];
+          bot2[r] = __expf(static_cast<float>(gC - g1[r])) * bot[r];
         }
         bfrag(top, bot, dh[jt], dl[jt], one);
         bfrag(top2, bot2, eh[jt], el[jt], one);
