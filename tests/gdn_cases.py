@@ -135,3 +135,23 @@ def compare(name, got, ref, act, tol=None):
     assert max_abs <= atol, "%s: max abs diff %.3e > %.1e" % (name, max_abs, atol)
     assert max_rel <= rtol, "%s: max rel diff %.3e > %.1e" % (name, max_rel, rtol)
     return max_abs, max_rel
+
+
+def extreme_inputs(data, seq_major, rng):
+    """Gate inputs at the ends of their range: b = -30 / 0 / 30 gives beta ~ 1e-13, 1/2
+    and 1; dt = -30 / -8 / 0 / 8 / 30 with A_log up to ln 16 gives log alpha from
+    ~-1e-12 (alpha = 1 in fp32) to -480 (alpha = 0 in fp32), so the running log-gate sum
+    of a 32-token chunk reaches ~-15000. z takes -20 / -2 / 0.5 / 3, and sequence 0 has
+    a zero conv state and all-zero activations at every token: its conv outputs are 0, the
+    L2 and RMS norms divide 0 by their epsilon root, its recurrent state only decays, and
+    its outputs are exactly 0."""
+    bf = lambda x: I.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+    data["a"] = bf(rng.choice([-30.0, -8.0, 0.0, 8.0, 30.0], size=data["a"].shape))
+    data["b"] = bf(rng.choice([-30.0, 0.0, 30.0], size=data["b"].shape))
+    data["z"] = bf(rng.choice([-20.0, -2.0, 0.5, 3.0], size=data["z"].shape))
+    data["conv_state"][0] = 0
+    if seq_major:
+        data["qkv"][0] = 0
+    else:
+        data["qkv"][:, 0] = 0
+    return data

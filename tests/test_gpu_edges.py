@@ -414,30 +414,10 @@ def test_decode_state_beyond_4GiB():
     assert not torch.isnan(out).any().item()
 
 
-def _extreme_inputs(data, seq_major, rng):
-    """Gate inputs at the ends of their range: b = -30 / 0 / 30 gives beta ~ 1e-13, 1/2
-    and 1; dt = -30 / -8 / 0 / 8 / 30 with A_log up to ln 16 gives log alpha from
-    ~-1e-12 (alpha = 1 in fp32) to -480 (alpha = 0 in fp32), so the running log-gate sum
-    of a 32-token chunk reaches ~-15000. z takes -20 / -2 / 0.5 / 3, and sequence 0 has
-    a zero conv state and all-zero activations at every token: its conv outputs are 0, the
-    L2 and RMS norms divide 0 by their epsilon root, its recurrent state only decays, and
-    its outputs are exactly 0."""
-    bf = lambda x: I.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
-    data["a"] = bf(rng.choice([-30.0, -8.0, 0.0, 8.0, 30.0], size=data["a"].shape))
-    data["b"] = bf(rng.choice([-30.0, 0.0, 30.0], size=data["b"].shape))
-    data["z"] = bf(rng.choice([-20.0, -2.0, 0.5, 3.0], size=data["z"].shape))
-    data["conv_state"][0] = 0
-    if seq_major:
-        data["qkv"][0] = 0
-    else:
-        data["qkv"][:, 0] = 0
-    return data
-
-
 def test_decode_extreme_gates_and_zero_inputs():
     cfg = cfg_of("extreme_decode", 3, 2, 4, 128, 4, "bf16", steps=6)
     print("case decode extreme gates B=3", flush=True)
-    data = _extreme_inputs(I.generate(cfg, steps=cfg.steps), False, np.random.default_rng(7))
+    data = GC.extreme_inputs(I.generate(cfg, steps=cfg.steps), False, np.random.default_rng(7))
     d = GC.DeviceInputs(cfg, data)
     outs = GC.gpu_decode(cfg, d, cfg.steps)
     r_out, r_st, r_cs = GC.oracle_decode(cfg, data, cfg.steps)
@@ -453,7 +433,7 @@ def test_decode_extreme_gates_and_zero_inputs():
 def test_sequence_extreme_gates_and_zero_inputs(T):
     cfg = cfg_of("extreme_seq", 3, 2, 4, 128, 4, "bf16", steps=T, mode="sequence")
     print("case sequence extreme gates B=3 T=%d" % T, flush=True)
-    data = _extreme_inputs(I.generate(cfg), True, np.random.default_rng(T))
+    data = GC.extreme_inputs(I.generate(cfg), True, np.random.default_rng(T))
     dv = GC.DeviceInputs(cfg, data)
     out = torch.full((cfg.batch, T, cfg.z_dim), float("nan"), dtype=torch.float32, device="cuda")
     gdn.gdn_sequence(GC.shape_for(cfg), T, dv.conv_state, dv.state, dv.qkv, dv.conv_w, dv.a, dv.b, dv.z,

@@ -21,7 +21,7 @@ from gated_deltanet_linear_causal_amd import gdn
 from gated_deltanet_linear_causal_amd import inputs as I
 from oracle import oracle as O
 
-from gdn_cases import TOL, compare, conv_state_bits_expected, dev, host_bits, host_f64, shape_for
+from gdn_cases import TOL, compare, conv_state_bits_expected, dev, extreme_inputs, host_bits, host_f64, shape_for
 
 pytestmark = pytest.mark.gpu
 
@@ -54,9 +54,11 @@ CASES = [
 
 
 class Case:
-    def __init__(self, name, B, Hk, Hv, d, K, act, T):
+    def __init__(self, name, B, Hk, Hv, d, K, act, T, extreme=False):
         self.cfg = cfg_of(name, B, Hk, Hv, d, K, act, T)
         self.data = I.generate(self.cfg)
+        if extreme:
+            extreme_inputs(self.data, True, np.random.default_rng(T))
         ad = act
         dd = self.data
         self.conv_w = dev(dd["conv_w"], ad)
@@ -107,8 +109,19 @@ def oracle_prefix(cfg, data, b, n):
 def test_verify_then_commit(case):
     name, B, Hk, Hv, d, K, act, T, accepted = case
     print("case", name, flush=True)
-    c = Case(name, B, Hk, Hv, d, K, act, T)
+    _verify_then_commit(Case(name, B, Hk, Hv, d, K, act, T), accepted)
+
+
+def test_verify_then_commit_extreme_gates():
+    """Gates at the ends of their range and a sequence of all-zero activations (the
+    inputs of the decode and sequence edge tests), over 8 draft tokens."""
+    print("case extreme_B3_T8", flush=True)
+    _verify_then_commit(Case("extreme_B3_T8", 3, 2, 4, 128, 4, "bf16", 8, extreme=True), [8, 3, 0])
+
+
+def _verify_then_commit(c, accepted):
     cfg, data = c.cfg, c.data
+    name, act, d, T = cfg.name, cfg.act_dtype, cfg.head_v_dim, cfg.steps
     tol = tol_of(act, d)
     state0, conv0 = host_bits(c.state).copy(), host_bits(c.conv_state).copy()
 
