@@ -144,14 +144,19 @@ def extreme_inputs(data, seq_major, rng):
     of a 32-token chunk reaches ~-15000. z takes -20 / -2 / 0.5 / 3, and sequence 0 has
     a zero conv state and all-zero activations at every token: its conv outputs are 0, the
     L2 and RMS norms divide 0 by their epsilon root, its recurrent state only decays, and
-    its outputs are exactly 0."""
+    its outputs are exactly 0. Sequence 1 has activations 64 times larger than drawn."""
     bf = lambda x: I.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
     data["a"] = bf(rng.choice([-30.0, -8.0, 0.0, 8.0, 30.0], size=data["a"].shape))
     data["b"] = bf(rng.choice([-30.0, 0.0, 30.0], size=data["b"].shape))
     data["z"] = bf(rng.choice([-20.0, -2.0, 0.5, 3.0], size=data["z"].shape))
     data["conv_state"][0] = 0
+    # sequence 1: activations 64 times larger (exact in bf16), so v, delta and the
+    # state grow by that factor while q and k are normalised
+    big = lambda x: I.f32_to_bf16_bits(I.bf16_bits_to_f32(x) * np.float32(64.0))
     if seq_major:
         data["qkv"][0] = 0
+        data["qkv"][1] = big(data["qkv"][1])
     else:
         data["qkv"][:, 0] = 0
+        data["qkv"][:, 1] = big(data["qkv"][:, 1])
     return data
