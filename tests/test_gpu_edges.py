@@ -259,6 +259,7 @@ def test_pooled_decode(name, Hk, Hv, d, K, act):
 CHUNKED = [
     # name, B, Hk, Hv, d, K, act, T   (d = 128, K = 4 and T >= 32 take the chunked MFMA form)
     ("G2_T32_one_chunk", 2, 2, 4, 128, 4, "bf16", 32),
+    ("G2_T33_tail_of_one", 2, 2, 4, 128, 4, "bf16", 33),
     ("G2_T70_ragged", 3, 2, 4, 128, 4, "bf16", 70),
     ("G1_T45", 2, 3, 3, 128, 4, "bf16", 45),
     ("G4_T64", 2, 2, 8, 128, 4, "bf16", 64),
