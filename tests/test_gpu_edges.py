@@ -447,3 +447,44 @@ def test_sequence_extreme_gates_and_zero_inputs(T):
     GC.compare("extreme seq T%d out" % T, got, r_out, "bf16")
     GC.compare("extreme seq T%d state" % T, GC.host_f64(dv.state), r_st, "bf16")
     np.testing.assert_array_equal(GC.host_bits(dv.conv_state), GC.conv_state_bits_expected(r_cs, "bf16"))
+
+
+def test_chunked_verify_and_projections_are_deterministic():
+    """Two runs of the chunked sequence (T = 70), of verify (T = 8) and of both
+    projections (B = 512, the 256 x 128 and 64 x 64 rings) from the same inputs agree
+    bit for bit: no kernel on these paths accumulates in a run-dependent order."""
+    cfg = cfg_of("det_chunk", 3, 2, 4, 128, 4, "bf16", steps=70, mode="sequence")
+    data = I.generate(cfg)
+    runs = []
+    for _ in range(2):
+        dv = GC.DeviceInputs(cfg, data)
+        s = GC.shape_for(cfg)
+        out = torch.full((cfg.batch, cfg.steps, cfg.z_dim), float("nan"), dtype=torch.float32, device="cuda")
+        gdn.gdn_sequence(s, cfg.steps, dv.conv_state, dv.state, dv.qkv, dv.conv_w, dv.a, dv.b, dv.z, dv.A_log,
+                         dv.dt_bias, dv.norm_w, out)
+        dv2 = GC.DeviceInputs(cfg, data)
+        T = 8
+        vout = torch.full((cfg.batch, T, cfg.z_dim), float("nan"), dtype=torch.float32, device="cuda")
+        trail = torch.zeros(gdn.gdn_verify_trail_bytes(s, T), dtype=torch.uint8, device="cuda")
+        gdn.gdn_decode_verify(s, T, dv2.conv_state, dv2.state, dv2.qkv[:, :T].contiguous(), dv2.conv_w,
+                              dv2.a[:, :T].contiguous(), dv2.b[:, :T].contiguous(), dv2.z[:, :T].contiguous(),
+                              dv2.A_log, dv2.dt_bias, dv2.norm_w, vout, trail)
+        torch.cuda.synchronize()
+        runs.append([out, dv.state, dv.conv_state, vout, trail])
+    pc = I.config(3)
+    P = I.generate_projections(pc)
+    sp = GC.shape_for(pc)
+    C, zd, Hv = pc.channels, pc.z_dim, pc.num_v_heads
+    w = {k: GC.dev(P[k], "bf16") for k in ("x_norm", "w_qkv", "w_z", "w_a", "w_b", "w_out")}
+    g = GC.dev(I.f32_to_bf16_bits(np.random.default_rng(5).standard_normal((pc.batch, zd), dtype=np.float32)), "bf16")
+    for r in range(2):
+        outs = [torch.empty((pc.batch, n), dtype=torch.bfloat16, device="cuda") for n in (C, zd, Hv, Hv)]
+        y = torch.empty((pc.batch, I.HIDDEN), dtype=torch.float32, device="cuda")
+        gdn.gdn_in_proj(sp, I.HIDDEN, w["x_norm"], w["w_qkv"], w["w_z"], w["w_a"], w["w_b"], *outs)
+        gdn.gdn_out_proj(sp, I.HIDDEN, g, w["w_out"], y)
+        torch.cuda.synchronize()
+        runs[r] += outs + [y]
+    for x, y_ in zip(*runs):
+        if x.dtype != torch.uint8:
+            assert torch.isfinite(x.float()).all()
+        assert torch.equal(x, y_)
