@@ -72,6 +72,16 @@ CASES = [
     (600, 16, 32, 128, 2048, [0, 63, 64, 511, 512, 575, 576, 599]),
     (512, 16, 32, 128, 2048, [0, 1, 63, 64, 255, 300, 511]),
     (1024, 4, 20, 128, 2048, [0, 1, 255, 256, 511, 767, 1000, 1023]),
+    # contractions of 1, 2 and 3 stages through the 256 x 128 ring (in_proj, hidden 64 /
+    # 128 / 192) and of 1..4 stages through the 64 x 64 ring (out_proj, H_v d_v = 64 ..
+    # 256): the prologue issues fewer stages than the ring holds and every stage is a tail
+    (512, 16, 32, 128, 64, [0, 255, 256, 511]),
+    (512, 16, 32, 128, 128, [0, 300, 511]),
+    (512, 16, 32, 128, 192, [1, 256, 510]),
+    (512, 1, 1, 64, 2048, [0, 255, 256, 511]),
+    (512, 1, 2, 64, 2048, [0, 511]),
+    (512, 1, 3, 64, 2048, [0, 511]),
+    (512, 2, 4, 64, 2048, [0, 511]),
 ]
 
 
