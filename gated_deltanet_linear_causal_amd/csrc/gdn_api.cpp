@@ -4,6 +4,7 @@
 
 #include "gdn.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -22,12 +23,30 @@ namespace {
 #endif
 constexpr uint64_t kStreamStateBytes = GDN_STREAM_STATE_BYTES;
 
-// gdn_sequence switches from the token-by-token kernel to the chunked MFMA form at
-// this many tokens (one chunk).
-#ifndef GDN_CHUNKED_MIN_TOKENS
-#define GDN_CHUNKED_MIN_TOKENS 32
-#endif
-constexpr int32_t kChunkedMinTokens = GDN_CHUNKED_MIN_TOKENS;
+// Compute units of the current device, queried once per device (256 on MI355X).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// gdn_sequence takes the chunked MFMA form from this many tokens on, the token-by-token
+// kernel below it. The chunked form runs one workgroup per (sequence, v-head) and CU
+// for each chunk of 32 tokens, so its cost for T <= 32 is about one chunk per pass of
+// the B x H_v workgroups over the CUs, whatever T is. Crossing points measured on
+// MI355X (256 CUs, d = 128, K = 4, B x H_v = 128 ... 2048): T = 5 for one pass (B = 8,
+// T = 8: 20.5 against 30.3 us), 9 to 10 for two passes, 13 to 14 from four passes on.
+// Each threshold sits a token or so above its crossing point.
+int32_t chunked_min_tokens(long units) {
+  const long cus = device_cus();
+  const long passes = (units + cus - 1) / cus;
+  return passes <= 1 ? 6 : (passes <= 2 ? 10 : 14);
+}
 
 struct Buf {
   const void* p;
@@ -361,7 +380,8 @@ gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_stat
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int d = shape->head_k_dim, G = a.G;
   (void)hipGetLastError();
-  if (T >= kChunkedMinTokens && gdn::chunked_supported(d, a.K)) return launched(gdn::launch_chunked_sequence(a, s));
+  if (gdn::chunked_supported(d, a.K) && T >= chunked_min_tokens(static_cast<long>(z.B) * z.Hv))
+    return launched(gdn::launch_chunked_sequence(a, s));
   if (G <= 2 && a.K == 4) return launched(gdn::launch_sequence(d, G, a, s));
   // Shapes whose state or taps do not stay resident: one fused step launch per token.
   const size_t ea = z.ea, eo = z.eo;

@@ -145,11 +145,12 @@ gdn_status_t gdn_decode_layer_pooled(const gdn_shape_t* shape, int32_t pool_size
  * z [B][T][H_v*d_v]; out is [B][T][H_v*d_v]. Equal, up to rounding, to T calls of
  * gdn_decode_layer. `workspace` (device, may be NULL when the query returns 0) must
  * hold gdn_sequence_workspace_bytes(shape, T) bytes -> else GDN_ERR_WORKSPACE.
- * With d_k = d_v = 128, K = 4 and T >= 32 the tokens go in chunks of 32 through the
- * chunked form of the rule on the matrix cores, with every operand split into two fp16
- * halves (22 significant bits): the recurrent state and the per-token deltas must stay
- * below the fp16 range (6.5e4 in magnitude; the layer's values are orders of magnitude
- * smaller). Shorter sequences and other shapes run token by token in fp32. */
+ * With d_k = d_v = 128 and K = 4 the tokens go in chunks of 32 through the chunked form
+ * of the rule on the matrix cores once T reaches 6, 10 or 14 tokens (B x H_v fitting one,
+ * two or more passes over the device's compute units), with every operand split into
+ * two fp16 halves (22 significant bits): the recurrent state and the per-token deltas
+ * must stay below the fp16 range (6.5e4 in magnitude; the layer's values are orders of
+ * magnitude smaller). Shorter sequences and other shapes run token by token in fp32. */
 gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_state, float* state,
                           const void* qkv, const void* conv1d_weight, const void* dt_raw,
                           const void* b_raw, const void* z, const float* A_log,
