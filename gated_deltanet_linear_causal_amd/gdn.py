@@ -127,7 +127,7 @@ def _p(t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] = 
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be a GPU tensor, got %s" % (name, t.device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
@@ -135,15 +135,15 @@ def _p(t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] = 
         raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if numel is not None and t.numel() < numel:
         raise ValueError("%s has %d elements, the shape needs %d" % (name, t.numel(), numel))
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()  # an int: the c_void_p argtypes convert it
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
     if isinstance(stream, torch.cuda.Stream):
-        return ctypes.c_void_p(stream.cuda_stream)
-    return ctypes.c_void_p(int(stream))
+        return stream.cuda_stream
+    return int(stream)
 
 
 def _done(st: int, where: str, check: bool) -> int:
