@@ -490,3 +490,53 @@ def test_chunked_verify_and_projections_are_deterministic():
         if x.dtype != torch.uint8:
             assert torch.isfinite(x.float()).all()
         assert torch.equal(x, y_)
+
+
+def test_sequence_verify_commit_replayed_from_a_hip_graph():
+    """A 12-token gdn_sequence (the chunked form at this batch, plus its conv-state
+    launch), then verify of 4 draft tokens and a commit of 4 / 2 / 0 of them, captured in
+    one HIP graph and replayed three times with eager resets and synchronisations between
+    the replays: every replay reproduces the eager calls bit for bit."""
+    cfg = cfg_of("graph_seq", 3, 2, 4, 128, 4, "bf16", steps=12, mode="sequence")
+    data = I.generate(cfg)
+    d = GC.DeviceInputs(cfg, data)
+    s = GC.shape_for(cfg)
+    T, Tv = cfg.steps, 4
+    sl = lambda t: t[:, :Tv].contiguous()
+    vq, va, vb, vz = sl(d.qkv), sl(d.a), sl(d.b), sl(d.z)
+    acc = torch.tensor([4, 2, 0], dtype=torch.int32, device="cuda")
+    trail = torch.zeros(gdn.gdn_verify_trail_bytes(s, Tv), dtype=torch.uint8, device="cuda")
+    out = torch.full((cfg.batch, T, cfg.z_dim), float("nan"), dtype=torch.float32, device="cuda")
+    vout = torch.full((cfg.batch, Tv, cfg.z_dim), float("nan"), dtype=torch.float32, device="cuda")
+    st0, cs0 = d.state.clone(), d.conv_state.clone()
+
+    def calls(st=None):
+        gdn.gdn_sequence(s, T, d.conv_state, d.state, d.qkv, d.conv_w, d.a, d.b, d.z, d.A_log, d.dt_bias,
+                         d.norm_w, out, stream=st)
+        gdn.gdn_decode_verify(s, Tv, d.conv_state, d.state, vq, d.conv_w, va, vb, vz, d.A_log, d.dt_bias,
+                              d.norm_w, vout, trail, stream=st)
+        gdn.gdn_decode_commit(s, Tv, acc, d.conv_state, d.state, vq, trail, stream=st)
+
+    calls()
+    torch.cuda.synchronize()
+    r_out, _, _ = GC.oracle_sequence(cfg, data)
+    GC.compare("graph eager seq out", GC.host_f64(out), r_out, "bf16")
+    eager = [x.clone() for x in (out, vout, trail, d.state, d.conv_state)]
+    d.state.copy_(st0)
+    d.conv_state.copy_(cs0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(torch.cuda.current_stream())
+    for rep in range(3):
+        d.state.copy_(st0)
+        d.conv_state.copy_(cs0)
+        out.fill_(float("nan"))
+        vout.fill_(float("nan"))
+        trail.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, e in zip(("out", "verify out", "trail", "state", "conv state"),
+                              (out, vout, trail, d.state, d.conv_state), eager):
+            assert torch.equal(x, e), "replay %d: %s differs from the eager calls" % (rep, name)
