@@ -465,6 +465,11 @@ def main():
                                       "GB_s": round(b / ssec / 1e9, 1), "frac": round(b / ssec / 1e9 / HBM_PEAK_GBS, 4),
                                       "graph_us_per_step": round(gsec * 1e6, 2),
                                       "graph_GB_s": round(b / gsec / 1e9, 1)}
+            if c.batch == 1:
+                sweep["B1"]["note"] = "launch-latency bound; graph_us_per_step is the device time per step"
+            elif c.batch * c.num_v_heads * c.head_k_dim * c.head_v_dim * 4 <= (256 << 20):
+                sweep["B%d" % c.batch]["note"] = ("effective (cache-assisted): the state fits the 256 MB Infinity "
+                                                  "Cache, so GB_s may exceed what HBM alone delivers")
             del dd
         result["sweep"] = sweep
         torch.cuda.empty_cache()
