@@ -379,9 +379,11 @@ gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_stat
   a.out_ts = static_cast<long>(z.Hv * z.d);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int d = shape->head_k_dim, G = a.G;
+  // the path is chosen before the error state is cleared, so that the launch check
+  // below sees only the launch (the device query makes HIP calls of its own)
+  const bool chunked = gdn::chunked_supported(d, a.K) && T >= chunked_min_tokens(static_cast<long>(z.B) * z.Hv);
   (void)hipGetLastError();
-  if (gdn::chunked_supported(d, a.K) && T >= chunked_min_tokens(static_cast<long>(z.B) * z.Hv))
-    return launched(gdn::launch_chunked_sequence(a, s));
+  if (chunked) return launched(gdn::launch_chunked_sequence(a, s));
   if (G <= 2 && a.K == 4) return launched(gdn::launch_sequence(d, G, a, s));
   // Shapes whose state or taps do not stay resident: one fused step launch per token.
   const size_t ea = z.ea, eo = z.eo;
