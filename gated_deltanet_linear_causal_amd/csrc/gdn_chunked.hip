@@ -394,8 +394,9 @@ __device__ __forceinline__ void store_rows(const float (&y)[2][4][2], __amdgpu_b
       for (int jt = 0; jt < 2; ++jt) {
         const float x = y[tt][r][jt];
         if constexpr (OUT_BF16) {
+          // round to nearest even; a NaN stays a (quiet) NaN
           uint32_t u = __float_as_uint(x);
-          u += 0x7fffu + ((u >> 16) & 1u);
+          u = ((u & 0x7fffffffu) > 0x7f800000u) ? (u | 0x00400000u) : u + 0x7fffu + ((u >> 16) & 1u);
           __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(u >> 16), ors, ro + 16 * esz * jt, 0, 0);
         } else {
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), ors, ro + 16 * esz * jt, 0, 0);
@@ -523,10 +524,13 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         constexpr int kTB = 8;  // tokens loaded per batch of loads
 #pragma unroll 1
         for (int tb = 0; tb < kC; tb += kTB) {
+          // tokens past the end (last chunk) repeat the last input: finite values whose
+          // beta is 0, so their delta rows are exactly 0 and they change nothing (a zero
+          // row would give 0 * rsq(0) = NaN in the L2 norm when l2_eps is 0)
           uint32_t xv[kTB];
 #pragma unroll
           for (int e = 0; e < kTB; ++e)
-            xv[e] = (tb + e < nt) ? load_raw<BF>(a.qkv, (static_cast<long>(b) * T + t0 + tb + e) * C + gc) : 0u;
+            xv[e] = load_raw<BF>(a.qkv, (static_cast<long>(b) * T + t0 + min(tb + e, nt - 1)) * C + gc);
 #pragma unroll
           for (int e = 0; e < kTB; ++e) {
             const int t = tb + e;
@@ -535,7 +539,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
             uu = fmaf(wt[m][0][1], win[m][1], uu);
             uu = fmaf(wt[m][0][2], win[m][2], uu);
             uu = fmaf(wt[m][0][3], xf, uu);
-            const float val = (t < nt) ? silu_l2e(uu) : 0.0f;
+            const float val = silu_l2e(uu);
             if (m == 0)
               sm.u.raw[t][tid] = val;
             else

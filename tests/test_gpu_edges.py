@@ -272,7 +272,20 @@ CHUNKED = [
 
 @pytest.mark.parametrize("name,B,Hk,Hv,d,K,act,T", CHUNKED, ids=[s[0] for s in CHUNKED])
 def test_chunked_sequence(name, B, Hk, Hv, d, K, act, T):
-    cfg = cfg_of(name, B, Hk, Hv, d, K, act, steps=T, mode="sequence")
+    _chunked_case(cfg_of(name, B, Hk, Hv, d, K, act, steps=T, mode="sequence"))
+
+
+def test_chunked_f32_acts_zero_l2_eps_ragged_tail():
+    """fp32 activations with l2_eps = 0 and a ragged last chunk (T = 100: 4 tokens in
+    the last chunk of 32). The token slots past the end of the sequence must carry
+    finite values through the L2 norm (a zero row would give 0 * rsq(0) = NaN and
+    poison the chunk's valid outputs and the state through the products)."""
+    _chunked_case(cfg_of("G2_T100_f32_acts_l2eps0", 2, 2, 4, 128, 4, "f32", steps=100,
+                         mode="sequence").with_(l2_eps=0.0))
+
+
+def _chunked_case(cfg):
+    name, B, T, act, d = cfg.name, cfg.batch, cfg.steps, cfg.act_dtype, cfg.head_v_dim
     data = I.generate(cfg)
     dv = GC.DeviceInputs(cfg, data)
     s = GC.shape_for(cfg)
