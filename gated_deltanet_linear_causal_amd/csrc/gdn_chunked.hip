@@ -5,36 +5,45 @@
 // form of Gated DeltaNet). With H0 the state before the chunk, g_t the running sum of
 // log(alpha) inside the chunk and gamma_t = exp(g_t):
 //   A[t][s] = beta_t exp(g_t - g_s) (k_t . k_s)   for s < t, else 0
-//   (I + A) Delta = diag(beta) (V - diag(gamma) K H0)         (Delta rows = delta_t)
+//   R = diag(beta) (V - diag(gamma) K H0),   Delta = (I + A)^-1 R      (rows delta_t)
 //   O = diag(gamma) Q H0 + P Delta,  P[t][s] = exp(g_t - g_s) (q_t . k_s) for s <= t
 //   H_C = gamma_C H0 + K^T diag(exp(g_C - g)) Delta
 // and o_t = O_t / sqrt(d), then the per-head gated RMSNorm as in the decode step.
-// Tokens are processed in order; the result equals the token-by-token recurrence up
-// to rounding.
+// (I + A)^-1 is taken in 2 x 2 blocks of 16 tokens: T11 = (I + A11)^-1, T22 =
+// (I + A22)^-1, and Delta1 = T11 R1, Delta2 = T22 (R2 - A21 Delta1). Everything but
+// the products with H0 and Delta is independent of the state.
 //
-// Work unit: one workgroup (4 waves) per (sequence, v-head), looping over chunks.
-// The 128x128 state lives in MFMA accumulators for the whole sequence: wave w owns
-// columns 32w .. 32w+31 (8 x 2 tiles of 16x16). An accumulator tile, lane l holding
-// rows 4(l/16)+r, column l%16, is exactly the B-operand layout of the 16x16x32 f16
-// MFMA when the contraction index of each 32-block is ordered (4q..4q+3, 16+4q..
-// 16+4q+3) for lane group q: two stacked accumulator tiles feed B directly, and the
-// A operand reads the same permuted columns from LDS (two 8-byte reads).
+// Work unit: one workgroup of 8 waves per (sequence, v-head), looping over the chunks.
+// Waves 0-3 (consumers) hold the 128 x 128 state in MFMA accumulators for the whole
+// sequence and do the state-dependent products of chunk c; waves 4-7 (producers)
+// meanwhile build chunk c + 1's operands: its conv + SiLU, L2 norms and gates, and then
+// K K^T, Q K^T, the two 16 x 16 block inverses, A21 and P. Waves w and w + 4 share a
+// SIMD, so each SIMD runs one matrix-heavy and one vector-heavy wave. Two barriers per
+// chunk:
+//   phase 1  consumers: K H0, Q H0, R, Delta, O = gamma Q H0 + P Delta, row sums of O^2
+//            producers: conv / norms / gates of chunk c+1 into the other operand buffer,
+//                       z rows of chunk c; then the loads of chunk c+2
+//   phase 2  consumers: H = gamma_C H + K^T diag(exp(g_C - g)) Delta, outputs of chunk c
+//            producers: K K^T, Q K^T of chunk c+1 -> T11, T22, A21, P
+// The per-chunk buffers written in phase 1 (q, k planes, v, gates) are double-buffered;
+// those written in phase 2 (T, A21, P) are read by the consumers only in phase 1.
+// The A operand of the state update (K^T) is read from the [t][i] plane of k with the
+// LDS transpose load (ds_read_b64_tr_b16): in each group of 16 lanes, lane i receives
+// element i % 4 of the 8-byte slots addressed by lanes 4k + i / 4, k = 0..3.
+//
 // Precision: every operand is split into two fp16 halves (x = hi + lo, 22 significant
-// bits) and each product is evaluated as hi*hi + hi*lo + lo*hi with fp32 accumulation,
-// ~2^-21 relative per product; the three MFMAs of an accumulator are issued apart,
-// interleaved with independent ones. A bf16 split (8 + 8 bits) measured ~1e-4 relative
-// error on the outputs, too coarse for the fp32 recurrence. Operands must stay below
-// the fp16 range (6.5e4); the normalised q, k, the state and delta of this layer are
+// bits for normal values) and each product is evaluated as hi*hi + hi*lo + lo*hi with
+// fp32 accumulation. q and the scores P (bounded by 1) are scaled by 2^15 before the
+// split, the products by 2^-15 after; k stays unscaled because the same plane feeds
+// the state update. The 16 x 16 inverses are scaled by a power of two from their
+// largest entry (T has a unit diagonal, so it may exceed 1). The running sums g_t are
+// kept in fp64 and each difference is formed in fp64 before the exponential (in a
+// strongly decaying head g passes -1e3 within a chunk). Operands must stay below the
+// fp16 range (6.5e4); the normalised q, k, the state and delta of this layer are
 // orders of magnitude smaller.
-// The running sums g_t are kept in fp64: in a strongly decaying head g reaches -1e3
-// and beyond within a chunk, where an fp32 sum would carry ~1e-4 absolute error into
-// every exp(g_t - g_s); each difference is formed in fp64 and only then rounded.
-// The (I + A) solve is an fp32 forward substitution on VALU, two lanes per column.
-// With bf16 activations, the next chunk's conv inputs, z rows and gate inputs are
-// loaded while it runs and stored to LDS after it.
 //
-// The conv state is only read here; a separate epilogue launch writes the rolled
-// state afterwards (two workgroups of a k-head read the same Q/K conv columns).
+// The conv state is only read here; a separate launch writes the rolled state
+// afterwards (two workgroups of a k-head read the same Q/K conv columns).
 
 #include <type_traits>
 
@@ -44,198 +53,88 @@ namespace gdn {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kD = 128;   // head dim (d_k = d_v)
-constexpr int kC = 32;    // tokens per chunk
-constexpr int kNT = 256;  // 4 waves
-constexpr int kQKLd = kD + 8;  // bf16 row stride of the [t][i] planes
-constexpr int kKTLd = kC + 8;  // bf16 row stride of the [i][t] planes
-constexpr int kPLd = kC + 8;   // bf16 row stride of the [t][s] planes
-constexpr int kALd = kC + 4;   // fp32 row stride of A
-constexpr int kXLd = kD + 4;   // fp32 row stride of the [t][j] buffers
-constexpr int kRawLd = 2 * kD + 4;
-// Operands bounded by 1 in magnitude (normalised q, k and the decayed scores P) are
-// split after scaling by 2^15: fp16 keeps 11 significant bits only above 6.1e-5, so
-// unscaled the strongly decayed entries of P would carry an absolute error of ~3e-8
-// each (measured: ~1e-4 relative error on late tokens of a chunk). Products with
-// these operands go to fresh accumulators and are scaled back by 2^-15 in fp32.
+constexpr int kD = 128;       // head dim (d_k = d_v)
+constexpr int kC = 32;        // tokens per chunk
+constexpr int kNT = 512;      // 8 waves: 4 consumers, 4 producers
+constexpr int kTaps = 4;      // conv taps (K)
+constexpr int kRows = 8 + kTaps - 1;  // conv input rows of a producer wave (8 tokens + history)
+constexpr int kQKLd = kD + 8;  // halves per row of the [t][i] planes
+constexpr int kPLd = kC + 8;   // halves per row of the P planes
 constexpr float kUp = 32768.0f, kDown = 1.0f / 32768.0f;
+constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
 
-constexpr int kUnits = 3 * kD;  // conv channels of a workgroup: q, k of its k-head, v of its v-head
-constexpr int kPairs = kUnits / 2;  // bf16 channel pairs (one dword each)
-constexpr int kTaps = 4;             // conv taps (K)
+// One chunk's operands, written by the producers in phase 1 (double-buffered). v row t
+// keeps column j at j ^ vswz(t), so that the consumers' reads of rows t, t + 4, t + 8,
+// t + 12 fall in different banks without padding.
+struct Operands {
+  alignas(16) uint16_t k_hi[kC][kQKLd], k_lo[kC][kQKLd];  // unit k rows
+  alignas(16) uint16_t q_hi[kC][kQKLd], q_lo[kC][kQKLd];  // 2^15 unit q rows
+  alignas(16) float v[kC][kD];                             // log2(e) v (see silu_l2e), swizzled
+  alignas(16) double g[kC];                                // running log-gate sums
+  alignas(16) float beta[kC];
+};
+__device__ __forceinline__ int vswz(int t) { return 16 * ((t >> 2) & 3); }
 
-// Inputs of the next chunk, prefetched into LDS while the current chunk is solved
-// (bf16 activations only; with fp32 activations the inputs are read directly). Row
-// j of x holds the conv inputs of token j - 3 of the chunk: rows 0..2 are the three
-// inputs before it (the conv state for the first chunk), so every conv output of the
-// chunk can be formed from LDS alone.
+// z rows of this v-head for one chunk. bf16: 16 pieces of 16 bytes per row, piece pc of
+// row t at position pc ^ zswz(t) (the consumers' reads of rows t, t + 4, t + 8, t + 12
+// then fall in different banks); filled by DMA. fp32: padded rows, filled by stores.
+template <bool BF>
+struct ZRows {
+  alignas(16) uint32_t z[kC][kD / 2];
+};
+template <>
+struct ZRows<false> {
+  alignas(16) float z[kC][kD + 4];
+};
+__device__ __forceinline__ int zswz(int t) { return 2 * ((t >> 2) & 3); }
+
+// Conv inputs staged by DMA (bf16): per producer wave its 11 rows (8 tokens and the 3
+// before them) of the q, k and v segments, 64 dwords each (two channels per dword).
 template <bool BF>
 struct Staging {
-  alignas(16) uint32_t x[kC + kTaps - 1][kPairs + 4];  // two bf16 channels per word
-  alignas(16) uint32_t z[2][kC][kD / 2 + 4];           // z rows of this v-head, double-buffered by chunk parity
+  alignas(16) uint32_t x[4][kRows][3][kD / 2];
 };
 template <>
 struct Staging<false> {};
 
 template <bool BF>
-struct alignas(16) ChunkSmem {
-  alignas(16) uint16_t q_hi[kC][kQKLd], q_lo[kC][kQKLd];
-  alignas(16) uint16_t k_hi[kC][kQKLd], k_lo[kC][kQKLd];
-  alignas(16) uint16_t kt_hi[kD][kKTLd], kt_lo[kD][kKTLd];
-  union {
-    float raw[kC][kRawLd];  // silu(conv) of q (0..127) and k (128..255) before the L2 norm (steps 1-2)
-    struct {
-      alignas(16) float at[kC][kALd];  // -A transposed, at[s][16 (t & 1) + t / 2] = -A[t][s], zero for s >= t (steps 3-4)
-      float x[kC][kXLd];    // right-hand side, then Delta (steps 3-5)
-      uint16_t p_hi[kC][kPLd], p_lo[kC][kPLd];  // 2^15 P (steps 3-5)
-    } s;
-  } u;
-  float v[kC][kXLd];        // silu(conv) of v
-  alignas(16) double g[2][kC];  // running sum of log(alpha) inside the chunk (fp64), by chunk parity
-  alignas(16) float beta[2][kC];
-  alignas(16) float ss[kC][4];  // per-wave partial sums of o^2
-  Staging<BF> st;
+struct ChunkSmem {
+  Operands op[2];
+  alignas(16) uint16_t p_hi[kC][kPLd], p_lo[kC][kPLd];  // 2^15 P (tile (0,1) stays 0)
+  alignas(16) uint16_t t_hi[2][16][16], t_lo[2][16][16];  // scaled T11, T22
+  alignas(16) uint16_t a_hi[16][16], a_lo[16][16];        // 2^15 A21
+  alignas(16) float lsc[2][16][4][4];  // L of A11, A22 for the inverses: [s][rho][kappa] = L[rho + 4 kappa][s]
+  alignas(16) float wt[3 * kD][kTaps];  // log2(e) conv taps of the workgroup's q, k, v channels
+  alignas(16) float rsum[kC][4];        // per consumer wave: sums of O^2 over its 32 columns
+  float tscale[2];                      // 2^(E-15) of the scaled T11, T22
+  ZRows<BF> zr;
+  Staging<BF> stg;
 };
-
-// Gates of the tokens of a chunk, computed by one wave (lanes 0..31, one token each):
-// beta_t = sigmoid(b_t) and the inclusive running sum over the chunk of
-// log(alpha_t) = -exp(A_log) softplus(dt_t + dt_bias). Tokens past T get 0 and 0.
-// `left` = tokens of the sequence from the chunk's first on.
-template <bool BF>
-__device__ __forceinline__ void chunk_gate_inputs(const KernelArgs& a, int b, int h, int ch, int lane, float& dt,
-                                                  float& br);
-__device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float br, float A_exp, float dt_bias,
-                                            double* g_out, float* beta_out);
-
-// Prefetch of chunk `ch` (bf16 activations) by the four waves, wave `wv` (wave-uniform)
-// taking tokens 8 wv .. 8 wv + 7: conv inputs and z rows, and (wave 0) the gates. The
-// global loads go to registers first (stage_load) and the LDS stores follow later
-// (stage_store), so that the loads are in flight during the work in between. A row
-// segment is 64 dwords (256 bytes); one 16-byte load per lane covers four rows, lanes
-// 16 r .. 16 r + 15 taking row r, so a wave's 32 rows take 8 loads. Rows of tokens past
-// T (last chunk) repeat the last token: the conv outputs and the outputs of such tokens
-// are masked, so their values are never used.
-struct StageRegs {
-  u32x4 xv[6];   // conv inputs: segment k / 2 (q, k, v) of token 8 wv + 4 (k % 2) + lane / 16
-  u32x4 zv[2];   // z row of token 8 wv + 4 k + lane / 16
-  float dt, br;  // gate inputs of token `lane` (used by wave 0)
-};
-
-__device__ __forceinline__ int seg_offset(int sg, int g, int h, int hk) {  // dword offset of a conv segment
-  return sg == 0 ? g * (kD / 2) : (sg == 1 ? (hk + g) * (kD / 2) : (2 * hk + h) * (kD / 2));
-}
-
-// Buffer resource over `bytes` bytes from `base` (raw dwords; word 3 = 0x00020000 is the
-// raw-dword format of the gfx9 family): the base lives in SGPRs and each lane supplies a
-// 32-bit byte offset, so a load needs no 64-bit address arithmetic.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
-                                           0x00020000);
-}
-
-__device__ __forceinline__ void stage_load(const KernelArgs& a, int b, int g, int h, int ch, int lane, int wv,
-                                           StageRegs& r) {
-  const int T = a.T, t0 = ch * kC, nt = min(kC, T - t0);
-  // Row strides and segment offsets in dwords, opaque to the optimiser so that they are
-  // recomputed here (a few scalar ops) instead of being held across the chunk loop.
-  int cw = a.C / 2, zw = a.Hv * (kD / 2), hk = a.Hk;
-  asm volatile("" : "+s"(cw), "+s"(zw), "+s"(hk));
-  chunk_gate_inputs<true>(a, b, h, ch, lane, r.dt, r.br);
-  const uint32_t* xb = reinterpret_cast<const uint32_t*>(a.qkv) + (static_cast<long>(b) * T + t0) * cw;
-  const uint32_t* zb = reinterpret_cast<const uint32_t*>(a.z) + (static_cast<long>(b) * T + t0) * zw + h * (kD / 2);
-  const __amdgpu_buffer_rsrc_t xr = rows_rsrc(xb, static_cast<uint32_t>(nt * cw) * 4u);
-  const __amdgpu_buffer_rsrc_t zr = rows_rsrc(zb, static_cast<uint32_t>(nt * zw) * 4u);
-  const int col = 16 * (lane & 15);  // byte offset of the lane's 4 dwords in a segment
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int t = min(8 * wv + 4 * half + (lane >> 4), nt - 1);
-#pragma unroll
-    for (int sg = 0; sg < 3; ++sg)
-      r.xv[2 * sg + half] = __builtin_amdgcn_raw_buffer_load_b128(xr, 4 * (t * cw + seg_offset(sg, g, h, hk)) + col, 0, 0);
-    r.zv[half] = __builtin_amdgcn_raw_buffer_load_b128(zr, 4 * t * zw + col, 0, 0);
-  }
-}
-
-// With `first`, rows 0..2 of the staged conv inputs come from the conv state; otherwise
-// wave 3 first moves the previous chunk's last three rows there (it is the wave that
-// overwrites them, and a wave's LDS accesses complete in order).
-__device__ __forceinline__ void stage_store(ChunkSmem<true>& sm, const KernelArgs& a, int b, int g, int h, int ch,
-                                            int lane, int wv, bool first, float A_exp, float dt_bias,
-                                            const StageRegs& r) {
-  Staging<true>& st = sm.st;
-  constexpr int kHist = (kTaps - 1) * 3;  // history rows x segments
-  if (first) {
-    // conv state rows 0..2 ([B][K-1][C], same channel layout as a qkv row)
-    int cw = a.C / 2, hk = a.Hk;
-    asm volatile("" : "+s"(cw), "+s"(hk));
-    const uint32_t* cb = reinterpret_cast<const uint32_t*>(a.conv_state) + static_cast<long>(b) * (kTaps - 1) * cw;
-#pragma unroll
-    for (int k = 0; k < (kHist + 3) / 4; ++k) {
-      const int rr = wv + 4 * k;
-      if (rr < kHist) {
-        const int j = rr / 3, sg = rr - 3 * j;
-        st.x[j][sg * (kD / 2) + lane] = cb[j * cw + seg_offset(sg, g, h, hk) + lane];
-      }
-    }
-  } else if (wv == 3) {
-    uint32_t hist[kHist];
-#pragma unroll
-    for (int rr = 0; rr < kHist; ++rr) hist[rr] = st.x[kC + rr / 3][(rr % 3) * (kD / 2) + lane];
-#pragma unroll
-    for (int rr = 0; rr < kHist; ++rr) st.x[rr / 3][(rr % 3) * (kD / 2) + lane] = hist[rr];
-  }
-  if (wv == 0) chunk_gates(a.T - ch * kC, lane, r.dt, r.br, A_exp, dt_bias, sm.g[ch & 1], sm.beta[ch & 1]);
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int t = 8 * wv + 4 * half + (lane >> 4);
-#pragma unroll
-    for (int sg = 0; sg < 3; ++sg)
-      *reinterpret_cast<u32x4*>(&st.x[kTaps - 1 + t][sg * (kD / 2) + 4 * (lane & 15)]) = r.xv[2 * sg + half];
-    *reinterpret_cast<u32x4*>(&st.z[ch & 1][t][4 * (lane & 15)]) = r.zv[half];
-  }
-}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t u) { return __uint_as_float(u << 16); }
 
-template <bool BF>
-__device__ __forceinline__ uint32_t load_raw(const void* p, long i) {
-  if constexpr (BF)
-    return static_cast<const uint16_t*>(p)[i];
-  else
-    return static_cast<const uint32_t*>(p)[i];
-}
-template <bool BF>
-__device__ __forceinline__ float raw_f32(uint32_t v) {
-  if constexpr (BF)
-    return bf16_to_f32(v);
-  else
-    return __uint_as_float(v);
-}
-
 // silu with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an IEEE divide
 __device__ __forceinline__ float silu(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
-// log2(e) silu(u) from u2 = log2(e) u: u2 / (1 + 2^-u2). The conv weights are scaled by
+// log2(e) silu(u) from u2 = log2(e) u: u2 / (1 + 2^-u2). The conv taps are scaled by
 // log2(e) once, so the exponent needs no multiply; the factor log2(e) then cancels in
 // the L2 norms of q and k (whose epsilon is scaled by log2(e)^2) and is taken out of v
-// where v enters the right-hand side of the solve.
+// where v enters R.
 __device__ __forceinline__ float silu_l2e(float u2) {
   return u2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u2));
 }
-constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
 
-// Cross-lane adds inside a row of 16 lanes via DPP (no LDS traffic).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
-// the same move for an fp64 value, one DPP per half (a lane shifted in from outside
-// the row reads +0.0 in both halves)
 template <int CTRL>
 __device__ __forceinline__ double dpp64(double v) {
   const u32x2 w = __builtin_bit_cast(u32x2, v);
@@ -251,12 +150,10 @@ __device__ __forceinline__ double readlane64(double v, int lane) {
   r[1] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(w[1]), lane));
   return __builtin_bit_cast(double, r);
 }
-// v_permlane32_swap: lanes 32-63 of a trade places with lanes 0-31 of b (afterwards a
-// holds a[0..31], b[0..31] and b holds a[32..63], b[32..63]). v_permlane16_swap: the
-// odd rows of 16 lanes of a trade places with the even rows of b. Written as inline
-// asm with both registers read and written: the compiler's builtins for these return
-// one register for both results. Two wait states before the swap cover a VALU write
-// of either operand just before it.
+// v_permlane32_swap: lanes 32-63 of a trade places with lanes 0-31 of b. v_permlane16_swap:
+// the odd rows of 16 lanes of a trade places with the even rows of b. Inline asm with
+// both registers read and written (the builtins return one register for both results);
+// two wait states cover a VALU write of either operand just before the swap.
 __device__ __forceinline__ void swap_halves(float& a, float& b) {
   asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
@@ -271,16 +168,216 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0x140>(v);  // row_mirror
   return v;
 }
-template <bool BF>
-__device__ __forceinline__ void chunk_gate_inputs(const KernelArgs& a, int b, int h, int ch, int lane, float& dt,
-                                                  float& br) {
-  // lanes past the end read the last token (the gates mask them)
-  const int t0 = ch * kC;
-  const long ai = (static_cast<long>(b) * a.T + t0 + min(lane, min(kC, a.T - t0) - 1)) * a.Hv + h;
-  dt = raw_f32<BF>(load_raw<BF>(a.dt_raw, ai));
-  br = raw_f32<BF>(load_raw<BF>(a.b_raw, ai));
+// maximum over the 64 lanes (every lane gets it)
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  float a = v, b = v;
+  swap_rows(a, b);  // a: rows (0, 0, 2, 2), b: rows (1, 1, 3, 3)
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  swap_halves(a, b);  // a: lanes 0-31 twice, b: lanes 32-63 twice
+  return fmaxf(a, b);
 }
 
+// x = hi + lo in fp16, both rounded to nearest: hi = fp16(x), lo = fp16(x - hi)
+// (x - hi is exact in fp32). `one` is 1.0f held opaque to the optimiser: x * one - hi is
+// then a single v_fma_mix_f32 reading the fp16 hi directly.
+__device__ __forceinline__ void split1(float x, uint32_t& hi, uint32_t& lo, float one) {
+  const _Float16 hh = static_cast<_Float16>(x);
+  const _Float16 rr = static_cast<_Float16>(fmaf(x, one, -static_cast<float>(hh)));
+  hi = __builtin_bit_cast(uint16_t, hh);
+  lo = __builtin_bit_cast(uint16_t, rr);
+}
+// two fp32 -> packed fp16 pairs (hi0 | hi1 << 16), (lo0 | lo1 << 16)
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo, float one) {
+  const f32x2 x = {x0, x1};
+  const f16x2 hh = __builtin_convertvector(x, f16x2);
+  const f32x2 res = {fmaf(x0, one, -static_cast<float>(hh[0])), fmaf(x1, one, -static_cast<float>(hh[1]))};
+  hi = __builtin_bit_cast(uint32_t, hh);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(res, f16x2));
+}
+// four fp32 (an accumulator column of 4 rows) -> operand pieces of 4 halves
+__device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo, float one) {
+  uint32_t h0, h1, l0, l1;
+  split2(x[0], x[1], h0, l0, one);
+  split2(x[2], x[3], h1, l1, one);
+  hi = u32x2{h0, h1};
+  lo = u32x2{l0, l1};
+}
+// B-operand fragment of the 16x16x32 product from two stacked accumulator tiles (rows
+// 0..15 and 16..31 of a 32-row block): k-slots 0..3 of lane group q are rows 4q..4q+3
+// of the top tile, slots 4..7 rows 16+4q..16+4q+3 of the bottom one. The A operands
+// read their columns in the same order.
+__device__ __forceinline__ void bfrag(f32x4 top, f32x4 bottom, u32x4& hi, u32x4& lo, float one) {
+  u32x2 h0, l0, h1, l1;
+  split4(top, h0, l0, one);
+  split4(bottom, h1, l1, one);
+  hi = u32x4{h0[0], h0[1], h1[0], h1[1]};
+  lo = u32x4{l0[0], l0[1], l1[0], l1[1]};
+}
+
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0,
+                                               0);
+}
+// hi*hi + hi*lo + lo*hi
+__device__ __forceinline__ f32x4 mfma32x3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+  return mfma32(al, bh, mfma32(ah, bl, mfma32(ah, bh, c)));
+}
+__device__ __forceinline__ f32x4 mfma16x3(u32x2 ah, u32x2 al, u32x2 bh, u32x2 bl, f32x4 c) {
+  return mfma16(al, bh, mfma16(ah, bl, mfma16(ah, bh, c)));
+}
+
+// A-operand fragment of a row-major fp16 plane for the 16x16x32 product: row `row`,
+// 32-column block at k0, columns k0+4q..+3 and k0+16+4q..+3 for lane group q.
+__device__ __forceinline__ u32x4 frag(const uint16_t* plane, int ld, int row, int k0, int q) {
+  const uint16_t* p = plane + row * ld + k0 + 4 * q;
+  const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(p + 16);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+// A-operand fragment of the transposed [t][i] plane: rows i0 + c16 of plane^T, the 32
+// columns t in the fragment order above (t = 4q + m, then 16 + 4q + m), by two transpose
+// loads: lane (q, c16) addresses row 4q + c16/4 (then 16 + ...) at column i0 + 4 (c16 % 4).
+__device__ __forceinline__ u32x4 frag_t(const uint16_t* plane, int i0, int q, int c16) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  uint16_t* p0 = const_cast<uint16_t*>(plane) + (4 * q + (c16 >> 2)) * kQKLd + i0 + 4 * (c16 & 3);
+  uint16_t* p1 = p0 + 16 * kQKLd;
+  const i16x4 ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  const u32x2 ua = __builtin_bit_cast(u32x2, ta), ub = __builtin_bit_cast(u32x2, tb);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+// Buffer resource over `bytes` bytes from `base` (raw dwords; word 3 = 0x00020000 is the
+// raw-dword format of the gfx9 family): base in SGPRs, a 32-bit byte offset per lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// ---------------------------------------------------------------------------------
+// producer waves
+// ---------------------------------------------------------------------------------
+
+// LDS-only barrier: this wave's LDS accesses complete, then the workgroup barrier.
+// (__syncthreads would also wait for every global load in flight, the DMA included.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Row of the conv inputs at token `tok` of sequence b, in dwords: the conv state before
+// the sequence, the last token past its end (whose outputs are not stored and whose
+// beta is 0).
+__device__ __forceinline__ const uint32_t* input_row(const KernelArgs& a, int b, int tok, int cw) {
+  return tok < 0 ? static_cast<const uint32_t*>(a.conv_state) + (static_cast<long>(b) * (kTaps - 1) + (kTaps - 1 + tok)) * cw
+                 : static_cast<const uint32_t*>(a.qkv) + (static_cast<long>(b) * a.T + min(tok, a.T - 1)) * cw;
+}
+
+// bf16: DMA of producer wave p's conv inputs of chunk n (rows 8p-3 .. 8p+7 of the chunk)
+// into its staging rows: 33 row segments of 256 bytes in 9 instructions of 64 lanes x
+// 16 bytes (the last one 16 lanes).
+__device__ __forceinline__ void stage_inputs(ChunkSmem<true>& sm, const KernelArgs& a, int b, int g, int h, int n,
+                                             int p, int l) {
+  int cw = a.C / 2, hk = a.Hk;  // dwords per token row; k-head count
+  asm volatile("" : "+s"(cw), "+s"(hk));
+  uint32_t* dst = &sm.stg.x[p][0][0][0];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const int f = 64 * k + l;                                  // 16-byte piece
+    const int rs = min(f >> 4, 3 * kRows - 1), pc = f & 15;    // row segment, piece in it
+    const int e = rs / 3, sg = rs - 3 * e;
+    const int seg = (sg == 0 ? g : (sg == 1 ? hk + g : 2 * hk + h)) * (kD / 2);
+    const uint32_t* src = input_row(a, b, n * kC + 8 * p - (kTaps - 1) + e, cw) + seg + 4 * pc;
+    if (k < 8 || l < 16) __builtin_amdgcn_global_load_lds(src, dst + 256 * k, 16, 0, 0);
+  }
+}
+
+// bf16: DMA of the z rows 8p .. 8p+7 of chunk c of this v-head into the swizzled z
+// buffer (rows past the end repeat the last token): 2 instructions.
+__device__ __forceinline__ void stage_z(ChunkSmem<true>& sm, const KernelArgs& a, int b, int h, int c, int p,
+                                        int l) {
+  int zw = a.Hv * kD / 2;  // dwords per token row
+  asm volatile("" : "+s"(zw));
+  const uint32_t* zb = static_cast<const uint32_t*>(a.z) + static_cast<long>(b) * a.T * zw + h * (kD / 2);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int t = 8 * p + 4 * k + (l >> 4);  // LDS row of this lane's piece
+    const int pc = (l & 15) ^ zswz(t);       // the piece that belongs at position l & 15
+    const int tok = min(c * kC + t, a.T - 1);
+    __builtin_amdgcn_global_load_lds(zb + static_cast<long>(tok) * zw + 4 * pc, &sm.zr.z[8 * p + 4 * k][0], 16, 0, 0);
+  }
+}
+
+// fp32: a producer lane's conv inputs of one chunk (channel pair l of the q, k and v
+// segments, rows 8p-3 .. 8p+7) and z pieces, loaded where they are used.
+struct F32Inputs {
+  uint32_t x[kRows][3][2];
+  u32x4 zv[4];
+};
+__device__ __forceinline__ void load_inputs_f32(const KernelArgs& a, int b, int g, int h, int n, int p, int l,
+                                                F32Inputs& r) {
+  int cw = a.C, hk = a.Hk;
+  asm volatile("" : "+s"(cw), "+s"(hk));
+  const int seg[3] = {g * kD, (hk + g) * kD, (2 * hk + h) * kD};
+#pragma unroll
+  for (int e = 0; e < kRows; ++e) {
+    const uint32_t* row = input_row(a, b, n * kC + 8 * p - (kTaps - 1) + e, cw);
+#pragma unroll
+    for (int sg = 0; sg < 3; ++sg) {
+      const u32x2 v2 = *reinterpret_cast<const u32x2*>(row + seg[sg] + 2 * l);
+      r.x[e][sg][0] = v2[0];
+      r.x[e][sg][1] = v2[1];
+    }
+  }
+}
+__device__ __forceinline__ void copy_z_f32(ChunkSmem<false>& sm, const KernelArgs& a, int b, int h, int c, int p,
+                                           int l) {
+  int zw = a.Hv * kD;
+  asm volatile("" : "+s"(zw));
+  const float* zb = static_cast<const float*>(a.z) + static_cast<long>(b) * a.T * zw + h * kD;
+  u32x4 zv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int f = 64 * k + l, t = 8 * p + (f >> 5);
+    zv[k] = *reinterpret_cast<const u32x4*>(zb + static_cast<long>(min(c * kC + t, a.T - 1)) * zw + 4 * (f & 31));
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int f = 64 * k + l;
+    *reinterpret_cast<u32x4*>(&sm.zr.z[8 * p + (f >> 5)][4 * (f & 31)]) = zv[k];
+  }
+}
+
+// raw gate inputs of token `lane` of chunk n (lanes past the end read the last token),
+// widened only where they are used: a conversion right after a load waits for it
+template <bool BF>
+__device__ __forceinline__ void load_gate_inputs(const KernelArgs& a, int b, int h, int n, int lane, uint32_t& dt,
+                                                 uint32_t& br) {
+  const int t = min(n * kC + min(lane, kC - 1), a.T - 1);
+  const long ai = (static_cast<long>(b) * a.T + t) * a.Hv + h;
+  if constexpr (BF) {
+    dt = static_cast<const uint16_t*>(a.dt_raw)[ai];
+    br = static_cast<const uint16_t*>(a.b_raw)[ai];
+  } else {
+    dt = static_cast<const uint32_t*>(a.dt_raw)[ai];
+    br = static_cast<const uint32_t*>(a.b_raw)[ai];
+  }
+}
+template <bool BF>
+__device__ __forceinline__ float gate_input(uint32_t raw) {
+  return BF ? bf16_to_f32(raw) : __uint_as_float(raw);
+}
+
+// Gates of the chunk's tokens (lanes 0..31, one token each): beta_t = sigmoid(b_t) and
+// the inclusive running sum of log(alpha_t) = -exp(A_log) softplus(dt_t + dt_bias), in
+// fp64. Tokens past the end get beta 0 and log alpha 0.
 __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float br, float A_exp, float dt_bias,
                                             double* g_out, float* beta_out) {
   float la = 0.0f, bt = 0.0f;
@@ -290,111 +387,216 @@ __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float 
     la = -A_exp * (fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))));
     bt = __builtin_amdgcn_rcpf(1.0f + __expf(-br));
   }
-  // inclusive scan in fp64 over lanes 0..31: within each row of 16 lanes by DPP row
-  // shifts (lanes shifted in from outside the row read 0), then row 1 adds row 0's total
-  double g = la;
-  g += dpp64<0x111>(g);  // row_shr:1
-  g += dpp64<0x112>(g);  // row_shr:2
-  g += dpp64<0x114>(g);  // row_shr:4
-  g += dpp64<0x118>(g);  // row_shr:8
-  const double row0 = readlane64(g, 15);
-  if (lane >= 16) g += row0;
+  // inclusive scan over lanes 0..31: within each row of 16 lanes by DPP row shifts
+  // (lanes shifted in from outside the row read 0), then row 1 adds row 0's total
+  double gg = la;
+  gg += dpp64<0x111>(gg);  // row_shr:1
+  gg += dpp64<0x112>(gg);  // row_shr:2
+  gg += dpp64<0x114>(gg);  // row_shr:4
+  gg += dpp64<0x118>(gg);  // row_shr:8
+  const double row0 = readlane64(gg, 15);
+  if (lane >= 16) gg += row0;
   if (lane < kC) {
-    g_out[lane] = g;
+    g_out[lane] = gg;
     beta_out[lane] = bt;
   }
 }
 
-// x = hi + lo in fp16, both rounded to nearest: hi = fp16(x), lo = fp16(x - hi)
-// (x - hi is exact in fp32). 11 + 11 significant bits: |x - hi - lo| <= 2^-22 |x|
-// for normal values, and <= 2^-25 absolute in the fp16 subnormal range.
-// `one` is 1.0f held opaque to the optimiser: x * one - hi is then a single
-// v_fma_mix_f32 reading the fp16 hi directly (exact, like the subtraction it replaces)
-// instead of a conversion back to fp32 followed by a subtraction.
-__device__ __forceinline__ void split1(float x, uint32_t& hi, uint32_t& lo, float one) {
-  const _Float16 h = static_cast<_Float16>(x);
-  const _Float16 r = static_cast<_Float16>(fmaf(x, one, -static_cast<float>(h)));
-  hi = __builtin_bit_cast(uint16_t, h);
-  lo = __builtin_bit_cast(uint16_t, r);
-}
-// two fp32 -> packed fp16 pairs (hi0 | hi1 << 16), (lo0 | lo1 << 16), same rounding as
-// split1 (v_cvt_pk_f16_f32 rounds to nearest even)
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo, float one) {
-  const f32x2 x = {x0, x1};
-  const f16x2 h = __builtin_convertvector(x, f16x2);
-  const f32x2 res = {fmaf(x0, one, -static_cast<float>(h[0])), fmaf(x1, one, -static_cast<float>(h[1]))};
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(res, f16x2));
-}
-// four fp32 -> (hi pair, hi pair), (lo pair, lo pair)
-__device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo, float one) {
-  uint32_t h0, h1, l0, l1;
-  split2(x[0], x[1], h0, l0, one);
-  split2(x[2], x[3], h1, l1, one);
-  hi[0] = h0;
-  hi[1] = h1;
-  lo[0] = l0;
-  lo[1] = l1;
-}
-
-__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
-                                                0);
-}
-// A-operand fragment of a row-major bf16 plane: row `row`, 32-column block at `k0`,
-// permuted order (k0+4q .. +3, k0+16+4q .. +3) for lane group q.
-__device__ __forceinline__ u32x4 frag(const uint16_t* plane, int ld, int row, int k0, int q) {
-  const uint16_t* p = plane + row * ld + k0 + 4 * q;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
-  u32x4 r;
-  r[0] = lo[0];
-  r[1] = lo[1];
-  r[2] = hi[0];
-  r[3] = hi[1];
-  return r;
-}
-
-// B-operand fragment from two stacked accumulator-layout tiles (rows 0..15, 16..31 of
-// a 32-row block), split into hi and lo.
-__device__ __forceinline__ void bfrag(f32x4 top, f32x4 bottom, u32x4& hi, u32x4& lo, float one) {
-  u32x2 h0, l0, h1, l1;
-  split4(top, h0, l0, one);
-  split4(bottom, h1, l1, one);
-  hi[0] = h0[0];
-  hi[1] = h0[1];
-  hi[2] = h1[0];
-  hi[3] = h1[1];
-  lo[0] = l0[0];
-  lo[1] = l0[1];
-  lo[2] = l1[0];
-  lo[3] = l1[1];
-}
-
-__device__ __forceinline__ void put_split(uint16_t* hi_plane, uint16_t* lo_plane, int idx, float x, float one) {
-  uint32_t h, l;
-  split1(x, h, l, one);
-  hi_plane[idx] = static_cast<uint16_t>(h);
-  lo_plane[idx] = static_cast<uint16_t>(l);
-}
-
-// The 16 outputs of a lane (rows 16 (tt ^ hw) + 4q + r, columns 32w + 16jt + c16) as
-// buffer stores at byte offset vo (the lane's row 4q and column) plus the row offset;
-// bf16 outputs are rounded to nearest even.
-template <bool OUT_BF16>
-__device__ __forceinline__ void store_rows(const float (&y)[2][4][2], __amdgpu_buffer_rsrc_t ors, int vo, int hw,
-                                           int zr) {
-  constexpr int esz = OUT_BF16 ? 2 : 4;
+// Phase 1 of producer wave p (tokens 8p .. 8p+7) for chunk n: conv + SiLU of its q, k, v
+// channel pairs (inputs x[e][sg]: the raw words of row e, segment sg, channels 2l, 2l+1),
+// the L2 norms of q and k, and the split planes.
+template <bool BF, typename Fetch>
+__device__ __forceinline__ void produce_conv(ChunkSmem<BF>& sm, const KernelArgs& a, int n, int p, int l,
+                                             Fetch fetch, float one) {
+  Operands& op = sm.op[n & 1];
+  float y[3][8][2];  // conv outputs of channels 2l, 2l+1 of segment sg (q, k, v) for token e
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int sg = 0; sg < 3; ++sg) {
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.wt[sg * kD + 2 * l][0]);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.wt[sg * kD + 2 * l + 1][0]);
+    float x0[kRows], x1[kRows];
+#pragma unroll
+    for (int e = 0; e < kRows; ++e) fetch(e, sg, x0[e], x1[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float u0 = w0[0] * x0[e], u1 = w1[0] * x1[e];
+#pragma unroll
+      for (int j = 1; j < kTaps; ++j) {
+        u0 = fmaf(w0[j], x0[e + j], u0);
+        u1 = fmaf(w1[j], x1[e + j], u1);
+      }
+      y[sg][e][0] = silu_l2e(u0);
+      y[sg][e][1] = silu_l2e(u1);
+    }
+  }
+  // The 16 sums of squares (8 tokens x q, k) over the wave, transposed: each exchange
+  // step halves the values a lane carries while doubling the lanes each covers. After
+  // the 32-lane swaps value i (i < 8) lives in lanes 0-31 and value i + 8 in lanes 32-63;
+  // after the 16-lane swaps register j of row r holds value j + 4 r; a row sum ends it.
+  float ss[16];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ss[2 * e] = y[0][e][0] * y[0][e][0] + y[0][e][1] * y[0][e][1];
+    ss[2 * e + 1] = y[1][e][0] * y[1][e][0] + y[1][e][1] * y[1][e][1];
+  }
+  const float l2_eps = a.l2_eps * (kLog2e * kLog2e);  // q, k carry the factor log2(e)
+  float h8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float x0 = ss[i], x1 = ss[i + 8];
+    swap_halves(x0, x1);
+    h8[i] = x0 + x1;
+  }
+  float h4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float x0 = h8[j], x1 = h8[j + 4];
+    swap_rows(x0, x1);
+    h4[j] = __builtin_amdgcn_rsqf(row16_sum(x0 + x1) + l2_eps);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    ss[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, h4[i % 4]), 16 * (i / 4)));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = 8 * p + e;
+    const float rq = ss[2 * e] * kUp, rk = ss[2 * e + 1];
+    uint32_t hi, lo;
+    split2(y[0][e][0] * rq, y[0][e][1] * rq, hi, lo, one);
+    *reinterpret_cast<uint32_t*>(&op.q_hi[t][2 * l]) = hi;
+    *reinterpret_cast<uint32_t*>(&op.q_lo[t][2 * l]) = lo;
+    split2(y[1][e][0] * rk, y[1][e][1] * rk, hi, lo, one);
+    *reinterpret_cast<uint32_t*>(&op.k_hi[t][2 * l]) = hi;
+    *reinterpret_cast<uint32_t*>(&op.k_lo[t][2 * l]) = lo;
+    *reinterpret_cast<f32x2*>(&op.v[t][(2 * l) ^ vswz(t)]) = f32x2{y[2][e][0], y[2][e][1]};
+  }
+}
+
+// Phase 2 of producer wave p for chunk n: one 16 x 16 tile of K K^T and / or Q K^T
+// (contraction over the 128 channels) and its epilogue:
+//   p = 0: A11 -> T11 = (I + A11)^-1, and P tile (0, 0)
+//   p = 1: A22 -> T22, and P tile (1, 1)
+//   p = 2: A21 (times 2^15, split)
+//   p = 3: P tile (1, 0)
+// Lane (q, c16) holds rows t = 16 tt + 4q + r and column s = 16 ss + c16 of its tile.
+template <bool BF>
+__device__ __forceinline__ void produce_factors(ChunkSmem<BF>& sm, int n, int p, int l, float one) {
+  const Operands& op = sm.op[n & 1];
+  const int q = l >> 4, c16 = l & 15;
+  const int tt = p == 0 ? 0 : 1, ss = p == 1 ? 1 : 0;
+  const bool do_kk = p <= 2, do_qk = p != 2;
+  f32x4 kk = {0.0f, 0.0f, 0.0f, 0.0f}, qk = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const u32x4 bh = frag(&op.k_hi[0][0], kQKLd, 16 * ss + c16, 32 * kb, q);
+    const u32x4 bl = frag(&op.k_lo[0][0], kQKLd, 16 * ss + c16, 32 * kb, q);
+    if (do_kk) {
+      const u32x4 ah = frag(&op.k_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+      const u32x4 al = frag(&op.k_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+      kk = mfma32x3(ah, al, bh, bl, kk);
+    }
+    if (do_qk) {
+      const u32x4 ah = frag(&op.q_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+      const u32x4 al = frag(&op.q_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
+      qk = mfma32x3(ah, al, bh, bl, qk);
+    }
+  }
+  const int s = 16 * ss + c16;
+  const double gs = op.g[s];
+  float dec[4], bt[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 16 * tt + 4 * q + r;
+    // exp(g_t - g_s) <= 1 for s <= t; the other entries are masked (argument clamped)
+    dec[r] = (s <= t) ? __expf(fminf(static_cast<float>(op.g[t] - gs), 0.0f)) : 0.0f;
+    bt[r] = op.beta[t];
+  }
+  if (do_qk) {  // 2^15 P (q carries 2^15)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int ro = vo + (16 * (tt ^ hw) + r) * zr * esz;
+      const int t = 16 * tt + 4 * q + r;
+      uint32_t hi, lo;
+      split1(dec[r] * qk[r], hi, lo, one);
+      sm.p_hi[t][s] = static_cast<uint16_t>(hi);
+      sm.p_lo[t][s] = static_cast<uint16_t>(lo);
+    }
+  }
+  if (p == 2) {  // 2^15 A21
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t hi, lo;
+      split1(bt[r] * dec[r] * kk[r] * kUp, hi, lo, one);
+      sm.a_hi[4 * q + r][c16] = static_cast<uint16_t>(hi);
+      sm.a_lo[4 * q + r][c16] = static_cast<uint16_t>(lo);
+    }
+  }
+  if (p <= 1) {
+    // L = A_pp (strictly lower): lsc[p][s][rho][kappa] = L[rho + 4 kappa][s]; this lane
+    // holds rows t' = 4q + r (rho = r, kappa = q) of column c16
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.lsc[p][c16][r][q] = (4 * q + r > c16) ? bt[r] * dec[r] * kk[r] : 0.0f;
+    // the substitution reads what other lanes of the wave wrote (a wave's LDS accesses
+    // complete in order; the fences keep the compiler from moving them)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // X = (I + L)^-1 by substitution: column j = l / 4 on the quad of lanes 4j .. 4j+3,
+    // lane rho holding rows rho + 4 kappa. At step st the pivot x_st (lane st % 4, slot
+    // st / 4) is final; a quad broadcast hands it to the quad and every row is updated
+    // (rows at or above st have L[.][st] = 0).
+    const int j = l >> 2, rho = l & 3;
+    float x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = (rho + 4 * k == j) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int st = 0; st < 15; ++st) {
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(&sm.lsc[p][st][rho][0]);
+      float xs;
+      switch (st & 3) {
+        case 0: xs = dpp<0x00>(x[st >> 2]); break;   // quad_perm [0,0,0,0]
+        case 1: xs = dpp<0x55>(x[st >> 2]); break;   // [1,1,1,1]
+        case 2: xs = dpp<0xAA>(x[st >> 2]); break;   // [2,2,2,2]
+        default: xs = dpp<0xFF>(x[st >> 2]); break;  // [3,3,3,3]
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = fmaf(-lv[k], xs, x[k]);
+    }
+    // scale by 2^(15 - E), E the exponent of the largest |entry| (E >= 1: unit diagonal)
+    float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    m = wave_max(m);
+    int E;
+    (void)frexpf(m, &E);
+    const float up = ldexpf(1.0f, 15 - E);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t hi, lo;
+      split1(x[k] * up, hi, lo, one);
+      sm.t_hi[p][rho + 4 * k][j] = static_cast<uint16_t>(hi);
+      sm.t_lo[p][rho + 4 * k][j] = static_cast<uint16_t>(lo);
+    }
+    if (l == 0) sm.tscale[p] = ldexpf(1.0f, E - 15);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// consumer waves
+// ---------------------------------------------------------------------------------
+
+// The 16 outputs of a lane (rows 16 lt + 4q + r, columns 32w + 16jt + c16) as buffer
+// stores at byte offset vo (the lane's row 4q and column) plus the row offset; bf16
+// outputs are rounded to nearest even (a NaN stays a quiet NaN).
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_rows(const float (&y)[2][4][2], __amdgpu_buffer_rsrc_t ors, int vo, int zr) {
+  constexpr int esz = OUT_BF16 ? 2 : 4;
+#pragma unroll
+  for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ro = vo + (16 * lt + r) * zr * esz;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
-        const float x = y[tt][r][jt];
+        const float x = y[lt][r][jt];
         if constexpr (OUT_BF16) {
-          // round to nearest even; a NaN stays a (quiet) NaN
           uint32_t u = __float_as_uint(x);
           u = ((u & 0x7fffffffu) > 0x7f800000u) ? (u | 0x00400000u) : u + 0x7fffu + ((u >> 16) & 1u);
           __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(u >> 16), ors, ro + 16 * esz * jt, 0, 0);
@@ -409,566 +611,305 @@ template <bool BF>
 __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
   __shared__ ChunkSmem<BF> sm;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, q = l >> 4, c16 = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, q = l >> 4, c16 = l & 15;
   const int b = blockIdx.x / a.Hv;
   const int h = blockIdx.x - b * a.Hv;
   const int g = h / a.G;
   const int T = a.T;
-  const long C = a.C;
+  const int nchunks = (T + kC - 1) / kC;
+  const bool consumer = w < 4;
+  const int p = w - 4;  // producer index
 
-  // ---- state: wave w holds H[16 it + 4q + r][32 w + 16 jt + c16]
+  // ---- set-up: conv taps (log2(e)-scaled fp32) of the workgroup's channels; the upper
+  // right tile of P (always 0)
+  for (int u = tid; u < 3 * kD; u += kNT) {
+    const long gc = u < kD ? static_cast<long>(g) * kD + u
+                           : (u < 2 * kD ? static_cast<long>(a.Hk + g) * kD + (u - kD)
+                                         : static_cast<long>(2 * a.Hk + h) * kD + (u - 2 * kD));
+#pragma unroll
+    for (int j = 0; j < kTaps; ++j) {
+      const float wv = BF ? bf16_to_f32(static_cast<const uint16_t*>(a.conv_w)[gc * kTaps + j])
+                          : static_cast<const float*>(a.conv_w)[gc * kTaps + j];
+      sm.wt[u][j] = kLog2e * wv;
+    }
+  }
+  for (int u = tid; u < 16 * 16; u += kNT) {
+    sm.p_hi[u >> 4][16 + (u & 15)] = 0;
+    sm.p_lo[u >> 4][16 + (u & 15)] = 0;
+  }
+
+  // consumers: wave w holds H[16 it + 4q + r][32 w + 16 jt + c16]
   float* hst = a.state + (static_cast<long>(b) * a.Hv + h) * (kD * kD);
   f32x4 hacc[8][2];
+  float nw[2] = {0.0f, 0.0f};
+  if (consumer) {
 #pragma unroll
-  for (int it = 0; it < 8; ++it)
+    for (int it = 0; it < 8; ++it)
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
+      for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hacc[it][jt][r] = hst[(16 * it + 4 * q + r) * kD + 32 * w + 16 * jt + c16];
-
+        for (int r = 0; r < 4; ++r) hacc[it][jt][r] = hst[(16 * it + 4 * q + r) * kD + 32 * w + 16 * jt + c16];
+    nw[0] = a.norm_w[32 * w + c16];
+    nw[1] = a.norm_w[32 * w + 16 + c16];
+  }
   const float A_exp = __expf(a.A_log[h]);
   const float dt_bias = a.dt_bias[h];
   const float rsd = 1.0f / sqrtf(static_cast<float>(kD));
-  const float nw[2] = {a.norm_w[32 * w + c16], a.norm_w[32 * w + 16 + c16]};  // norm weights of the output columns
 
-  // ---- conv weights of this lane's channels. Unit channel c of the workgroup:
-  // [0,128) q of k-head g, [128,256) k of k-head g, [256,384) v of v-head h.
-  // bf16: lane takes 3 work units u = tid + 256 i, each the channel pair p = u % 192
-  // (unit channels 2p, 2p+1) over the 8 tokens 8 (u / 192) .. +7 of a chunk.
-  // fp32: lane takes unit channel tid, and tid + 256 when below 384, over all tokens.
-  constexpr int kCU = BF ? 3 : 2;  // work units (bf16) or channels (fp32) of a lane
-  constexpr int kCW = BF ? 2 : 1;  // channels per unit
-  float wt[kCU][kCW][kTaps];
-  auto unit_channel = [&](int c) -> long {  // unit channel -> channel of the qkv row
-    return c < kD ? static_cast<long>(g) * kD + c
-                  : (c < 2 * kD ? static_cast<long>(a.Hk + g) * kD + (c - kD)
-                                : static_cast<long>(2 * a.Hk + h) * kD + (c - 2 * kD));
-  };
-#pragma unroll
-  for (int i = 0; i < kCU; ++i) {
-    const int c0 = BF ? 2 * ((tid + kNT * i) % kPairs) : min(tid + kNT * i, kUnits - 1);
-#pragma unroll
-    for (int e = 0; e < kCW; ++e) {
-      const long gc = unit_channel(c0 + e);
-#pragma unroll
-      for (int j = 0; j < kTaps; ++j) wt[i][e][j] = kLog2e * raw_f32<BF>(load_raw<BF>(a.conv_w, gc * kTaps + j));
-    }
-  }
-  float win[2][kTaps - 1];  // fp32: the channel's last three inputs
-  if constexpr (!BF) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const long gc = unit_channel(min(tid + kNT * m, kUnits - 1));
-#pragma unroll
-      for (int j = 0; j < kTaps - 1; ++j)
-        win[m][j] = raw_f32<BF>(load_raw<BF>(a.conv_state, (static_cast<long>(b) * (kTaps - 1) + j) * C + gc));
-    }
-  }
-
-  const int nchunks = (T + kC - 1) / kC;
+  // producers (bf16): chunk 0's conv inputs by DMA and its gate inputs
+  uint32_t gdt = 0, gbr = 0;
   if constexpr (BF) {
-    if (nchunks > 0) {
-      const int wv = __builtin_amdgcn_readfirstlane(w);
-      StageRegs sr;
-      stage_load(a, b, g, h, 0, l, wv, sr);
-      stage_store(sm, a, b, g, h, 0, l, wv, true, A_exp, dt_bias, sr);
+    if (!consumer && nchunks > 0) {
+      if (p == 0) load_gate_inputs<BF>(a, b, h, 0, l, gdt, gbr);
+      stage_inputs(sm, a, b, g, h, 0, p, l);
     }
-    __syncthreads();
   }
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int t0 = ch * kC;
-    const int nt = min(kC, T - t0);
-    const int par = ch & 1;
+  __syncthreads();
+
+  f32x4 oacc[2][2];  // consumers: O of the chunk (times 2^15), from phase 1 to phase 2
+
+  for (int c = -1; c < nchunks; ++c) {
+    float one = 1.0f;
+    asm volatile("" : "+s"(one));
     // lane indices re-derived per chunk (opaque to the optimiser), so that the many
     // lane-dependent LDS addresses are recomputed instead of held across the loop
     int tid_ = tid;
     asm volatile("" : "+v"(tid_));
-    float one = 1.0f;
-    asm volatile("" : "+s"(one));
-    const int tid = tid_;
-    const int w = tid >> 6, l = tid & 63, q = l >> 4, c16 = l & 15;
-    const int hw = __builtin_amdgcn_readfirstlane(w) >> 1;  // row block of the wave's K K^T / Q K^T tile
-
-    // ---- 1. conv + SiLU of this chunk's tokens (and, fp32, the gates)
-    if constexpr (BF) {
+    const int l = tid_ & 63, q = l >> 4, c16 = l & 15;
+    const int n = c + 1;  // the chunk the producers prepare
+    // ================= phase 1 =================
+    if (consumer) {
+      if (c >= 0) {
+        const Operands& op = sm.op[c & 1];
+        // K H0 and Q H0 for the wave's columns: rows t = 16 lt + 4q + r
+        f32x4 kh[2][2], qh[2][2];
 #pragma unroll
-      for (int i = 0; i < kCU; ++i) {
-        const int u = tid + kNT * i, p = u % kPairs, t8 = 8 * (u / kPairs);
-        float xl[8 + kTaps - 1], xh[8 + kTaps - 1];  // inputs of channels 2p, 2p+1
+        for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
-        for (int j = 0; j < 8 + kTaps - 1; ++j) {
-          const uint32_t wv = sm.st.x[t8 + j][p];
-          xl[j] = bf16_to_f32(wv & 0xffffu);
-          xh[j] = __uint_as_float(wv & 0xffff0000u);
-        }
-        float* dst = p < kD ? &sm.u.raw[0][2 * p] : &sm.v[0][2 * p - 2 * kD];
-        const int ld = p < kD ? kRawLd : kXLd;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float u0 = wt[i][0][0] * xl[e], u1 = wt[i][1][0] * xh[e];
-#pragma unroll
-          for (int j = 1; j < kTaps; ++j) {
-            u0 = fmaf(wt[i][0][j], xl[e + j], u0);
-            u1 = fmaf(wt[i][1][j], xh[e + j], u1);
+          for (int jt = 0; jt < 2; ++jt) {
+            kh[lt][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            qh[lt][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
           }
-          // tokens past the end (last chunk) repeat the last input row: finite values
-          // whose beta is 0, so their delta rows are exactly 0 and they change nothing
-          *reinterpret_cast<f32x2*>(dst + (t8 + e) * ld) = f32x2{silu_l2e(u0), silu_l2e(u1)};
-        }
-      }
-    } else {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (m == 1 && tid >= kUnits - kNT) break;
-        const long gc = unit_channel(tid + kNT * m);
-        constexpr int kTB = 8;  // tokens loaded per batch of loads
-#pragma unroll 1
-        for (int tb = 0; tb < kC; tb += kTB) {
-          // tokens past the end (last chunk) repeat the last input: finite values whose
-          // beta is 0, so their delta rows are exactly 0 and they change nothing (a zero
-          // row would give 0 * rsq(0) = NaN in the L2 norm when l2_eps is 0)
-          uint32_t xv[kTB];
+        for (int kb = 0; kb < 4; ++kb) {
+          u32x4 bh[2], bl[2];
 #pragma unroll
-          for (int e = 0; e < kTB; ++e)
-            xv[e] = load_raw<BF>(a.qkv, (static_cast<long>(b) * T + t0 + min(tb + e, nt - 1)) * C + gc);
+          for (int jt = 0; jt < 2; ++jt) bfrag(hacc[2 * kb][jt], hacc[2 * kb + 1][jt], bh[jt], bl[jt], one);
 #pragma unroll
-          for (int e = 0; e < kTB; ++e) {
-            const int t = tb + e;
-            const float xf = raw_f32<BF>(xv[e]);
-            float uu = wt[m][0][0] * win[m][0];
-            uu = fmaf(wt[m][0][1], win[m][1], uu);
-            uu = fmaf(wt[m][0][2], win[m][2], uu);
-            uu = fmaf(wt[m][0][3], xf, uu);
-            const float val = silu_l2e(uu);
-            if (m == 0)
-              sm.u.raw[t][tid] = val;
-            else
-              sm.v[t][tid] = val;
-            if (t < nt) {
-              win[m][0] = win[m][1];
-              win[m][1] = win[m][2];
-              win[m][2] = xf;
+          for (int lt = 0; lt < 2; ++lt) {
+            const u32x4 kah = frag(&op.k_hi[0][0], kQKLd, 16 * lt + c16, 32 * kb, q);
+            const u32x4 kal = frag(&op.k_lo[0][0], kQKLd, 16 * lt + c16, 32 * kb, q);
+            const u32x4 qah = frag(&op.q_hi[0][0], kQKLd, 16 * lt + c16, 32 * kb, q);
+            const u32x4 qal = frag(&op.q_lo[0][0], kQKLd, 16 * lt + c16, 32 * kb, q);
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+              kh[lt][jt] = mfma32x3(kah, kal, bh[jt], bl[jt], kh[lt][jt]);
+              qh[lt][jt] = mfma32x3(qah, qal, bh[jt], bl[jt], qh[lt][jt]);
             }
           }
         }
-      }
-      if (w == 0) {
-        float dt = 0.0f, br = 0.0f;
-        chunk_gate_inputs<BF>(a, b, h, ch, l, dt, br);
-        chunk_gates(T - t0, l, dt, br, A_exp, dt_bias, sm.g[par], sm.beta[par]);
-      }
-    }
-    __syncthreads();
-
-    // The next chunk's inputs (bf16 activations) are loaded here and stored to LDS after
-    // the solve: phases 2 and 3 cover the loads' latency.
-    const int wv = __builtin_amdgcn_readfirstlane(w);
-    [[maybe_unused]] StageRegs sr;
-    const int chn = min(ch + 1, nchunks - 1);
-    if constexpr (BF) stage_load(a, b, g, h, chn, l, wv, sr);
-
-    // ---- 2. L2 norms of q and k; split planes [t][i] and [i][t]. Wave w takes tokens
-    // 8w .. 8w+7, lane l channels 2l and 2l+1; the 16 reductions run side by side.
-    {
-      constexpr int kTW = kC / 4;
-      const int tb = w * kTW;
-      const float l2_eps = a.l2_eps * (kLog2e * kLog2e);  // q, k carry the factor log2(e)
-      float2 qv[kTW], kv[kTW];
-      float ss[2 * kTW];
+        // R = beta (v - gamma K H0) (v is stored as log2(e) v); O starts as gamma Q H0
+        f32x4 R[2][2];
 #pragma unroll
-      for (int tt = 0; tt < kTW; ++tt) {
-        qv[tt] = *reinterpret_cast<const float2*>(&sm.u.raw[tb + tt][2 * l]);
-        kv[tt] = *reinterpret_cast<const float2*>(&sm.u.raw[tb + tt][kD + 2 * l]);
-      }
+        for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
-      for (int tt = 0; tt < kTW; ++tt) {
-        ss[2 * tt] = qv[tt].x * qv[tt].x + qv[tt].y * qv[tt].y;
-        ss[2 * tt + 1] = kv[tt].x * kv[tt].x + kv[tt].y * kv[tt].y;
-      }
-      // The 16 sums over the wave, transposed: each exchange step halves the values a
-      // lane carries while doubling the lanes each covers. After the 32-lane swaps value
-      // i (i < 8) lives in lanes 0-31 and value i + 8 in lanes 32-63, each summed over
-      // lanes l and l ^ 32; after the 16-lane swaps register j of row r holds value
-      // j + 4 r summed over l, l ^ 16, l ^ 32, l ^ 48; a row sum completes it.
-      float h8[kTW];
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * lt + 4 * q + r;
+            const float gam = __expf(static_cast<float>(op.g[t]));
+            const float bt = op.beta[t];
 #pragma unroll
-      for (int i = 0; i < kTW; ++i) {
-        float x0 = ss[i], x1 = ss[i + kTW];
-        swap_halves(x0, x1);
-        h8[i] = x0 + x1;
-      }
-      float h4[kTW / 2];
+            for (int jt = 0; jt < 2; ++jt) {
+              const float v = op.v[t][(32 * w + 16 * jt + c16) ^ vswz(t)];
+              R[lt][jt][r] = fmaf(-bt * gam, kh[lt][jt][r], bt * kLn2 * v);
+              oacc[lt][jt][r] = gam * qh[lt][jt][r];
+            }
+          }
+        // Delta1 = T11 R1; Delta2 = T22 (R2 - A21 Delta1)
+        f32x4 delta[2][2];
+        {
+          const float ts1 = sm.tscale[0], ts2 = sm.tscale[1];
+          const u32x2 t1h = *reinterpret_cast<const u32x2*>(&sm.t_hi[0][c16][4 * q]);
+          const u32x2 t1l = *reinterpret_cast<const u32x2*>(&sm.t_lo[0][c16][4 * q]);
+          const u32x2 t2h = *reinterpret_cast<const u32x2*>(&sm.t_hi[1][c16][4 * q]);
+          const u32x2 t2l = *reinterpret_cast<const u32x2*>(&sm.t_lo[1][c16][4 * q]);
+          const u32x2 a1h = *reinterpret_cast<const u32x2*>(&sm.a_hi[c16][4 * q]);
+          const u32x2 a1l = *reinterpret_cast<const u32x2*>(&sm.a_lo[c16][4 * q]);
+          const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < kTW / 2; ++j) {
-        float x0 = h8[j], x1 = h8[j + kTW / 2];
-        swap_rows(x0, x1);
-        h4[j] = __builtin_amdgcn_rsqf(row16_sum(x0 + x1) + l2_eps);
-      }
+          for (int jt = 0; jt < 2; ++jt) {
+            u32x2 rh, rl;
+            split4(R[0][jt], rh, rl, one);
+            delta[0][jt] = mfma16x3(t1h, t1l, rh, rl, zero) * ts1;
+            split4(delta[0][jt], rh, rl, one);
+            const f32x4 ad = mfma16x3(a1h, a1l, rh, rl, zero);
+            f32x4 y2;
 #pragma unroll
-      for (int i = 0; i < 2 * kTW; ++i)
-        ss[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, h4[i % 4]), 16 * (i / 4)));
-      float kn[2][kTW];  // normalised k of channels 2l, 2l+1
-#pragma unroll
-      for (int tt = 0; tt < kTW; ++tt) {
-        const int t = tb + tt;
-        const float rq = ss[2 * tt], rk = ss[2 * tt + 1];
-        uint32_t h, lo;
-        split2(qv[tt].x * rq * kUp, qv[tt].y * rq * kUp, h, lo, one);
-        *reinterpret_cast<uint32_t*>(&sm.q_hi[t][2 * l]) = h;
-        *reinterpret_cast<uint32_t*>(&sm.q_lo[t][2 * l]) = lo;
-        kn[0][tt] = kv[tt].x * rk;
-        kn[1][tt] = kv[tt].y * rk;
-        split2(kn[0][tt] * kUp, kn[1][tt] * kUp, h, lo, one);
-        *reinterpret_cast<uint32_t*>(&sm.k_hi[t][2 * l]) = h;
-        *reinterpret_cast<uint32_t*>(&sm.k_lo[t][2 * l]) = lo;
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        u32x4 hv, lv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t h, lo;
-          split2(kn[c][2 * e], kn[c][2 * e + 1], h, lo, one);
-          hv[e] = h;
-          lv[e] = lo;
+            for (int r = 0; r < 4; ++r) y2[r] = fmaf(-kDown, ad[r], R[1][jt][r]);
+            split4(y2, rh, rl, one);
+            delta[1][jt] = mfma16x3(t2h, t2l, rh, rl, zero) * ts2;
+          }
         }
-        *reinterpret_cast<u32x4*>(&sm.kt_hi[2 * l + c][tb]) = hv;
-        *reinterpret_cast<u32x4*>(&sm.kt_lo[2 * l + c][tb]) = lv;
-      }
-    }
-    __syncthreads();
-
-    // ---- 3. K K^T and Q K^T (32 x 32), K H0 and Q H0 (this wave's columns) on MFMA, in
-    // one pass over the K and Q fragments. Wave w computes tile (w/2, w%2) of K K^T and
-    // Q K^T (tile (0, 1) lies above the diagonal: all its entries are masked). The wave
-    // holds its fragments with its own row block first, slot lt holding row block
-    // lt ^ hw (hw = w / 2), so the A operand of its K K^T / Q K^T tile is always slot 0;
-    // the accumulators of K H0, Q H0 and O follow the same slots.
-    f32x4 kh[2][2], qh[2][2];
+        // O += P Delta (both terms carry 2^15: P and q)
+        {
+          u32x4 dh[2], dl[2];
 #pragma unroll
-    for (int lt = 0; lt < 2; ++lt)
+          for (int jt = 0; jt < 2; ++jt) bfrag(delta[0][jt], delta[1][jt], dh[jt], dl[jt], one);
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        kh[lt][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        qh[lt][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
-    // two accumulators each for K K^T and Q K^T (even and odd blocks), so that the three
-    // MFMAs of one are issued apart
-    f32x4 kk2[2] = {}, qk2[2] = {};
-    // Factors of the epilogues, formed before the products so that their LDS reads and
-    // exponentials overlap the MFMAs. Tile (w/2, w%2), rows t = 16 hw + 4q + r, column
-    // s = 16 (w % 2) + c16: ea = -beta_t exp(g_t - g_s) 2^-30 for s < t, else 0 (A from
-    // 2^30 k_t.k_s), eb = exp(g_t - g_s) 2^-15 for s <= t, else 0 (2^15 P from 2^30 q_t.k_s).
-    // Rows of slot lt (t = 16 (lt ^ hw) + 4q + r), column j: rhs = c1v + c3 (2^15 K H0) with
-    // c1v = beta_t ln2 v_t[j] (v is stored as log2(e) v), c3 = -beta_t ln2 gamma_t 2^-15
-    // log2(e); O starts as c4 (2^15 Q H0), c4 = gamma_t 2^-15.
-    float ea[4], eb[4];
-    {
-      const int t4 = 16 * hw + 4 * q, s = 16 * (w & 1) + c16;
-      const double* gt = &sm.g[par][t4];
-      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
-      const double gs = sm.g[par][s];
+          for (int lt = 0; lt < 2; ++lt) {
+            const u32x4 ph = frag(&sm.p_hi[0][0], kPLd, 16 * lt + c16, 0, q);
+            const u32x4 pl = frag(&sm.p_lo[0][0], kPLd, 16 * lt + c16, 0, q);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t4 + r;
-        // exp(g_t - g_s) <= 1 for s <= t; the other entries are masked (argument clamped)
-        const float e = (s <= t) ? __expf(fminf(static_cast<float>(gt[r] - gs), 0.0f)) : 0.0f;
-        ea[r] = (s < t) ? -(bt[r] * e * (kDown * kDown)) : 0.0f;
-        eb[r] = e * kDown;
-      }
-    }
-    float c1v[2][4][2], c3[2][4], c4[2][4];
+            for (int jt = 0; jt < 2; ++jt) oacc[lt][jt] = mfma32x3(ph, pl, dh[jt], dl[jt], oacc[lt][jt]);
+          }
+        }
+        // sums of O^2 over the wave's 32 columns, per row
 #pragma unroll
-    for (int lt = 0; lt < 2; ++lt) {
-      const int t4 = 16 * (lt ^ hw) + 4 * q;
-      const double* gt = &sm.g[par][t4];
-      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][t4]);
+        for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float gam = __expf(static_cast<float>(gt[r])), c1 = bt[r] * kLn2;
-        c3[lt][r] = -c1 * (gam * (kDown * kLog2e));
-        c4[lt][r] = gam * kDown;
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) c1v[lt][r][jt] = c1 * sm.v[t4 + r][32 * w + 16 * jt + c16];
-      }
-    }
-    {
-      const bool same = (w & 1) == hw;  // B operand (K rows of block w % 2) in slot 0, else slot 1
-      // Operands of block kb: K and Q fragments fq[kb & 1] (8: slot lt, plane k_hi, k_lo,
-      // q_hi, q_lo) and the split state hb*[kb & 1] (8 pairs: column tile jt, rows
-      // 32 kb + 4q + {0,1 | 2,3} and 16 + ...). Those of block kb + 1 are produced one
-      // slice at a time between the MFMAs of block kb, each slice with two MFMAs behind
-      // a scheduling barrier, so that the loads and splits issue while the matrix core
-      // works instead of before it.
-      u32x4 fq[2][2][4];
-      u32x4 hbh[2][2], hbl[2][2];
-      auto frag_slice = [&](int kb, int k, u32x4(&dst)[2][4]) {
-        const int lt = k >> 2, pl = k & 3;
-        const uint16_t* plane = pl == 0 ? &sm.k_hi[0][0] : (pl == 1 ? &sm.k_lo[0][0] : (pl == 2 ? &sm.q_hi[0][0] : &sm.q_lo[0][0]));
-        dst[lt][pl] = frag(plane, kQKLd, 16 * (lt ^ hw) + c16, 32 * kb, q);
-      };
-      auto split_slice = [&](int kb, int k, u32x4(&hh)[2], u32x4(&hl)[2]) {
-        const int jt = k >> 2, e = k & 3;
-        const f32x4 src = e < 2 ? hacc[2 * kb][jt] : hacc[2 * kb + 1][jt];
-        uint32_t h_, l_;
-        split2(src[2 * (e & 1)], src[2 * (e & 1) + 1], h_, l_, one);
-        hh[jt][e] = h_;
-        hl[jt][e] = l_;
-      };
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        frag_slice(0, k, fq[0]);
-        split_slice(0, k, hbh[0], hbl[0]);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int cb = kb & 1, nb = cb ^ 1;
-        const u32x4(&f0)[4] = fq[cb][0];
-        const u32x4 bkh = same ? fq[cb][0][0] : fq[cb][1][0];
-        const u32x4 bkl = same ? fq[cb][0][1] : fq[cb][1][1];
-        // hi*hi, hi*lo, lo*hi of all ten accumulators in turn (independent neighbours)
-#pragma unroll
-        for (int part = 0; part < 3; ++part) {
-          kk2[kb & 1] = mfma(part == 2 ? f0[1] : f0[0], part == 1 ? bkl : bkh, kk2[kb & 1]);
-          qk2[kb & 1] = mfma(part == 2 ? f0[3] : f0[2], part == 1 ? bkl : bkh, qk2[kb & 1]);
+          for (int r = 0; r < 4; ++r) {
+            float v = oacc[lt][0][r] * oacc[lt][0][r];
+            v = fmaf(oacc[lt][1][r], oacc[lt][1][r], v);
+            v = row16_sum(v);
+            if (c16 == 0) sm.rsum[16 * lt + 4 * q + r][w] = v;
+          }
+        // H = gamma_C H + K^T diag(exp(g_C - g)) Delta
+        {
+          const double gC = op.g[kC - 1];
+          const float gamC = __expf(static_cast<float>(gC));
 #pragma unroll
           for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-              const u32x4(&f)[4] = fq[cb][lt];
-              const u32x4 bb = part == 1 ? hbl[cb][jt] : hbh[cb][jt];
-              kh[lt][jt] = mfma(part == 2 ? f[1] : f[0], bb, kh[lt][jt]);
-              qh[lt][jt] = mfma(part == 2 ? f[3] : f[2], bb, qh[lt][jt]);
-              const int k = 4 * part + 2 * lt + jt;
-              if (kb + 1 < 4 && k < 8) {
-                frag_slice(kb + 1, k, fq[nb]);
-                split_slice(kb + 1, k, hbh[nb], hbl[nb]);
-              }
-              // (the last block has no fences: the epilogues below may start among its
-              // MFMAs once the products they read are final)
-              if (kb + 1 < 4) __builtin_amdgcn_sched_barrier(0);
+            for (int r = 0; r < 4; ++r) {
+              const float f = __expf(static_cast<float>(gC - op.g[16 * lt + 4 * q + r]));
+#pragma unroll
+              for (int jt = 0; jt < 2; ++jt) delta[lt][jt][r] *= f;
             }
-        }
-      }
-    }
-    // A and P of tile (w / 2, w % 2)
-    {
-      const f32x4 kk = kk2[0] + kk2[1], qk = qk2[0] + qk2[1];
-      const int t4 = 16 * hw + 4 * q, s = 16 * (w & 1) + c16;
+          u32x4 eh[2], el[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t4 + r;
-        sm.u.s.at[s][16 * (t & 1) + (t >> 1)] = ea[r] * kk[r];
-        put_split(&sm.u.s.p_hi[0][0], &sm.u.s.p_lo[0][0], t * kPLd + s, eb[r] * qk[r], one);  // = 2^15 P
-      }
-    }
-
-    // rhs[t][j] = beta_t (v_t[j] - gamma_t (K H0)[t][j]);  O starts as gamma_t (Q H0)[t][j]
-    f32x4 oacc[2][2];  // slot lt: rows of block lt ^ hw
+          for (int jt = 0; jt < 2; ++jt) bfrag(delta[0][jt], delta[1][jt], eh[jt], el[jt], one);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int t4 = 16 * (tt ^ hw) + 4 * q;
+          for (int it = 0; it < 8; ++it)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+            for (int jt = 0; jt < 2; ++jt) hacc[it][jt] *= gamC;
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          sm.u.s.x[t4 + r][32 * w + 16 * jt + c16] = fmaf(c3[tt][r], kh[tt][jt][r], c1v[tt][r][jt]);
-          oacc[tt][jt][r] = c4[tt][r] * qh[tt][jt][r];
-        }
-    }
-    __syncthreads();
-
-    // ---- 4. forward substitution (I + A) Delta = rhs in right-looking order: once
-    // delta_s is final it is eliminated from every later row, so the updates of different
-    // rows are independent. Two lanes per column j (all four waves): lane parity p holds
-    // the rows t = 2i + p; at step s the lane holding row s passes delta_s to its partner
-    // by DPP. With bf16 activations the next chunk's inputs are stored to LDS afterwards.
-    {
-      const int j = 32 * w + (l >> 1), p = l & 1;
-      float d[kC / 2];
+          for (int it = 0; it < 8; ++it) {
+            const u32x4 ah = frag_t(&op.k_hi[0][0], 16 * it, q, c16);
+            const u32x4 al = frag_t(&op.k_lo[0][0], 16 * it, q, c16);
 #pragma unroll
-      for (int i = 0; i < kC / 2; ++i) d[i] = sm.u.s.x[2 * i + p][j];
-      // rows of -A^T (this lane's parity) are read two rows ahead of their use; at step s
-      // the rows i >= lo(s) are updated (for s even and p = 0 that includes row s itself,
-      // whose coefficient is 0)
-      auto lo = [](int s_) { return (s_ & 1) ? (s_ >> 1) + 1 : (s_ >> 1); };
-      constexpr int kAhead = 2;
-      f32x4 ring[kAhead + 1][kC / 8];
-      auto fetch = [&](int s_, f32x4(&dst)[kC / 8]) {
-#pragma unroll
-        for (int i4 = lo(s_) / 4; i4 < kC / 8; ++i4) dst[i4] = *reinterpret_cast<const f32x4*>(&sm.u.s.at[s_][16 * p + 4 * i4]);
-      };
-#pragma unroll
-      for (int s = 0; s < kAhead; ++s) fetch(s, ring[s]);
-      // delta_s from the lane holding row s: quad_perm [0,0,2,2] (even lane of the pair)
-      // or [1,1,3,3] (odd lane)
-      float ds = dpp<0xA0>(d[0]);
-#pragma unroll
-      for (int s = 0; s < kC - 1; ++s) {
-        if (s + kAhead < kC - 1) fetch(s + kAhead, ring[(s + kAhead) % (kAhead + 1)]);
-        const f32x4(&m)[kC / 8] = ring[s % (kAhead + 1)];
-        // the next pivot row (s + 1, slot (s + 1) / 2, always updated at step s) first, so
-        // that its hand-off overlaps the other updates of this step
-        // (two more updates separate it from the DPP read of its result); scheduling
-        // barriers keep the next step's updates, which wait for the hand-off, behind this
-        // step's
-        const int in = (s + 1) >> 1;
-        d[in] = fmaf(m[in >> 2][in & 3], ds, d[in]);
-#pragma unroll
-        for (int i = in + 1; i < min(in + 3, kC / 2); ++i) d[i] = fmaf(m[i >> 2][i & 3], ds, d[i]);
-        float dn = 0.0f;
-        if (s + 1 < kC - 1) dn = ((s + 1) & 1) ? dpp<0xF5>(d[in]) : dpp<0xA0>(d[in]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = lo(s); i < kC / 2; ++i)
-          if (i < in || i >= in + 3) d[i] = fmaf(m[i >> 2][i & 3], ds, d[i]);
-        __builtin_amdgcn_sched_barrier(0);
-        ds = dn;
-      }
-#pragma unroll
-      for (int i = 0; i < kC / 2; ++i) sm.u.s.x[2 * i + p][j] = d[i];
-      if constexpr (BF) {
-        if (ch + 1 < nchunks) stage_store(sm, a, b, g, h, ch + 1, l, wv, false, A_exp, dt_bias, sr);
-      }
-    }
-    __syncthreads();
-
-    // ---- 5. O += P Delta;  H = gamma_C H + K^T diag(exp(g_C - g)) Delta
-    {
-      // operand fragments first: P rows of this wave's two row tiles, K^T rows of all 8
-      u32x4 ph[2], pl[2], kth[8], ktl[8];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        ph[tt] = frag(&sm.u.s.p_hi[0][0], kPLd, 16 * (tt ^ hw) + c16, 0, q);  // slot order, as oacc
-        pl[tt] = frag(&sm.u.s.p_lo[0][0], kPLd, 16 * (tt ^ hw) + c16, 0, q);
-      }
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        kth[it] = frag(&sm.kt_hi[0][0], kKTLd, 16 * it + c16, 0, q);
-        ktl[it] = frag(&sm.kt_lo[0][0], kKTLd, 16 * it + c16, 0, q);
-      }
-      const double gC = sm.g[par][kC - 1];
-      const float gamC = __expf(static_cast<float>(gC));
-      const double* g0 = &sm.g[par][4 * q];
-      const double* g1 = &sm.g[par][16 + 4 * q];
-      u32x4 dh[2], dl[2], eh[2], el[2];
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const int j = 32 * w + 16 * jt + c16;
-        f32x4 top, bot, top2, bot2;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          top[r] = sm.u.s.x[4 * q + r][j];
-          bot[r] = sm.u.s.x[16 + 4 * q + r][j];
-          top2[r] = __expf(static_cast<float>(gC - g0[r])) * top[r];
-          bot2[r] = __expf(static_cast<float>(gC - g1[r])) * bot[r];
-        }
-        bfrag(top, bot, dh[jt], dl[jt], one);
-        bfrag(top2, bot2, eh[jt], el[jt], one);
-      }
-      f32x4 pd[2][2] = {};  // 2^15 P Delta
-#pragma unroll
-      for (int part = 0; part < 3; ++part)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt)
-            pd[tt][jt] = mfma(part == 2 ? pl[tt] : ph[tt], part == 1 ? dl[jt] : dh[jt], pd[tt][jt]);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) oacc[tt][jt][r] = fmaf(pd[tt][jt][r], kDown, oacc[tt][jt][r]);
-#pragma unroll
-      for (int it = 0; it < 8; ++it)
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) hacc[it][jt][r] *= gamC;
-#pragma unroll
-      for (int part = 0; part < 3; ++part)
-#pragma unroll
-        for (int it = 0; it < 8; ++it)
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt)
-            hacc[it][jt] = mfma(part == 2 ? ktl[it] : kth[it], part == 1 ? el[jt] : eh[jt], hacc[it][jt]);
-    }
-
-    // ---- 6. gated RMSNorm of o = O / sqrt(d) and the output rows
-    {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        float s4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = 0.0f;
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) v += oacc[tt][jt][r] * oacc[tt][jt][r];
-          v = row16_sum(v);
-          s4[r] = v;
-        }
-        if (c16 == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm.ss[16 * (tt ^ hw) + 4 * q + r][w] = s4[r];
-        }
-      }
-      __syncthreads();
-      // all inputs first (row sums, z), then the 16 outputs of this lane, then the stores
-      const long zrow = static_cast<long>(a.Hv) * kD;
-      const long row0 = (static_cast<long>(b) * T + t0) * zrow + static_cast<long>(h) * kD;
-      f32x4 sv[2][4];
-      float zz[2][4][2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * (tt ^ hw) + 4 * q + r;
-          sv[tt][r] = *reinterpret_cast<const f32x4*>(&sm.ss[t][0]);
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            const int j = 32 * w + 16 * jt + c16;
-            if constexpr (BF)
-              zz[tt][r][jt] = bf16_to_f32((sm.st.z[par][t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
-            else
-              zz[tt][r][jt] = raw_f32<BF>(load_raw<BF>(a.z, row0 + min(t, nt - 1) * zrow + j));
+            for (int jt = 0; jt < 2; ++jt) hacc[it][jt] = mfma32x3(ah, al, eh[jt], el[jt], hacc[it][jt]);
           }
         }
-      float y[2][4][2];
+      }
+    } else {
+      if constexpr (BF) {
+        if (n < nchunks) {
+          // this wave's staged rows of chunk n have landed (its DMA was the last memory
+          // operation it issued before the barrier): into registers, then the staging
+          // rows take chunk n + 1
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          uint32_t xr[kRows][3];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+          for (int e = 0; e < kRows; ++e)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 v4 = sv[tt][r];
-          const float tot = (v4[0] + v4[1] + v4[2] + v4[3]) * (rsd * rsd);
-          const float rr = __builtin_amdgcn_rsqf(tot * (1.0f / kD) + a.rms_eps);
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) y[tt][r][jt] = oacc[tt][jt][r] * rsd * rr * nw[jt] * silu(zz[tt][r][jt]);
+            for (int sg = 0; sg < 3; ++sg) xr[e][sg] = sm.stg.x[p][e][sg][l];
+          const float dt = gate_input<BF>(gdt), br = gate_input<BF>(gbr);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          // memory operations in issue order: z rows of chunk c (2), gate inputs of chunk
+          // n + 1 (2, wave p = 0), conv inputs of chunk n + 1 (9)
+          if (c >= 0) stage_z(sm, a, b, h, c, p, l);
+          if (p == 0 && n + 1 < nchunks) load_gate_inputs<BF>(a, b, h, n + 1, l, gdt, gbr);
+          if (n + 1 < nchunks) stage_inputs(sm, a, b, g, h, n + 1, p, l);
+          if (p == 0) chunk_gates(T - n * kC, l, dt, br, A_exp, dt_bias, sm.op[n & 1].g, sm.op[n & 1].beta);
+          produce_conv<BF>(sm, a, n, p, l, [&](int e, int sg, float& x0, float& x1) {
+            x0 = bf16_to_f32(xr[e][sg] & 0xffffu);
+            x1 = __uint_as_float(xr[e][sg] & 0xffff0000u);
+          }, one);
+          // the z rows of chunk c must have landed before the barrier (the gate loads
+          // and the 9 staging instructions may still be in flight)
+          if (n + 1 >= nchunks)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          else if (p == 0)
+            asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        } else if (c >= 0) {
+          stage_z(sm, a, b, h, c, p, l);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-      // The chunk's nt output rows form one buffer resource: rows past the end of the
-      // sequence (last chunk) fall outside it and are not written (hardware range check).
-      // The lane's part of the byte offset (row 4q, column 32w + c16) is fixed; the row
-      // block and r are wave-uniform.
-      const int esz = a.out_bf16 ? 2 : 4;
-      const int zr = a.Hv * kD;  // elements per token row
-      const __amdgpu_buffer_rsrc_t ors = rows_rsrc(
-          static_cast<char*>(a.out) + ((static_cast<long>(b) * T + t0) * zr + static_cast<long>(h) * kD) * esz,
-          static_cast<uint32_t>(nt * zr * esz));
-      const int vo = (4 * q * zr + 32 * w + c16) * esz;
-      if (a.out_bf16)
-        store_rows<true>(y, ors, vo, hw, zr);
-      else
-        store_rows<false>(y, ors, vo, hw, zr);
+      } else {
+        if (c >= 0) copy_z_f32(sm, a, b, h, c, p, l);
+        if (n < nchunks) {
+          F32Inputs xr;
+          load_inputs_f32(a, b, g, h, n, p, l, xr);
+          if (p == 0) {
+            uint32_t dt, br;
+            load_gate_inputs<BF>(a, b, h, n, l, dt, br);
+            chunk_gates(T - n * kC, l, gate_input<BF>(dt), gate_input<BF>(br), A_exp, dt_bias, sm.op[n & 1].g,
+                        sm.op[n & 1].beta);
+          }
+          produce_conv<BF>(sm, a, n, p, l, [&](int e, int sg, float& x0, float& x1) {
+            x0 = __uint_as_float(xr.x[e][sg][0]);
+            x1 = __uint_as_float(xr.x[e][sg][1]);
+          }, one);
+        }
+      }
     }
-    __syncthreads();  // LDS is rewritten by the next chunk
+    lds_barrier();
+    // ================= phase 2 =================
+    if (consumer) {
+      if (c >= 0) {
+        // gated RMSNorm of o = O 2^-15 / sqrt(d), and the output rows
+        const int t0 = c * kC, nt = min(kC, T - t0);
+        float y[2][4][2];
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * lt + 4 * q + r;
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(&sm.rsum[t][0]);
+            const float tot = (v4[0] + v4[1] + v4[2] + v4[3]) * (kDown * kDown * rsd * rsd);
+            const float rr = __builtin_amdgcn_rsqf(tot * (1.0f / kD) + a.rms_eps) * (kDown * rsd);
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+              const int j = 32 * w + 16 * jt + c16;
+              float zz;
+              if constexpr (BF) {
+                const int pos = (j >> 3) ^ zswz(t);
+                zz = bf16_to_f32((sm.zr.z[t][4 * pos + ((j & 7) >> 1)] >> (16 * (j & 1))) & 0xffffu);
+              } else {
+                zz = sm.zr.z[t][j];
+              }
+              y[lt][r][jt] = oacc[lt][jt][r] * rr * nw[jt] * silu(zz);
+            }
+          }
+        // The chunk's nt output rows form one buffer resource: rows past the end of the
+        // sequence (last chunk) fall outside it and are not written (hardware range check).
+        const int esz = a.out_bf16 ? 2 : 4;
+        const int zr = a.Hv * kD;  // elements per token row
+        const __amdgpu_buffer_rsrc_t ors = rows_rsrc(
+            static_cast<char*>(a.out) + ((static_cast<long>(b) * T + t0) * zr + static_cast<long>(h) * kD) * esz,
+            static_cast<uint32_t>(nt * zr * esz));
+        const int vo = (4 * q * zr + 32 * w + c16) * esz;
+        if (a.out_bf16)
+          store_rows<true>(y, ors, vo, zr);
+        else
+          store_rows<false>(y, ors, vo, zr);
+      }
+    } else if (n < nchunks) {
+      produce_factors<BF>(sm, n, p, l, one);
+    }
+    lds_barrier();
   }
 
+  if (consumer) {
 #pragma unroll
-  for (int it = 0; it < 8; ++it)
+    for (int it = 0; it < 8; ++it)
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
+      for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hst[(16 * it + 4 * q + r) * kD + 32 * w + 16 * jt + c16] = hacc[it][jt][r];
+        for (int r = 0; r < 4; ++r) hst[(16 * it + 4 * q + r) * kD + 32 * w + 16 * jt + c16] = hacc[it][jt][r];
+  }
 }
 
 // Final conv state after T tokens: row j of the K-1 rows is element T + j of the
@@ -977,23 +918,19 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 // before it is overwritten.
 template <bool BF>
 __global__ __launch_bounds__(256) void gdn_conv_state_tail(const KernelArgs a) {
+  using raw_t = typename std::conditional<BF, uint16_t, uint32_t>::type;
   const long C = a.C;
   const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= static_cast<long>(a.B) * C) return;
   const long b = idx / C, c = idx - b * C;
   const int Km1 = a.K - 1;
   const long T = a.T;
+  raw_t* cs = static_cast<raw_t*>(a.conv_state);
+  const raw_t* x = static_cast<const raw_t*>(a.qkv);
   for (int j = 0; j < Km1; ++j) {
     const long e = T + j;  // element of the combined sequence
-    uint32_t v;
-    if (e < Km1)
-      v = load_raw<BF>(a.conv_state, (b * Km1 + e) * C + c);
-    else
-      v = load_raw<BF>(a.qkv, (b * T + (e - Km1)) * C + c);
-    if constexpr (BF)
-      static_cast<uint16_t*>(a.conv_state)[(b * Km1 + j) * C + c] = static_cast<uint16_t>(v);
-    else
-      static_cast<uint32_t*>(a.conv_state)[(b * Km1 + j) * C + c] = v;
+    const raw_t v = e < Km1 ? cs[(b * Km1 + e) * C + c] : x[(b * T + (e - Km1)) * C + c];
+    cs[(b * Km1 + j) * C + c] = v;
   }
 }
 
