@@ -66,7 +66,8 @@ constexpr int kC = 32;        // tokens per chunk
 constexpr int kNT = 512;      // 8 waves: 4 consumers, 4 producers
 constexpr int kTaps = 4;      // conv taps (K)
 constexpr int kRows = 8 + kTaps - 1;  // conv input rows of a producer wave (8 tokens + history)
-constexpr int kQKLd = kD + 8;  // halves per row of the [t][i] planes
+constexpr int kQKLd = kD + 4;  // halves per row of the [t][i] planes (66 dwords: the 16 rows of a
+                               // fragment read start in 16 different even banks)
 constexpr int kPLd = kC + 8;   // halves per row of the P planes
 constexpr float kUp = 32768.0f, kDown = 1.0f / 32768.0f;
 constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
@@ -96,11 +97,11 @@ struct ZRows<false> {
 };
 __device__ __forceinline__ int zswz(int t) { return 2 * ((t >> 2) & 3); }
 
-// Conv inputs staged by DMA (bf16): per producer wave its 11 rows (8 tokens and the 3
-// before them) of the q, k and v segments, 64 dwords each (two channels per dword).
+// Conv inputs staged by DMA (bf16): per producer wave, the q, k and v segments of its 11
+// rows (8 tokens and the 3 before them), 64 dwords each (two channels per dword).
 template <bool BF>
 struct Staging {
-  alignas(16) uint32_t x[4][kRows][3][kD / 2];
+  alignas(16) uint32_t x[4][3][kRows][kD / 2];
 };
 template <>
 struct Staging<false> {};
@@ -213,11 +214,14 @@ __device__ __forceinline__ void split4(f32x4 x, u32x2& hi, u32x2& lo, float one)
 // of the top tile, slots 4..7 rows 16+4q..16+4q+3 of the bottom one. The A operands
 // read their columns in the same order.
 __device__ __forceinline__ void bfrag(f32x4 top, f32x4 bottom, u32x4& hi, u32x4& lo, float one) {
-  u32x2 h0, l0, h1, l1;
-  split4(top, h0, l0, one);
-  split4(bottom, h1, l1, one);
-  hi = u32x4{h0[0], h0[1], h1[0], h1[1]};
-  lo = u32x4{l0[0], l0[1], l1[0], l1[1]};
+  typedef __attribute__((ext_vector_type(8))) float f32x8;
+  const f32x8 x = {top[0], top[1], top[2], top[3], bottom[0], bottom[1], bottom[2], bottom[3]};
+  const f16x8 h = __builtin_convertvector(x, f16x8);
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = fmaf(x[i], one, -static_cast<float>(h[i]));
+  hi = __builtin_bit_cast(u32x4, h);
+  lo = __builtin_bit_cast(u32x4, __builtin_convertvector(r, f16x8));
 }
 
 __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
@@ -280,22 +284,36 @@ __device__ __forceinline__ const uint32_t* input_row(const KernelArgs& a, int b,
                  : static_cast<const uint32_t*>(a.qkv) + (static_cast<long>(b) * a.T + min(tok, a.T - 1)) * cw;
 }
 
-// bf16: DMA of producer wave p's conv inputs of chunk n (rows 8p-3 .. 8p+7 of the chunk)
-// into its staging rows: 33 row segments of 256 bytes in 9 instructions of 64 lanes x
-// 16 bytes (the last one 16 lanes).
+// bf16: producer wave p's conv inputs of chunk n (rows 8p-3 .. 8p+7 of the chunk) into
+// its staging rows. Inside the sequence by DMA: per segment 3 instructions of 64 lanes x
+// 16 bytes, each filling 4 rows (lane i: row e0 + i / 16, 16-byte piece i % 16; the last
+// one 3 rows) from a wave-uniform row base. For the wave whose rows start before the
+// sequence (conv state) or reach past its end (the last token repeated), by plain loads
+// and LDS stores, which the barrier that follows makes visible.
+// (one segment sg at a time, so that the instructions of a chunk can be spread over the
+// conv of the chunk before)
 __device__ __forceinline__ void stage_inputs(ChunkSmem<true>& sm, const KernelArgs& a, int b, int g, int h, int n,
-                                             int p, int l) {
+                                             int p, int l, int sg) {
   int cw = a.C / 2, hk = a.Hk;  // dwords per token row; k-head count
   asm volatile("" : "+s"(cw), "+s"(hk));
-  uint32_t* dst = &sm.stg.x[p][0][0][0];
+  const int tok0 = n * kC + 8 * p - (kTaps - 1);  // token of row 0
+  const int seg = (sg == 0 ? g : (sg == 1 ? hk + g : 2 * hk + h)) * (kD / 2);
+  if (tok0 >= 0 && tok0 + kRows <= a.T) {
+    const int lr = l >> 4, pc = l & 15;
+    const uint32_t* base = static_cast<const uint32_t*>(a.qkv) + (static_cast<long>(b) * a.T + tok0) * cw + seg;
 #pragma unroll
-  for (int k = 0; k < 9; ++k) {
-    const int f = 64 * k + l;                                  // 16-byte piece
-    const int rs = min(f >> 4, 3 * kRows - 1), pc = f & 15;    // row segment, piece in it
-    const int e = rs / 3, sg = rs - 3 * e;
-    const int seg = (sg == 0 ? g : (sg == 1 ? hk + g : 2 * hk + h)) * (kD / 2);
-    const uint32_t* src = input_row(a, b, n * kC + 8 * p - (kTaps - 1) + e, cw) + seg + 4 * pc;
-    if (k < 8 || l < 16) __builtin_amdgcn_global_load_lds(src, dst + 256 * k, 16, 0, 0);
+    for (int e0 = 0; e0 < kRows; e0 += 4)
+      if (e0 + 4 <= kRows || lr < kRows - e0)
+        __builtin_amdgcn_global_load_lds(base + (e0 + lr) * cw + 4 * pc, &sm.stg.x[p][sg][e0][0], 16, 0, 0);
+  } else {
+    const uint32_t* qkv = static_cast<const uint32_t*>(a.qkv) + static_cast<long>(b) * a.T * cw;
+    const uint32_t* cst = static_cast<const uint32_t*>(a.conv_state) + static_cast<long>(b) * (kTaps - 1) * cw;
+#pragma unroll
+    for (int e = 0; e < kRows; ++e) {
+      const int tok = tok0 + e;  // wave-uniform
+      const uint32_t* row = tok < 0 ? cst + (kTaps - 1 + tok) * cw : qkv + static_cast<long>(min(tok, a.T - 1)) * cw;
+      sm.stg.x[p][sg][e][l] = row[seg + l];
+    }
   }
 }
 
@@ -403,11 +421,12 @@ __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float 
 }
 
 // Phase 1 of producer wave p (tokens 8p .. 8p+7) for chunk n: conv + SiLU of its q, k, v
-// channel pairs (inputs x[e][sg]: the raw words of row e, segment sg, channels 2l, 2l+1),
-// the L2 norms of q and k, and the split planes.
-template <bool BF, typename Fetch>
+// channel pairs, the L2 norms of q and k, and the split planes. fetch(sg, x0, x1) gives
+// channels 2l, 2l+1 of the rows of segment sg; fetched(sg) runs once they are in
+// registers.
+template <bool BF, typename Fetch, typename Fetched>
 __device__ __forceinline__ void produce_conv(ChunkSmem<BF>& sm, const KernelArgs& a, int n, int p, int l,
-                                             Fetch fetch, float one) {
+                                             Fetch fetch, Fetched fetched, float one) {
   Operands& op = sm.op[n & 1];
   float y[3][8][2];  // conv outputs of channels 2l, 2l+1 of segment sg (q, k, v) for token e
 #pragma unroll
@@ -415,8 +434,8 @@ __device__ __forceinline__ void produce_conv(ChunkSmem<BF>& sm, const KernelArgs
     const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.wt[sg * kD + 2 * l][0]);
     const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.wt[sg * kD + 2 * l + 1][0]);
     float x0[kRows], x1[kRows];
-#pragma unroll
-    for (int e = 0; e < kRows; ++e) fetch(e, sg, x0[e], x1[e]);
+    fetch(sg, x0, x1);
+    fetched(sg);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float u0 = w0[0] * x0[e], u1 = w1[0] * x1[e];
@@ -472,35 +491,13 @@ __device__ __forceinline__ void produce_conv(ChunkSmem<BF>& sm, const KernelArgs
   }
 }
 
-// Phase 2 of producer wave p for chunk n: one 16 x 16 tile of K K^T and / or Q K^T
-// (contraction over the 128 channels) and its epilogue:
-//   p = 0: A11 -> T11 = (I + A11)^-1, and P tile (0, 0)
-//   p = 1: A22 -> T22, and P tile (1, 1)
-//   p = 2: A21 (times 2^15, split)
-//   p = 3: P tile (1, 0)
-// Lane (q, c16) holds rows t = 16 tt + 4q + r and column s = 16 ss + c16 of its tile.
+// Epilogue of one 16 x 16 tile (tt, ss), x = K K^T (kk) or 2^15 Q K^T: K K^T (0, 0) -> T11,
+// (1, 1) -> T22, (1, 0) -> A21; Q K^T -> P.
 template <bool BF>
-__device__ __forceinline__ void produce_factors(ChunkSmem<BF>& sm, int n, int p, int l, float one) {
-  const Operands& op = sm.op[n & 1];
+__device__ __forceinline__ void tile_epilogue(ChunkSmem<BF>& sm, const Operands& op, int l, int tt, int ss,
+                                              bool is_kk, f32x4 x, float one) {
   const int q = l >> 4, c16 = l & 15;
-  const int tt = p == 0 ? 0 : 1, ss = p == 1 ? 1 : 0;
-  const bool do_kk = p <= 2, do_qk = p != 2;
-  f32x4 kk = {0.0f, 0.0f, 0.0f, 0.0f}, qk = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const u32x4 bh = frag(&op.k_hi[0][0], kQKLd, 16 * ss + c16, 32 * kb, q);
-    const u32x4 bl = frag(&op.k_lo[0][0], kQKLd, 16 * ss + c16, 32 * kb, q);
-    if (do_kk) {
-      const u32x4 ah = frag(&op.k_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-      const u32x4 al = frag(&op.k_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-      kk = mfma32x3(ah, al, bh, bl, kk);
-    }
-    if (do_qk) {
-      const u32x4 ah = frag(&op.q_hi[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-      const u32x4 al = frag(&op.q_lo[0][0], kQKLd, 16 * tt + c16, 32 * kb, q);
-      qk = mfma32x3(ah, al, bh, bl, qk);
-    }
-  }
+  const int p = tt == 0 ? 0 : (ss == 1 ? 1 : 2);  // which K K^T block
   const int s = 16 * ss + c16;
   const double gs = op.g[s];
   float dec[4], bt[4];
@@ -511,30 +508,30 @@ __device__ __forceinline__ void produce_factors(ChunkSmem<BF>& sm, int n, int p,
     dec[r] = (s <= t) ? __expf(fminf(static_cast<float>(op.g[t] - gs), 0.0f)) : 0.0f;
     bt[r] = op.beta[t];
   }
-  if (do_qk) {  // 2^15 P (q carries 2^15)
+  if (!is_kk) {  // 2^15 P (q carries 2^15)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * tt + 4 * q + r;
       uint32_t hi, lo;
-      split1(dec[r] * qk[r], hi, lo, one);
+      split1(dec[r] * x[r], hi, lo, one);
       sm.p_hi[t][s] = static_cast<uint16_t>(hi);
       sm.p_lo[t][s] = static_cast<uint16_t>(lo);
     }
   }
-  if (p == 2) {  // 2^15 A21
+  if (is_kk && p == 2) {  // 2^15 A21
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       uint32_t hi, lo;
-      split1(bt[r] * dec[r] * kk[r] * kUp, hi, lo, one);
+      split1(bt[r] * dec[r] * x[r] * kUp, hi, lo, one);
       sm.a_hi[4 * q + r][c16] = static_cast<uint16_t>(hi);
       sm.a_lo[4 * q + r][c16] = static_cast<uint16_t>(lo);
     }
   }
-  if (p <= 1) {
+  if (is_kk && p <= 1) {
     // L = A_pp (strictly lower): lsc[p][s][rho][kappa] = L[rho + 4 kappa][s]; this lane
     // holds rows t' = 4q + r (rho = r, kappa = q) of column c16
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.lsc[p][c16][r][q] = (4 * q + r > c16) ? bt[r] * dec[r] * kk[r] : 0.0f;
+    for (int r = 0; r < 4; ++r) sm.lsc[p][c16][r][q] = (4 * q + r > c16) ? bt[r] * dec[r] * x[r] : 0.0f;
     // the substitution reads what other lanes of the wave wrote (a wave's LDS accesses
     // complete in order; the fences keep the compiler from moving them)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -545,24 +542,26 @@ __device__ __forceinline__ void produce_factors(ChunkSmem<BF>& sm, int n, int p,
     // st / 4) is final; a quad broadcast hands it to the quad and every row is updated
     // (rows at or above st have L[.][st] = 0).
     const int j = l >> 2, rho = l & 3;
-    float x[4];
+    f32x4 lv[15];  // all columns of L this lane needs, read before the dependent steps
 #pragma unroll
-    for (int k = 0; k < 4; ++k) x[k] = (rho + 4 * k == j) ? 1.0f : 0.0f;
+    for (int st = 0; st < 15; ++st) lv[st] = *reinterpret_cast<const f32x4*>(&sm.lsc[p][st][rho][0]);
+    float xv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xv[k] = (rho + 4 * k == j) ? 1.0f : 0.0f;
 #pragma unroll
     for (int st = 0; st < 15; ++st) {
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(&sm.lsc[p][st][rho][0]);
       float xs;
       switch (st & 3) {
-        case 0: xs = dpp<0x00>(x[st >> 2]); break;   // quad_perm [0,0,0,0]
-        case 1: xs = dpp<0x55>(x[st >> 2]); break;   // [1,1,1,1]
-        case 2: xs = dpp<0xAA>(x[st >> 2]); break;   // [2,2,2,2]
-        default: xs = dpp<0xFF>(x[st >> 2]); break;  // [3,3,3,3]
+        case 0: xs = dpp<0x00>(xv[st >> 2]); break;   // quad_perm [0,0,0,0]
+        case 1: xs = dpp<0x55>(xv[st >> 2]); break;   // [1,1,1,1]
+        case 2: xs = dpp<0xAA>(xv[st >> 2]); break;   // [2,2,2,2]
+        default: xs = dpp<0xFF>(xv[st >> 2]); break;  // [3,3,3,3]
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[k] = fmaf(-lv[k], xs, x[k]);
+      for (int k = 0; k < 4; ++k) xv[k] = fmaf(-lv[st][k], xs, xv[k]);
     }
     // scale by 2^(15 - E), E the exponent of the largest |entry| (E >= 1: unit diagonal)
-    float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    float m = fmaxf(fmaxf(fabsf(xv[0]), fabsf(xv[1])), fmaxf(fabsf(xv[2]), fabsf(xv[3])));
     m = wave_max(m);
     int E;
     (void)frexpf(m, &E);
@@ -570,12 +569,58 @@ __device__ __forceinline__ void produce_factors(ChunkSmem<BF>& sm, int n, int p,
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t hi, lo;
-      split1(x[k] * up, hi, lo, one);
+      split1(xv[k] * up, hi, lo, one);
       sm.t_hi[p][rho + 4 * k][j] = static_cast<uint16_t>(hi);
       sm.t_lo[p][rho + 4 * k][j] = static_cast<uint16_t>(lo);
     }
     if (l == 0) sm.tscale[p] = ldexpf(1.0f, E - 15);
   }
+}
+
+
+// 16 x 16 tiles (tt, ss0 + i), i < np, of K K^T (kk) or Q K^T of chunk n (contraction over
+// the 128 channels) and their epilogues. All fragments are read first, and each
+// 32-channel block accumulates into its own registers (no long chain of dependent
+// products).
+template <bool BF>
+__device__ __forceinline__ void produce_tiles(ChunkSmem<BF>& sm, int n, int l, int tt, int np, int ss0, bool kk,
+                                              float one) {
+  const Operands& op = sm.op[n & 1];
+  const int q = l >> 4, c16 = l & 15;
+  const uint16_t* ahp = kk ? &op.k_hi[0][0] : &op.q_hi[0][0];
+  const uint16_t* alp = kk ? &op.k_lo[0][0] : &op.q_lo[0][0];
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i >= np) break;
+    u32x4 ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      ah[kb] = frag(ahp, kQKLd, 16 * tt + c16, 32 * kb, q);
+      al[kb] = frag(alp, kQKLd, 16 * tt + c16, 32 * kb, q);
+      bh[kb] = frag(&op.k_hi[0][0], kQKLd, 16 * (ss0 + i) + c16, 32 * kb, q);
+      bl[kb] = frag(&op.k_lo[0][0], kQKLd, 16 * (ss0 + i) + c16, 32 * kb, q);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc[i][kb] = mfma32x3(ah[kb], al[kb], bh[kb], bl[kb], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i >= np) break;
+    const f32x4 x = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
+    tile_epilogue<BF>(sm, op, l, tt, ss0 + i, kk, x, one);
+  }
+}
+
+// Phase 2 of producer wave p for chunk n:
+//   p = 0: K K^T (0, 0) -> A11 -> T11 = (I + A11)^-1
+//   p = 1: K K^T (1, 1) -> A22 -> T22
+//   p = 2: K K^T (1, 0) -> A21 (times 2^15, split)
+//   p = 3: Q K^T (0, 0) -> P
+// (consumer waves 0 and 1 take Q K^T (1, 0) and (1, 1) after the outputs of chunk c).
+template <bool BF>
+__device__ __forceinline__ void produce_factors(ChunkSmem<BF>& sm, int n, int p, int l, float one) {
+  produce_tiles<BF>(sm, n, l, p == 0 || p == 3 ? 0 : 1, 1, p == 1 ? 1 : 0, p <= 2, one);
 }
 
 // ---------------------------------------------------------------------------------
@@ -662,7 +707,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
   if constexpr (BF) {
     if (!consumer && nchunks > 0) {
       if (p == 0) load_gate_inputs<BF>(a, b, h, 0, l, gdt, gbr);
-      stage_inputs(sm, a, b, g, h, 0, p, l);
+      for (int sg = 0; sg < 3; ++sg) stage_inputs(sm, a, b, g, h, 0, p, l, sg);
     }
   }
   __syncthreads();
@@ -805,26 +850,32 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
       if constexpr (BF) {
         if (n < nchunks) {
           // this wave's staged rows of chunk n have landed (its DMA was the last memory
-          // operation it issued before the barrier): into registers, then the staging
-          // rows take chunk n + 1
+          // operation it issued before the barrier)
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          uint32_t xr[kRows][3];
-#pragma unroll
-          for (int e = 0; e < kRows; ++e)
-#pragma unroll
-            for (int sg = 0; sg < 3; ++sg) xr[e][sg] = sm.stg.x[p][e][sg][l];
           const float dt = gate_input<BF>(gdt), br = gate_input<BF>(gbr);
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           // memory operations in issue order: z rows of chunk c (2), gate inputs of chunk
-          // n + 1 (2, wave p = 0), conv inputs of chunk n + 1 (9)
+          // n + 1 (2, wave p = 0), conv inputs of chunk n + 1 (3 per segment, each issued
+          // once the segment's staged rows of chunk n are in registers)
           if (c >= 0) stage_z(sm, a, b, h, c, p, l);
           if (p == 0 && n + 1 < nchunks) load_gate_inputs<BF>(a, b, h, n + 1, l, gdt, gbr);
-          if (n + 1 < nchunks) stage_inputs(sm, a, b, g, h, n + 1, p, l);
           if (p == 0) chunk_gates(T - n * kC, l, dt, br, A_exp, dt_bias, sm.op[n & 1].g, sm.op[n & 1].beta);
-          produce_conv<BF>(sm, a, n, p, l, [&](int e, int sg, float& x0, float& x1) {
-            x0 = bf16_to_f32(xr[e][sg] & 0xffffu);
-            x1 = __uint_as_float(xr[e][sg] & 0xffff0000u);
-          }, one);
+          produce_conv<BF>(
+              sm, a, n, p, l,
+              [&](int sg, float(&x0)[kRows], float(&x1)[kRows]) {
+                uint32_t xr[kRows];
+#pragma unroll
+                for (int e = 0; e < kRows; ++e) xr[e] = sm.stg.x[p][sg][e][l];
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int e = 0; e < kRows; ++e) {
+                  x0[e] = bf16_to_f32(xr[e] & 0xffffu);
+                  x1[e] = __uint_as_float(xr[e] & 0xffff0000u);
+                }
+              },
+              [&](int sg) {
+                if (n + 1 < nchunks) stage_inputs(sm, a, b, g, h, n + 1, p, l, sg);
+              },
+              one);
           // the z rows of chunk c must have landed before the barrier (the gate loads
           // and the 9 staging instructions may still be in flight)
           if (n + 1 >= nchunks)
@@ -848,16 +899,24 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
             chunk_gates(T - n * kC, l, gate_input<BF>(dt), gate_input<BF>(br), A_exp, dt_bias, sm.op[n & 1].g,
                         sm.op[n & 1].beta);
           }
-          produce_conv<BF>(sm, a, n, p, l, [&](int e, int sg, float& x0, float& x1) {
-            x0 = __uint_as_float(xr.x[e][sg][0]);
-            x1 = __uint_as_float(xr.x[e][sg][1]);
-          }, one);
+          produce_conv<BF>(
+              sm, a, n, p, l,
+              [&](int sg, float(&x0)[kRows], float(&x1)[kRows]) {
+#pragma unroll
+                for (int e = 0; e < kRows; ++e) {
+                  x0[e] = __uint_as_float(xr.x[e][sg][0]);
+                  x1[e] = __uint_as_float(xr.x[e][sg][1]);
+                }
+              },
+              [](int) {}, one);
         }
       }
     }
     lds_barrier();
     // ================= phase 2 =================
     if (consumer) {
+      // Q K^T tiles (1, 0) and (1, 1) of the next chunk -> P (waves 0 and 1)
+      if (w < 2 && n < nchunks) produce_tiles<BF>(sm, n, l, 1, 1, w, false, one);
       if (c >= 0) {
         // gated RMSNorm of o = O 2^-15 / sqrt(d), and the output rows
         const int t0 = c * kC, nt = min(kC, T - t0);
