@@ -424,13 +424,13 @@ __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float 
 // channel pairs, the L2 norms of q and k, and the split planes. fetch(sg, x0, x1) gives
 // channels 2l, 2l+1 of the rows of segment sg; fetched(sg) runs once they are in
 // registers.
-template <bool BF, typename Fetch, typename Fetched>
+template <bool BF, int NSEG, typename Fetch, typename Fetched>
 __device__ __forceinline__ void produce_conv(ChunkSmem<BF>& sm, const KernelArgs& a, int n, int p, int l,
                                              Fetch fetch, Fetched fetched, float one) {
   Operands& op = sm.op[n & 1];
   float y[3][8][2];  // conv outputs of channels 2l, 2l+1 of segment sg (q, k, v) for token e
 #pragma unroll
-  for (int sg = 0; sg < 3; ++sg) {
+  for (int sg = 0; sg < NSEG; ++sg) {
     const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.wt[sg * kD + 2 * l][0]);
     const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.wt[sg * kD + 2 * l + 1][0]);
     float x0[kRows], x1[kRows];
@@ -487,7 +487,42 @@ __device__ __forceinline__ void produce_conv(ChunkSmem<BF>& sm, const KernelArgs
     split2(y[1][e][0] * rk, y[1][e][1] * rk, hi, lo, one);
     *reinterpret_cast<uint32_t*>(&op.k_hi[t][2 * l]) = hi;
     *reinterpret_cast<uint32_t*>(&op.k_lo[t][2 * l]) = lo;
-    *reinterpret_cast<f32x2*>(&op.v[t][(2 * l) ^ vswz(t)]) = f32x2{y[2][e][0], y[2][e][1]};
+    if constexpr (NSEG == 3) *reinterpret_cast<f32x2*>(&op.v[t][(2 * l) ^ vswz(t)]) = f32x2{y[2][e][0], y[2][e][1]};
+  }
+}
+
+// bf16, consumer waves 2 and 3 in phase 2: conv + SiLU of the v channels (pair l) of
+// chunk n for tokens 16 hv .. 16 hv + 15 (hv = w - 2), from the producers' staging rows:
+// token tau of the chunk (tau >= -3) is row tau - 8 pp + 3 of producer wave
+// pp = max(tau, 0) / 8.
+__device__ __forceinline__ void conv_v(ChunkSmem<true>& sm, int n, int hv, int l) {
+  constexpr int kR = 16 + kTaps - 1;
+  Operands& op = sm.op[n & 1];
+  const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.wt[2 * kD + 2 * l][0]);
+  const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.wt[2 * kD + 2 * l + 1][0]);
+  uint32_t xr[kR];
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const int tau = 16 * hv - (kTaps - 1) + i;
+    const int pp = tau < 0 ? 0 : (tau >> 3);
+    xr[i] = sm.stg.x[pp][2][tau - 8 * pp + (kTaps - 1)][l];
+  }
+  float x0[kR], x1[kR];
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    x0[i] = bf16_to_f32(xr[i] & 0xffffu);
+    x1[i] = __uint_as_float(xr[i] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float u0 = w0[0] * x0[e], u1 = w1[0] * x1[e];
+#pragma unroll
+    for (int j = 1; j < kTaps; ++j) {
+      u0 = fmaf(w0[j], x0[e + j], u0);
+      u1 = fmaf(w1[j], x1[e + j], u1);
+    }
+    const int t = 16 * hv + e;
+    *reinterpret_cast<f32x2*>(&op.v[t][(2 * l) ^ vswz(t)]) = f32x2{silu_l2e(u0), silu_l2e(u1)};
   }
 }
 
@@ -598,8 +633,13 @@ __device__ __forceinline__ void produce_tiles(ChunkSmem<BF>& sm, int n, int l, i
     for (int kb = 0; kb < 4; ++kb) {
       ah[kb] = frag(ahp, kQKLd, 16 * tt + c16, 32 * kb, q);
       al[kb] = frag(alp, kQKLd, 16 * tt + c16, 32 * kb, q);
-      bh[kb] = frag(&op.k_hi[0][0], kQKLd, 16 * (ss0 + i) + c16, 32 * kb, q);
-      bl[kb] = frag(&op.k_lo[0][0], kQKLd, 16 * (ss0 + i) + c16, 32 * kb, q);
+      if (kk && ss0 + i == tt) {  // diagonal K K^T tile: B holds the same rows as A
+        bh[kb] = ah[kb];
+        bl[kb] = al[kb];
+      } else {
+        bh[kb] = frag(&op.k_hi[0][0], kQKLd, 16 * (ss0 + i) + c16, 32 * kb, q);
+        bl[kb] = frag(&op.k_lo[0][0], kQKLd, 16 * (ss0 + i) + c16, 32 * kb, q);
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) acc[i][kb] = mfma32x3(ah[kb], al[kb], bh[kb], bl[kb], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
@@ -707,14 +747,18 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
   if constexpr (BF) {
     if (!consumer && nchunks > 0) {
       if (p == 0) load_gate_inputs<BF>(a, b, h, 0, l, gdt, gbr);
-      for (int sg = 0; sg < 3; ++sg) stage_inputs(sm, a, b, g, h, 0, p, l, sg);
+      for (int sg = 0; sg < 2; ++sg) stage_inputs(sm, a, b, g, h, 0, p, l, sg);
     }
   }
   __syncthreads();
 
   f32x4 oacc[2][2];  // consumers: O of the chunk (times 2^15), from phase 1 to phase 2
 
-  for (int c = -1; c < nchunks; ++c) {
+  // One pass of the two phases: the producers prepare chunk c + 1, the consumers (from
+  // c = 0 on) process chunk c. The first pass (c = -1) only prepares chunk 0; it is a
+  // separate instance so that the consumers' part of the loop has no condition.
+  auto chunk_step = [&](const int c, auto first) {
+    constexpr bool kFirst = decltype(first)::value;
     float one = 1.0f;
     asm volatile("" : "+s"(one));
     // lane indices re-derived per chunk (opaque to the optimiser), so that the many
@@ -725,7 +769,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     const int n = c + 1;  // the chunk the producers prepare
     // ================= phase 1 =================
     if (consumer) {
-      if (c >= 0) {
+      if constexpr (!kFirst) {
         const Operands& op = sm.op[c & 1];
         // K H0 and Q H0 for the wave's columns: rows t = 16 lt + 4q + r
         f32x4 kh[2][2], qh[2][2];
@@ -853,13 +897,15 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
           // operation it issued before the barrier)
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           const float dt = gate_input<BF>(gdt), br = gate_input<BF>(gbr);
-          // memory operations in issue order: z rows of chunk c (2), gate inputs of chunk
-          // n + 1 (2, wave p = 0), conv inputs of chunk n + 1 (3 per segment, each issued
-          // once the segment's staged rows of chunk n are in registers)
+          // memory operations in issue order: z rows of chunk c (2), v rows of chunk n (3;
+          // consumer waves 2 and 3 convolve them in phase 2), gate inputs of chunk n + 1
+          // (2, wave p = 0), q and k rows of chunk n + 1 (3 per segment, each issued once
+          // the segment's staged rows of chunk n are in registers)
           if (c >= 0) stage_z(sm, a, b, h, c, p, l);
+          stage_inputs(sm, a, b, g, h, n, p, l, 2);
           if (p == 0 && n + 1 < nchunks) load_gate_inputs<BF>(a, b, h, n + 1, l, gdt, gbr);
           if (p == 0) chunk_gates(T - n * kC, l, dt, br, A_exp, dt_bias, sm.op[n & 1].g, sm.op[n & 1].beta);
-          produce_conv<BF>(
+          produce_conv<BF, 2>(
               sm, a, n, p, l,
               [&](int sg, float(&x0)[kRows], float(&x1)[kRows]) {
                 uint32_t xr[kRows];
@@ -876,14 +922,15 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
                 if (n + 1 < nchunks) stage_inputs(sm, a, b, g, h, n + 1, p, l, sg);
               },
               one);
-          // the z rows of chunk c must have landed before the barrier (the gate loads
-          // and the 9 staging instructions may still be in flight)
+          // the z rows of chunk c and the v rows of chunk n must have landed before the
+          // barrier (the gate loads and the 6 q / k staging instructions may still be in
+          // flight)
           if (n + 1 >= nchunks)
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           else if (p == 0)
-            asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
           else
-            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
         } else if (c >= 0) {
           stage_z(sm, a, b, h, c, p, l);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -899,7 +946,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
             chunk_gates(T - n * kC, l, gate_input<BF>(dt), gate_input<BF>(br), A_exp, dt_bias, sm.op[n & 1].g,
                         sm.op[n & 1].beta);
           }
-          produce_conv<BF>(
+          produce_conv<BF, 3>(
               sm, a, n, p, l,
               [&](int sg, float(&x0)[kRows], float(&x1)[kRows]) {
 #pragma unroll
@@ -917,7 +964,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
     if (consumer) {
       // Q K^T tiles (1, 0) and (1, 1) of the next chunk -> P (waves 0 and 1)
       if (w < 2 && n < nchunks) produce_tiles<BF>(sm, n, l, 1, 1, w, false, one);
-      if (c >= 0) {
+      if constexpr (!kFirst) {
         // gated RMSNorm of o = O 2^-15 / sqrt(d), and the output rows
         const int t0 = c * kC, nt = min(kC, T - t0);
         float y[2][4][2];
@@ -955,11 +1002,16 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         else
           store_rows<false>(y, ors, vo, zr);
       }
+      if constexpr (BF) {
+        if (w >= 2 && n < nchunks) conv_v(sm, n, w - 2, l);
+      }
     } else if (n < nchunks) {
       produce_factors<BF>(sm, n, p, l, one);
     }
     lds_barrier();
-  }
+  };
+  chunk_step(-1, std::true_type{});
+  for (int c = 0; c < nchunks; ++c) chunk_step(c, std::false_type{});
 
   if (consumer) {
 #pragma unroll
