@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN decode steps/s (seq·layer) at B=1/64/512 + achieved HBM GB/s vs peak"
 UNIT = "seq·layer steps/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix peak of MI355X
 # sources the decode kernel is built from (the traffic record is keyed on them)
 KERNEL_SRCS = [os.path.join(ROOT, "gated_deltanet_linear_causal_amd", "csrc", f)
                for f in ("gdn_kernels.hip", "gdn_device.h", "gdn_internal.h")]
@@ -266,7 +267,10 @@ def time_verify(cfg, T, reps, torch, gdn):
             "verify_us": round(vsec * 1e6, 2), "commit_us": round(csec * 1e6, 2),
             "draft_tokens_per_s": round(B * T / vsec, 1),
             "verify_GB_s": round(vbytes / vsec / 1e9, 1), "commit_GB_s": round(cbytes / csec / 1e9, 1),
-            "verify_algorithmic_bytes": vbytes, "commit_algorithmic_bytes": cbytes}
+            "verify_algorithmic_bytes": vbytes, "commit_algorithmic_bytes": cbytes,
+            "verify_roofline": roofline_block("hbm", vbytes / vsec / 1e9, HBM_PEAK_GBS, "GB/s"),
+            "commit_roofline": roofline_block("hbm", cbytes / csec / 1e9, HBM_PEAK_GBS, "GB/s"),
+            "note": "the B=64 states (128 MiB) fit the 256 MB Infinity Cache: effective (cache-assisted) GB/s"}
 
 
 def time_proj(cfg, B, reps, torch, gdn):
@@ -302,77 +306,168 @@ def time_proj(cfg, B, reps, torch, gdn):
     ob = 2 * (H * zd + B * zd + B * H)
     res = {}
     for name, sec, nb, fl in (("in_proj", isec, ib, 2 * B * n_in * H), ("out_proj", osec, ob, 2 * B * H * zd)):
+        # the binding roof: HBM when the bytes take longer at peak than the flops
+        hbm_bound = nb / (HBM_PEAK_GBS * 1e9) >= fl / (MFMA_PEAK_TFLOPS * 1e12)
         res[name] = {"us": round(sec * 1e6, 2), "GB_s": round(nb / sec / 1e9, 1),
                      "hbm_frac": round(nb / sec / 1e9 / HBM_PEAK_GBS, 4), "TFLOP_s": round(fl / sec / 1e12, 2),
-                     "mfma_frac": round(fl / sec / 1e12 / 2500.0, 4), "algorithmic_bytes": nb, "flops": fl}
+                     "mfma_frac": round(fl / sec / 1e12 / MFMA_PEAK_TFLOPS, 4), "algorithmic_bytes": nb, "flops": fl,
+                     "roofline": (roofline_block("hbm", nb / sec / 1e9, HBM_PEAK_GBS, "GB/s") if hbm_bound else
+                                  roofline_block("mfma", fl / sec / 1e12, MFMA_PEAK_TFLOPS, "TFLOP/s"))}
     del w, qkv, z, a, b, gated, y
     return res
 
 
-def cpu_baseline(cfg, data, target_s=10.0):
-    """The fp64 oracle, as it is, on a bounded sample of the same workload: the first
-    n sequences over the drawn steps (n grown until one pass takes >= target_s / 4, at
-    most the whole batch), the pass repeated from the initial states until about
-    target_s of CPU time has been measured."""
+def cpu_info():
+    """Host CPU model (from /proc/cpuinfo), logical CPUs and the CPUs this process may use."""
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.lower().startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def time_oracle(cfg, data, nseq, steps, target_s):
+    """Seconds per run of the fp64 oracle over the first `nseq` sequences and `steps`
+    tokens of `data` (decode inputs [S][B][...] or sequence inputs [B][T][...]), from the
+    initial states; the run is repeated until about target_s has been measured.
+    Returns (seconds per run, runs)."""
     import numpy as np
     from gated_deltanet_linear_causal_amd import inputs as I
     from oracle import oracle as O
-    threads = O.threads(0)
+    idx = np.arange(nseq)
+    s = O.shape_of(cfg, batch=nseq)
+    if cfg.mode == "sequence":
+        sl = lambda k: np.ascontiguousarray(I.widen(data[k][idx, :steps], cfg.act_dtype))
+    else:
+        sl = lambda k: np.ascontiguousarray(np.swapaxes(I.widen(data[k][:steps][:, idx], cfg.act_dtype), 0, 1))
+    args = (sl("qkv"), I.widen(data["conv_w"], cfg.act_dtype), sl("a"), sl("b"), sl("z"))
+    cs0 = I.widen(data["conv_state"][idx], cfg.act_dtype).astype(np.float64)
+    st0 = data["state"][idx].astype(np.float64)
+    total, runs = 0.0, 0
+    while total < target_s:
+        cs, st = cs0.copy(), st0.copy()
+        t0 = time.perf_counter()
+        O.sequence(s, steps, cs, st, args[0], args[1], args[2], args[3], args[4], data["A_log"], data["dt_bias"],
+                   data["norm_w"])
+        total += time.perf_counter() - t0
+        runs += 1
+    return total / runs, runs
+
+
+def cpu_baseline(cfg, data, seq_cfg=None, seq_data=None, target_s=8.0):
+    """The fp64 oracle, as it is, on the GPU machine's host cores, in the units of the GPU
+    figures and on bounded samples of the same workloads (about 20 s of CPU time).
+    Headline: the B = 512 decode workload (seq-layer steps/s), all usable cores. Also:
+    the same with one thread; B = 1, one step (seq-layer steps/s); B = 64, its 32 steps;
+    and the B = 8 x T = 4096 sequence (tokens/s), on a sample of its sequences and
+    tokens."""
+    from gated_deltanet_linear_causal_amd import inputs as I
+    from oracle import oracle as O
+    info = cpu_info()
+    threads = O.threads(info["usable_cpus"] or 1)
     S = data["qkv"].shape[0]
+    # headline: grow the sample of B = 512 sequences until one run takes >= 1 s
     n = 8
     while True:
-        idx = np.arange(min(n, cfg.batch))
-        s = O.shape_of(cfg, batch=len(idx))
-        sw = lambda k: np.ascontiguousarray(np.swapaxes(I.widen(data[k][:, idx], cfg.act_dtype), 0, 1))
-        args = (sw("qkv"), I.widen(data["conv_w"], cfg.act_dtype), sw("a"), sw("b"), sw("z"))
-        cs0 = I.widen(data["conv_state"][idx], cfg.act_dtype).astype(np.float64)
-        st0 = data["state"][idx].astype(np.float64)
-        total, reps = 0.0, 0
-        while True:
-            cs, st = cs0.copy(), st0.copy()
-            t0 = time.perf_counter()
-            O.sequence(s, S, cs, st, args[0], args[1], args[2], args[3], args[4], data["A_log"], data["dt_bias"],
-                       data["norm_w"])
-            total += time.perf_counter() - t0
-            reps += 1
-            if total >= target_s or (len(idx) < cfg.batch and total >= target_s / 4):
-                break
-        if total >= target_s or len(idx) >= cfg.batch:
+        sec, runs = time_oracle(cfg, data, n, S, target_s / 8)
+        if sec >= 1.0 or n >= cfg.batch:
             break
-        n = min(cfg.batch, int(n * max(2.0, min(8.0, target_s / max(total, 1e-3)))))
-    return {"value": len(idx) * S * reps / total, "unit": UNIT, "cores": threads, "kind": "oracle",
-            "sample": "first %d of the %d sequences x %d decode steps of the same inputs, run %d time(s) from "
-                      "the initial states, fp64 C oracle (OpenMP over sequence x k-head units), %.1f s"
-                      % (len(idx), cfg.batch, S, reps, total)}
+        n = min(cfg.batch, n * 4)
+    sec, runs = time_oracle(cfg, data, n, S, target_s)
+    res = {"value": n * S / sec, "unit": UNIT, "cores": threads, "kind": "oracle",
+           "sample": "first %d of the %d sequences x %d decode steps of the B=512 workload's inputs, run %d time(s) "
+                     "from the initial states, fp64 C oracle (OpenMP over sequence x k-head units) on %d threads, "
+                     "%.1f s" % (n, cfg.batch, S, runs, threads, sec * runs)}
+    res.update(info)
+    legs = {}
+    O.threads(1)
+    sec1, runs1 = time_oracle(cfg, data, 8, S, target_s / 4)
+    legs["B512_1_thread"] = {"steps_per_s": round(8 * S / sec1, 1), "threads": 1,
+                             "sample": "8 sequences x %d steps, %d run(s)" % (S, runs1)}
+    O.threads(threads)
+    for i, name in ((1, "B1"), (2, "B64")):
+        c = I.config(i)
+        d = I.generate(c)
+        sec_c, runs_c = time_oracle(c, d, c.batch, c.steps, target_s / 8)
+        legs[name] = {"steps_per_s": round(c.batch * c.steps / sec_c, 1), "threads": threads,
+                      "sample": "all %d sequence(s) x %d step(s), %d run(s)" % (c.batch, c.steps, runs_c)}
+    if seq_cfg is not None:
+        T = min(seq_cfg.steps, 512)
+        sec_s, runs_s = time_oracle(seq_cfg, seq_data, seq_cfg.batch, T, target_s / 4)
+        legs["B8_T4096"] = {"tokens_per_s": round(seq_cfg.batch * T / sec_s, 1), "threads": threads,
+                            "sample": "all %d sequences, first %d of the %d tokens, %d run(s)"
+                                      % (seq_cfg.batch, T, seq_cfg.steps, runs_s)}
+    res["legs"] = legs
+    return res
+
+
+def bench_library():
+    """The benchmark's own streaming-copy library (libgdn_bench.so, built with libgdn.so)."""
+    import ctypes
+    path = os.path.join(ROOT, "gated_deltanet_linear_causal_amd", "libgdn_bench.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libgdn_bench.so is not built; run `python -m gated_deltanet_linear_causal_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.gdn_bench_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.gdn_bench_stream_copy.restype = ctypes.c_int
+    return lib
 
 
 def copy_bandwidth(torch, nbytes=1 << 30, reps=20):
-    """Achievable-bandwidth reference: a plain device copy of `nbytes` (read + write
-    counted), timed with HIP events."""
+    """Achievable-bandwidth reference: the streaming copy of `nbytes` (read + write
+    counted) with 128-bit buffer loads and stores, the access path of the decode kernel,
+    with the non-temporal and with the default cache policy; GB/s of each, HIP events."""
+    lib = bench_library()
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3 / reps
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, nt in (("nt", 1), ("default", 0)):
+        def run():
+            rc = lib.gdn_bench_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, nt, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("gdn_bench_stream_copy failed (%d)" % rc)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = 2 * nbytes / (e0.elapsed_time(e1) / 1e3 / reps) / 1e9
+    assert torch.equal(src, dst)
     del src, dst
-    return 2 * nbytes / sec / 1e9
+    return res
 
 
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
+    """A streaming copy of known size (nt policy) for scaling the PMC traffic counters."""
+    lib = bench_library()
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
     for _ in range(reps):
-        dst.copy_(src)
+        if lib.gdn_bench_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, 1, stream.cuda_stream) != 0:
+            raise RuntimeError("gdn_bench_stream_copy failed")
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
-                      "reps": reps}))
+                      "reps": reps, "kernel": "stream_copy<2> (nt)"}))
+
+
+def roofline_block(bound, achieved, peak, unit):
+    return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4)}
 
 
 def summarize(path):
@@ -473,9 +568,13 @@ def main():
             del dd
         result["sweep"] = sweep
         torch.cuda.empty_cache()
-        result["roofline"]["copy_GB_s"] = round(copy_bandwidth(torch), 1)
+        cb = copy_bandwidth(torch)
+        result["roofline"]["copy_GB_s"] = round(max(cb.values()), 1)
+        result["roofline"]["copy_nt_GB_s"] = round(cb["nt"], 1)
+        result["roofline"]["copy_default_GB_s"] = round(cb["default"], 1)
         c = I.config(4)
-        _, dd = build_inputs(c, c.steps, torch)
+        seq_cfg = c
+        seq_data, dd = build_inputs(c, c.steps, torch)
         ssec = time_sequence(c, dd, 20, torch, gdn)
         b = algorithmic_bytes(c, T=c.steps)
         fl = chunk_flops(c) * ((c.steps + 31) // 32) * c.batch * c.num_v_heads
@@ -484,7 +583,11 @@ def main():
                               "GB_s": round(b / ssec / 1e9, 1), "hbm_frac": round(b / ssec / 1e9 / HBM_PEAK_GBS, 4),
                               "useful_TFLOP_s": round(fl / ssec / 1e12, 2),
                               "mfma_issued_TFLOP_s": round(3 * fl / ssec / 1e12, 2),
-                              "mfma_frac": round(3 * fl / ssec / 1e12 / 2500.0, 4)}
+                              "mfma_frac": round(3 * fl / ssec / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                              "algorithmic_bytes": b,
+                              # the bytes at peak (173 us) take longer than the issued fp16 products
+                              # at peak (155 us): HBM is the binding roof
+                              "roofline": roofline_block("hbm", b / ssec / 1e9, HBM_PEAK_GBS, "GB/s")}
         del dd
         torch.cuda.empty_cache()
         result["verify"] = time_verify(I.config(2), 4, 50, torch, gdn)
@@ -494,7 +597,10 @@ def main():
             result["proj"]["B%d" % B] = time_proj(I.config(2), B, 50, torch, gdn)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, data)
+        if args.no_sweep:
+            seq_cfg = I.config(4).with_(steps=512)
+            seq_data = I.generate(seq_cfg)
+        result["cpu_baseline"] = cpu_baseline(cfg, data, seq_cfg, seq_data)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -1,4 +1,5 @@
-"""Builds libgdn.so (host C++ + HIP kernels for gfx950) in the package directory.
+"""Builds libgdn.so (host C++ + HIP kernels for gfx950) in the package directory, and
+libgdn_bench.so (the benchmark's streaming-copy reference kernel).
 
     python -m gated_deltanet_linear_causal_amd.build
 
@@ -19,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_kernels.hip", "gdn_verify.hip", "gdn_chunked.hip", "gdn_proj.hip"]
+BENCH_LIB = os.path.join(PKG, "libgdn_bench.so")
+BENCH_SOURCES = ["bench_copy.hip"]
 ARCH = "gfx950"
 
 
@@ -36,14 +39,21 @@ def flags(extra=()):
 
 
 def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
+    """Builds libgdn.so at `out` and the benchmark library beside the package."""
+    _build(out, SOURCES, extra, verbose)
+    _build(BENCH_LIB, BENCH_SOURCES, extra, verbose)
+    return out
+
+
+def _build(out, sources, extra, verbose):
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *flags(extra), "-shared", *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    cmd = [hipcc(), *flags(extra), "-shared", *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("building libgdn.so failed")
+        raise RuntimeError("building %s failed" % os.path.basename(out))
     os.replace(tmp, out)
     return out
 

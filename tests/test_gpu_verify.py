@@ -27,12 +27,12 @@ pytestmark = pytest.mark.gpu
 
 
 def tol_of(act, d):
-    """bf16 activations: the workload bound. fp32 activations: 1e-5 at d = 32; at
-    d >= 64 the readout sums d products per output and fp32 itself lands near 1e-5
-    relative, so 1e-4 there."""
+    """bf16 activations: the workload bound. fp32 activations: 1e-5, the bound stated
+    for the all-fp32 layer (verify and commit run the token-by-token rule in fp32; they
+    measure ~3e-6 at d = 128)."""
     if act == "bf16":
         return TOL["bf16"]
-    return (1e-5, 1e-5, 1e-1) if d <= 32 else (1e-4, 1e-4, 1e-1)
+    return (1e-5, 1e-5, 1e-1)
 
 
 def cfg_of(name, B, Hk, Hv, d, K, act, T):
