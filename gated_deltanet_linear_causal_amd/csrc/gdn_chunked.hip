@@ -698,8 +698,13 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, q = l >> 4, c16 = l & 15;
-  const int b = blockIdx.x / a.Hv;
-  const int h = blockIdx.x - b * a.Hv;
+  // Workgroups are dealt to the 8 XCDs round robin by id. When the grid divides by 8,
+  // consecutive (sequence, v-head) units share an XCD, so the G v-heads that read one
+  // k-head's q and k rows find them in the same L2 (the rows are fetched from HBM once).
+  const unsigned nwg = gridDim.x, x = blockIdx.x;
+  const int u = static_cast<int>(nwg % 8 == 0 ? (x % 8) * (nwg / 8) + x / 8 : x);
+  const int b = u / a.Hv;
+  const int h = u - b * a.Hv;
   const int g = h / a.G;
   const int T = a.T;
   const int nchunks = (T + kC - 1) / kC;

@@ -150,7 +150,12 @@ gdn_status_t gdn_decode_layer_pooled(const gdn_shape_t* shape, int32_t pool_size
  * two or more passes over the device's compute units), with every operand split into
  * two fp16 halves (22 significant bits): the recurrent state and the per-token deltas
  * must stay below the fp16 range (6.5e4 in magnitude; the layer's values are orders of
- * magnitude smaller). Shorter sequences and other shapes run token by token in fp32. */
+ * magnitude smaller). The state and the deltas are split unscaled, so their low halves
+ * can fall in fp16's subnormal range: with fp32 activations this form agrees with the
+ * fp64 recurrence to about 2e-5 relative, where the token-by-token path reaches about
+ * 1e-6. Shorter sequences and other shapes run token by token in fp32. Since the choice
+ * depends on T and on B x H_v, the same sequence may be evaluated at either precision
+ * (and to different bits) at a different batch size. */
 gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_state, float* state,
                           const void* qkv, const void* conv1d_weight, const void* dt_raw,
                           const void* b_raw, const void* z, const float* A_log,
