@@ -65,45 +65,50 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
 
   // ---- A. conv inputs and taps into LDS, then conv + SiLU of every (token, channel), gates
   {
-    // 16-byte pieces of 8 consecutive unit channels (a segment's channels are
-    // consecutive in a qkv row and in conv1d_weight), every load issued before the
-    // first LDS store
-    constexpr int kPieces = NCH / 8;                                   // per row
-    constexpr int kXPer = (kRows * kPieces + NT - 1) / NT;
-    constexpr int kWChunks = NCH * kMaxConvTaps / 8;                   // taps, 8 per chunk
-    constexpr int kWPer = (kWChunks + NT - 1) / NT;
-    constexpr int kE = BF ? 1 : 2;                                     // 16-byte words per 8 elements
-    constexpr int kZPer = (kTM * D / 8 + NT - 1) / NT;                 // z pieces
-    const int nrow = K - 1 + T, nw = NCH * K / 8, nz = T * (D / 8);
-    u32x4 xr[kXPer][kE], wr[kWPer][kE], zr[kZPer][kE];
-    auto ld8 = [&](const void* base, long elem, u32x4(&dst)[kE]) {
+    // 16-byte pieces of 8 consecutive unit channels (a segment's D channels are
+    // consecutive in a qkv row and in conv1d_weight). The pieces are assigned segment by
+    // segment, so the segment's channel offset is uniform and each lane's address is a
+    // row base plus a fixed piece offset. Every load is issued before the first LDS store.
+    constexpr int kE = BF ? 1 : 2;             // 16-byte words per 8 elements
+    constexpr int kEs = BF ? 2 : 4;            // bytes per element
+    constexpr int kPR = D / 8;                 // pieces per row and segment
+    constexpr int kXPer = (kRows * kPR + NT - 1) / NT;
+    constexpr int kWPer = (D * kMaxConvTaps / 8 + NT - 1) / NT;
+    constexpr int kZPer = (kTM * kPR + NT - 1) / NT;
+    const int nrow = K - 1 + T;
+    const int npw = D * K / 8;                 // tap pieces per segment
+    u32x4 xr[3][kXPer][kE], wr[3][kWPer][kE], zr[kZPer][kE];
+    auto ld8 = [&](const char* p, u32x4(&dst)[kE]) {
 #pragma unroll
-      for (int e = 0; e < kE; ++e)
-        dst[e] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + (elem * (BF ? 2 : 4)) + 16 * e);
+      for (int e = 0; e < kE; ++e) dst[e] = *reinterpret_cast<const u32x4*>(p + 16 * e);
     };
+    // first channel of each segment: Q and K of k-head g, V of v-head h
+    const long ch[3] = {static_cast<long>(g) * D, static_cast<long>(a.Hk + g) * D, static_cast<long>(2 * a.Hk + h) * D};
+    const char* cs_row0 = static_cast<const char*>(a.conv_state) + static_cast<long>(b) * (K - 1) * C * kEs;
+    const char* x_row0 = static_cast<const char*>(a.qkv) + b * a.qkv_bs * kEs;
     // Loads are unconditional, with indices clamped to valid rows (only the LDS stores
     // below are conditional): a load inside a branch is waited for where the branch
     // joins, which would put each load's latency in series.
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
-      const int it = min(t + i * NT, nrow * kPieces - 1), j = it / kPieces, pc = it - j * kPieces;
-      const long gc = chan(8 * pc);
-      const bool from_state = j < K - 1;
-      const void* base = from_state ? a.conv_state : a.qkv;
-      const long elem = from_state ? (static_cast<long>(b) * (K - 1) + j) * C + gc
-                                   : b * a.qkv_bs + (j - (K - 1)) * a.qkv_ts + gc;
-      ld8(base, elem, xr[i]);
+      const int it = min(t + i * NT, nrow * kPR - 1), j = it / kPR, pc = it - j * kPR;
+      // rows 0..K-2 come from the conv state, the rest are the draft tokens
+      const char* row = j < K - 1 ? cs_row0 + static_cast<long>(j) * C * kEs : x_row0 + (j - (K - 1)) * a.qkv_ts * kEs;
+#pragma unroll
+      for (int sg = 0; sg < 3; ++sg) ld8(row + (ch[sg] + 8 * pc) * kEs, xr[sg][i]);
     }
 #pragma unroll
     for (int i = 0; i < kWPer; ++i) {
-      const int it = min(t + i * NT, nw - 1);
-      const int per_seg = D * K / 8, sg = it / per_seg, off = 8 * (it - sg * per_seg);
-      ld8(a.conv_w, chan(sg * D) * K + off, wr[i]);
+      const int it = min(t + i * NT, npw - 1);
+#pragma unroll
+      for (int sg = 0; sg < 3; ++sg)
+        ld8(static_cast<const char*>(a.conv_w) + (ch[sg] * K + 8 * it) * kEs, wr[sg][i]);
     }
 #pragma unroll
     for (int i = 0; i < kZPer; ++i) {
-      const int it = min(t + i * NT, nz - 1), tok = it / (D / 8), pc = it - tok * (D / 8);
-      ld8(a.z, b * a.z_bs + tok * a.z_ts + static_cast<long>(h) * D + 8 * pc, zr[i]);
+      const int it = min(t + i * NT, T * kPR - 1), tok = it / kPR, pc = it - tok * kPR;
+      ld8(static_cast<const char*>(a.z) + (b * a.z_bs + tok * a.z_ts + static_cast<long>(h) * D + 8 * pc) * kEs,
+          zr[i]);
     }
     // the gate inputs and then the state of head h (read only) go out before the first
     // LDS store waits for the loads above, so all three latencies overlap; the state is
@@ -121,18 +126,22 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
     };
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
-      const int it = t + i * NT, j = it / kPieces, pc = it - j * kPieces;
-      if (j < nrow) put8(&s_x[j][8 * pc], xr[i]);
+      const int it = t + i * NT, j = it / kPR, pc = it - j * kPR;
+      if (j < nrow)
+#pragma unroll
+        for (int sg = 0; sg < 3; ++sg) put8(&s_x[j][sg * D + 8 * pc], xr[sg][i]);
     }
 #pragma unroll
     for (int i = 0; i < kWPer; ++i) {
       const int it = t + i * NT;
-      if (it < nw) put8(&s_w[8 * it], wr[i]);
+      if (it < npw)
+#pragma unroll
+        for (int sg = 0; sg < 3; ++sg) put8(&s_w[sg * D * K + 8 * it], wr[sg][i]);
     }
 #pragma unroll
     for (int i = 0; i < kZPer; ++i) {
-      const int it = t + i * NT, tok = it / (D / 8), pc = it - tok * (D / 8);
-      if (it < nz) put8(&s_z[tok][8 * pc], zr[i]);
+      const int it = t + i * NT, tok = it / kPR, pc = it - tok * kPR;
+      if (tok < T) put8(&s_z[tok][8 * pc], zr[i]);
     }
   }
   if (t < T) {
@@ -214,19 +223,23 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   }
   __syncthreads();
 
-  // ---- B. the T delta-rule steps (no barrier: each lane reads LDS written above)
-  for (int tok = 0; tok < T; ++tok) {
+  // ---- B. the T delta-rule steps (no barrier: each lane reads LDS written above). The
+  // state after the last token is not needed here (commit rebuilds it from the trail),
+  // so the last step only forms delta and the readout.
+  auto step = [&](int tok, auto form) {
     const float alpha = s_gate[0][tok], beta = s_gate[1][tok];
     const float4 v4 = *reinterpret_cast<const float4*>(&s_v[tok][4 * cg]);
     float4 delta;
-    const float4 ot = delta_rule<D, 1, false, false>(hreg, &s_k[tok][rg * R], &s_q[tok][rg * R], v4, alpha, beta,
-                                                     s_gate[2][tok], srs, voff, 0, &delta);
+    const float4 ot = delta_rule<D, 1, false, false, R, decltype(form)::value>(
+        hreg, &s_k[tok][rg * R], &s_q[tok][rg * R], v4, alpha, beta, s_gate[2][tok], srs, voff, 0, &delta);
     if (rg == 0) {
       *reinterpret_cast<float4*>(&s_o[tok][4 * cg]) = ot;
       *reinterpret_cast<float4*>(a.trail_delta + ((bt0 + tok) * a.Hv + h) * D + 4 * cg) = delta;
     }
     if (t == 0) a.trail_alpha[(bt0 + tok) * a.Hv + h] = alpha;
-  }
+  };
+  for (int tok = 0; tok + 1 < T; ++tok) step(tok, std::integral_constant<int, 1>{});
+  step(T - 1, std::integral_constant<int, 2>{});  // T >= 1
 
   // ---- C. per-head RMSNorm and gated outputs of all tokens
   float ss[kTM];
