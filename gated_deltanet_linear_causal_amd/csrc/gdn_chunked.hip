@@ -65,6 +65,7 @@ constexpr int kD = 128;       // head dim (d_k = d_v)
 constexpr int kC = 32;        // tokens per chunk
 constexpr int kNT = 512;      // 8 waves: 4 consumers, 4 producers
 constexpr int kTaps = 4;      // conv taps (K)
+constexpr int kGateWave = 1;  // the producer wave that loads the gate inputs and scans the gates
 constexpr int kRows = 8 + kTaps - 1;  // conv input rows of a producer wave (8 tokens + history)
 constexpr int kQKLd = kD + 4;  // halves per row of the [t][i] planes (66 dwords: the 16 rows of a
                                // fragment read start in 16 different even banks)
@@ -81,6 +82,8 @@ struct Operands {
   alignas(16) float v[kC][kD];                             // log2(e) v (see silu_l2e), swizzled
   alignas(16) double g[kC];                                // running log-gate sums
   alignas(16) float beta[kC];
+  alignas(16) float gam[kC];                               // exp(g_t)
+  alignas(16) float dec[kC];                               // exp(g_C - g_t), g_C = g[kC - 1]
 };
 __device__ __forceinline__ int vswz(int t) { return 16 * ((t >> 2) & 3); }
 
@@ -397,7 +400,7 @@ __device__ __forceinline__ float gate_input(uint32_t raw) {
 // the inclusive running sum of log(alpha_t) = -exp(A_log) softplus(dt_t + dt_bias), in
 // fp64. Tokens past the end get beta 0 and log alpha 0.
 __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float br, float A_exp, float dt_bias,
-                                            double* g_out, float* beta_out) {
+                                            Operands& op) {
   float la = 0.0f, bt = 0.0f;
   if (lane < min(kC, left)) {
     // softplus(x) = max(x, 0) + log(1 + exp(-|x|)); the log's argument lies in (1, 2]
@@ -414,9 +417,14 @@ __device__ __forceinline__ void chunk_gates(int left, int lane, float dt, float 
   gg += dpp64<0x118>(gg);  // row_shr:8
   const double row0 = readlane64(gg, 15);
   if (lane >= 16) gg += row0;
+  // the decay factors the consumers apply to every row: gamma_t = exp(g_t) and
+  // exp(g_C - g_t), each difference formed in fp64 before the exponential
+  const double gC = readlane64(gg, kC - 1);
   if (lane < kC) {
-    g_out[lane] = gg;
-    beta_out[lane] = bt;
+    op.g[lane] = gg;
+    op.beta[lane] = bt;
+    op.gam[lane] = __expf(static_cast<float>(gg));
+    op.dec[lane] = __expf(static_cast<float>(gC - gg));
   }
 }
 
@@ -751,7 +759,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
   uint32_t gdt = 0, gbr = 0;
   if constexpr (BF) {
     if (!consumer && nchunks > 0) {
-      if (p == 0) load_gate_inputs<BF>(a, b, h, 0, l, gdt, gbr);
+      if (p == kGateWave) load_gate_inputs<BF>(a, b, h, 0, l, gdt, gbr);
       for (int sg = 0; sg < 2; ++sg) stage_inputs(sm, a, b, g, h, 0, p, l, sg);
     }
   }
@@ -810,7 +818,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = 16 * lt + 4 * q + r;
-            const float gam = __expf(static_cast<float>(op.g[t]));
+            const float gam = op.gam[t];
             const float bt = op.beta[t];
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
@@ -869,13 +877,12 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
           }
         // H = gamma_C H + K^T diag(exp(g_C - g)) Delta
         {
-          const double gC = op.g[kC - 1];
-          const float gamC = __expf(static_cast<float>(gC));
+          const float gamC = op.gam[kC - 1];
 #pragma unroll
           for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float f = __expf(static_cast<float>(gC - op.g[16 * lt + 4 * q + r]));
+              const float f = op.dec[16 * lt + 4 * q + r];
 #pragma unroll
               for (int jt = 0; jt < 2; ++jt) delta[lt][jt][r] *= f;
             }
@@ -904,12 +911,12 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
           const float dt = gate_input<BF>(gdt), br = gate_input<BF>(gbr);
           // memory operations in issue order: z rows of chunk c (2), v rows of chunk n (3;
           // consumer waves 2 and 3 convolve them in phase 2), gate inputs of chunk n + 1
-          // (2, wave p = 0), q and k rows of chunk n + 1 (3 per segment, each issued once
+          // (2, wave p = kGateWave), q and k rows of chunk n + 1 (3 per segment, each issued once
           // the segment's staged rows of chunk n are in registers)
           if (c >= 0) stage_z(sm, a, b, h, c, p, l);
           stage_inputs(sm, a, b, g, h, n, p, l, 2);
-          if (p == 0 && n + 1 < nchunks) load_gate_inputs<BF>(a, b, h, n + 1, l, gdt, gbr);
-          if (p == 0) chunk_gates(T - n * kC, l, dt, br, A_exp, dt_bias, sm.op[n & 1].g, sm.op[n & 1].beta);
+          if (p == kGateWave && n + 1 < nchunks) load_gate_inputs<BF>(a, b, h, n + 1, l, gdt, gbr);
+          if (p == kGateWave) chunk_gates(T - n * kC, l, dt, br, A_exp, dt_bias, sm.op[n & 1]);
           produce_conv<BF, 2>(
               sm, a, n, p, l,
               [&](int sg, float(&x0)[kRows], float(&x1)[kRows]) {
@@ -932,7 +939,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
           // flight)
           if (n + 1 >= nchunks)
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          else if (p == 0)
+          else if (p == kGateWave)
             asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
           else
             asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
@@ -945,11 +952,10 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
         if (n < nchunks) {
           F32Inputs xr;
           load_inputs_f32(a, b, g, h, n, p, l, xr);
-          if (p == 0) {
+          if (p == kGateWave) {
             uint32_t dt, br;
             load_gate_inputs<BF>(a, b, h, n, l, dt, br);
-            chunk_gates(T - n * kC, l, gate_input<BF>(dt), gate_input<BF>(br), A_exp, dt_bias, sm.op[n & 1].g,
-                        sm.op[n & 1].beta);
+            chunk_gates(T - n * kC, l, gate_input<BF>(dt), gate_input<BF>(br), A_exp, dt_bias, sm.op[n & 1]);
           }
           produce_conv<BF, 3>(
               sm, a, n, p, l,

@@ -259,6 +259,7 @@ __global__ __launch_bounds__(64 * KW) void gdn_proj_skinny(const ProjArgs p) {
     if (i < p.nseg && static_cast<int>(blockIdx.x) >= p.seg[i].tile0) si = i;
   const ProjSeg s = p.seg[si];
   const long n0 = static_cast<long>(blockIdx.x - s.tile0) * BN;
+  const int m0 = static_cast<int>(blockIdx.y) * BM;  // row block
   const int K = p.K;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
   const int kw = K / KW, nkb = kw / 64;
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(64 * KW) void gdn_proj_skinny(const ProjArgs p) {
   const uint16_t* xp[TI];
   const uint16_t* wp[TJ];
 #pragma unroll
-  for (int i = 0; i < TI; ++i) xp[i] = p.x + static_cast<long>(min(16 * i + c16, p.M - 1)) * K + k0;
+  for (int i = 0; i < TI; ++i) xp[i] = p.x + static_cast<long>(min(m0 + 16 * i + c16, p.M - 1)) * K + k0;
 #pragma unroll
   for (int j = 0; j < TJ; ++j) wp[j] = s.w + min(n0 + 16 * j + c16, s.n - 1) * K + k0;
 
@@ -322,28 +323,35 @@ __global__ __launch_bounds__(64 * KW) void gdn_proj_skinny(const ProjArgs p) {
     for (int u = 0; u < KW; ++u) v += red[u][e];
     const int m = e / BN;
     const long n = n0 + (e - m * BN);
-    if (m < p.M && n < s.n) put(s, m, n, v);
+    if (m0 + m < p.M && n < s.n) put(s, m0 + m, n, v);
   }
 }
 
 template <int TI, int TJ, int KW>
-hipError_t launch_skinny(ProjArgs& p, hipStream_t st) {
+hipError_t launch_skinny(ProjArgs& p, int mblocks, hipStream_t st) {
   int tiles = 0;
   for (int i = 0; i < p.nseg; ++i) {
     p.seg[i].tile0 = tiles;
     tiles += static_cast<int>((p.seg[i].n + 16 * TJ - 1) / (16 * TJ));
   }
-  gdn_proj_skinny<TI, TJ, KW, 3><<<tiles, 64 * KW, 0, st>>>(p);
+  gdn_proj_skinny<TI, TJ, KW, 3><<<dim3(tiles, mblocks), 64 * KW, 0, st>>>(p);
   return hipGetLastError();
 }
 
-// TI from the row count (16 rows per accumulator tile)
+// Row blocks and TI (16 rows per accumulator tile) from the row count. With fewer than
+// 256 column tiles the rows are split into blocks until the grid covers the CUs: each
+// workgroup then streams fewer X rows through its CU, and the row blocks of a column
+// tile (workgroups t and t + tiles, on the same XCD when tiles is a multiple of 8) find
+// its W rows in the shared L2.
 template <int TJ, int KW>
-hipError_t launch_skinny_m(ProjArgs& p, hipStream_t st) {
-  if (p.M <= 16) return launch_skinny<1, TJ, KW>(p, st);
-  if (p.M <= 32) return launch_skinny<2, TJ, KW>(p, st);
-  if (p.M <= 48) return launch_skinny<3, TJ, KW>(p, st);
-  return launch_skinny<4, TJ, KW>(p, st);
+hipError_t launch_skinny_m(ProjArgs& p, long ntiles, int cus, hipStream_t st) {
+  int mb = 1;
+  while (ntiles * mb < cus && 16 * mb < p.M) mb *= 2;
+  const int rows = (p.M + mb - 1) / mb;
+  if (rows <= 16) return launch_skinny<1, TJ, KW>(p, (p.M + 15) / 16, st);
+  if (rows <= 32) return launch_skinny<2, TJ, KW>(p, (p.M + 31) / 32, st);
+  if (rows <= 48) return launch_skinny<3, TJ, KW>(p, (p.M + 47) / 48, st);
+  return launch_skinny<4, TJ, KW>(p, (p.M + 63) / 64, st);
 }
 
 // ----------------------------------------------------------------------------------
@@ -545,10 +553,12 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
   }
   p.rows = rows;
   // Few output columns and a long K (the out_proj shape) at 3..32 rows: the skinny MFMA
-  // kernel, K split over 8 waves, one 16-column tile per workgroup. Measured at hidden =
-  // 2048, K = 4096: 7.5 / 9.6 / 13.4 us at 4 / 16 / 32 rows, against 8.3 / 15.4 / 15.5
-  // with the weight-streaming and tiled paths.
-  if (p.M >= 3 && p.M <= 32 && rows <= 4096 && p.K % 512 == 0) return launch_skinny_m<1, 8>(p, st);
+  // kernel, K split over 8 waves, one 16-column tile per workgroup, 16 rows per workgroup
+  // when that doubles the grid. Measured at hidden = 2048, K = 4096: 8.3 / 9.6 / 9.7 us at
+  // 4 / 16 / 32 rows (32 rows in one block: 13.3 us), against 8.3 / 15.4 / 15.5 with the
+  // weight-streaming and tiled paths. At 48 and 64 rows the split gave no gain over the
+  // tiled kernel (13.3-13.5 us either way).
+  if (p.M >= 3 && p.M <= 32 && rows <= 4096 && p.K % 512 == 0) return launch_skinny_m<1, 8>(p, (rows + 15) / 16, 256, st);
   // 33..64 rows and many columns (the in_proj shape): one 64-row tile, so the weights
   // stream once (32-row tiles read them twice); 19.8 against 21.6 us at 64 rows.
   if (p.M > 32 && p.M <= 64 && rows >= 8192 && p.K % 256 == 0) return launch_mfma<64, 64, 256, 2, 2>(p, st);
