@@ -203,16 +203,21 @@ def time_sequence(cfg, d, reps, torch, gdn):
         gdn.gdn_sequence(s, cfg.steps, d["conv_state"], d["state"], d["qkv"], d["conv_w"], d["a"], d["b"], d["z"],
                          d["A_log"], d["dt_bias"], d["norm_w"], out, workspace=ws, stream=stream)
 
-    for _ in range(10):  # untimed: the clock settles over the first few calls
+    for _ in range(20):  # untimed: the clock settles over the first calls
         run()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / 1e3 / reps
+    # median of batches of `reps` calls (single calls of this kernel vary by up to ~30 %
+    # from call to call on a busy clock)
+    batches = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        batches.append(e0.elapsed_time(e1) / 1e3 / reps)
+    return sorted(batches)[len(batches) // 2]
 
 
 def chunk_flops(cfg, C=32):
@@ -578,7 +583,8 @@ def main():
         ssec = time_sequence(c, dd, 20, torch, gdn)
         b = algorithmic_bytes(c, T=c.steps)
         fl = chunk_flops(c) * ((c.steps + 31) // 32) * c.batch * c.num_v_heads
-        result["sequence"] = {"workload": "B=8 x T=4096 gdn_sequence (chunked MFMA form, 32-token chunks)",
+        result["sequence"] = {"workload": "B=8 x T=4096 gdn_sequence (chunked MFMA form, 32-token chunks); "
+                                          "median of 5 batches of 20 calls",
                               "ms": round(ssec * 1e3, 3), "tokens_per_s": round(c.batch * c.steps / ssec, 1),
                               "GB_s": round(b / ssec / 1e9, 1), "hbm_frac": round(b / ssec / 1e9 / HBM_PEAK_GBS, 4),
                               "useful_TFLOP_s": round(fl / ssec / 1e12, 2),
