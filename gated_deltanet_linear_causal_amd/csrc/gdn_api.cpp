@@ -156,7 +156,7 @@ struct TrailLayout {
 
 extern "C" {
 
-int32_t gdn_abi_version(void) { return (1 << 16) | 1; }
+int32_t gdn_abi_version(void) { return (1 << 16) | 2; }
 
 const char* gdn_status_string(int32_t st) {
   switch (st) {
@@ -268,6 +268,63 @@ gdn_status_t gdn_decode_layer(const gdn_shape_t* shape, void* conv1d_state, floa
   a.norm_w = norm_weight;
   a.out = out;
   a.out_bs = static_cast<long>(z.Hv * z.d);
+  (void)hipGetLastError();
+  return launched(gdn::launch_step(gdn::kModeFused, shape->head_k_dim, heads_per_pass(shape), a,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_decode_layer_debug(const gdn_shape_t* shape, void* conv1d_state, float* state, const void* qkv,
+                                    const void* conv1d_weight, const void* dt_raw, const void* b_raw,
+                                    const void* z_in, const float* A_log, const float* dt_bias,
+                                    const float* norm_weight, void* out, float* qkv_act_tap, float* alpha_tap,
+                                    float* beta_tap, float* y_tap, float* y_norm_tap, void* stream) {
+  gdn_status_t st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  const Sizes z(shape);
+  if (z.B == 0) return GDN_OK;
+  const size_t yb = z.B * z.Hv * z.d * 4;
+  const Buf bufs[] = {
+      {conv1d_state, z.conv_state(), true, 16},
+      {state, z.state(), true, 16},
+      {qkv, z.B * z.C * z.ea, false, 16},
+      {conv1d_weight, z.conv_w(), false, 16},
+      {dt_raw, z.B * z.Hv * z.ea, false, z.ea},
+      {b_raw, z.B * z.Hv * z.ea, false, z.ea},
+      {z_in, z.B * z.Hv * z.d * z.ea, false, 16},
+      {A_log, z.Hv * 4, false, 4},
+      {dt_bias, z.Hv * 4, false, 4},
+      {norm_weight, z.d * 4, false, 16},
+      {out, z.B * z.Hv * z.d * z.eo, true, 16},
+      // taps: optional (a null tap is not written)
+      {qkv_act_tap, qkv_act_tap ? z.B * z.C * 4 : 0, true, 4},
+      {alpha_tap, alpha_tap ? z.B * z.Hv * 4 : 0, true, 4},
+      {beta_tap, beta_tap ? z.B * z.Hv * 4 : 0, true, 4},
+      {y_tap, y_tap ? yb : 0, true, 16},
+      {y_norm_tap, y_norm_tap ? yb : 0, true, 16},
+  };
+  if ((st = check_buffers(bufs, 16)) != GDN_OK) return st;
+  gdn::KernelArgs a = base_args(shape);
+  a.conv_state = conv1d_state;
+  a.state = state;
+  a.qkv = qkv;
+  a.qkv_bs = static_cast<long>(z.C);
+  a.conv_w = conv1d_weight;
+  a.dt_raw = dt_raw;
+  a.b_raw = b_raw;
+  a.ab_bs = static_cast<long>(z.Hv);
+  a.z = z_in;
+  a.z_bs = static_cast<long>(z.Hv * z.d);
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.norm_w = norm_weight;
+  a.out = out;
+  a.out_bs = static_cast<long>(z.Hv * z.d);
+  a.tap_act = qkv_act_tap;
+  a.tap_alpha = alpha_tap;
+  a.tap_beta = beta_tap;
+  a.tap_y = y_tap;
+  a.tap_y_norm = y_norm_tap;
+  a.taps = 1;
   (void)hipGetLastError();
   return launched(gdn::launch_step(gdn::kModeFused, shape->head_k_dim, heads_per_pass(shape), a,
                                    static_cast<hipStream_t>(stream)));

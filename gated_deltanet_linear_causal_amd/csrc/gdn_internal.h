@@ -41,6 +41,13 @@ struct KernelArgs {
   float* trail_k;          // [B][T][Hk][D]  unit-norm k_t of each k-head
   float* trail_alpha;      // [B][T][Hv]     alpha_t of each v-head
   const int* accepted;     // [B] tokens to commit per sequence
+  // intermediate taps of a fused decode step (generic kernel only; each may be null)
+  float* tap_act;          // [B][C]       q, k after the L2 norms, v after SiLU
+  float* tap_alpha;        // [B][Hv]
+  float* tap_beta;         // [B][Hv]
+  float* tap_y;            // [B][Hv][D]   readout o = H'^T q / sqrt(d_k)
+  float* tap_y_norm;       // [B][Hv][D]   o r norm_weight (before the silu(z) gate)
+  int taps;                // 1: some tap is set (the launcher then takes the generic kernel)
 };
 
 enum Mode : int { kModeConv = 0, kModeRec = 1, kModeFused = 2 };

@@ -331,6 +331,9 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_generic(const Ker
       else {
         s_v[c - 2 * D] = v;
         if constexpr (MODE == kModeConv) a.qkv_act_out[static_cast<long>(b) * a.C + gc] = v;
+        if constexpr (MODE == kModeFused) {
+          if (a.tap_act) a.tap_act[static_cast<long>(b) * a.C + gc] = v;
+        }
       }
     }
     __syncthreads();
@@ -354,6 +357,11 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_generic(const Ker
       } else {
         s_q[i] = qn;
         s_k[i] = kn;
+        if (MODE == kModeFused && a.tap_act) {
+          float* act = a.tap_act + static_cast<long>(b) * a.C;
+          act[static_cast<long>(g) * D + i] = qn;
+          act[static_cast<long>(a.Hk) * D + static_cast<long>(g) * D + i] = kn;
+        }
       }
     }
     if constexpr (MODE == kModeConv) return;
@@ -392,6 +400,15 @@ __global__ __launch_bounds__((Layout<D, P>::NT)) void gdn_step_generic(const Ker
         if (rg == 0)
           store_out4(a.out, b * a.out_bs + static_cast<long>(h) * D + 4 * cg, gated(o, r, w4, Act<BF>::cvt4(z_raw)),
                      a.out_bf16 != 0);
+        if (MODE == kModeFused && a.taps) {
+          const long hb = static_cast<long>(b) * a.Hv + h;
+          if (rg == 0 && a.tap_y) *reinterpret_cast<float4*>(a.tap_y + hb * D + 4 * cg) = o;
+          if (rg == 0 && a.tap_y_norm)
+            *reinterpret_cast<float4*>(a.tap_y_norm + hb * D + 4 * cg) =
+                make_float4(o.x * r * w4.x, o.y * r * w4.y, o.z * r * w4.z, o.w * r * w4.w);
+          if (u == 0 && a.tap_alpha) a.tap_alpha[hb] = alpha;
+          if (u == 0 && a.tap_beta) a.tap_beta[hb] = beta;
+        }
         if (pass + 1 < passes) __syncthreads();  // hred is rewritten by the next pass
       }
     }
@@ -545,8 +562,9 @@ hipError_t launch_seq_t(const KernelArgs& a, hipStream_t s) {
 bool step_supported(int d, int p) { return (d == 32 || d == 64 || d == 128) && (p == 1 || p == 2); }
 
 hipError_t launch_step(int mode, int d, int p, const KernelArgs& a, hipStream_t s) {
-  // fast path: K = 4 and a single pass (G == P); every other shape takes the generic one
-  const bool fast = (a.K == 4) && (a.G == p);
+  // fast path: K = 4 and a single pass (G == P); every other shape, and a step with
+  // taps, takes the generic one
+  const bool fast = (a.K == 4) && (a.G == p) && !a.taps;
   if (d == 128) return p == 2 ? launch_step_p<128, 2>(mode, fast, a, s) : launch_step_p<128, 1>(mode, fast, a, s);
   if (d == 64) return p == 2 ? launch_step_p<64, 2>(mode, fast, a, s) : launch_step_p<64, 1>(mode, fast, a, s);
   return p == 2 ? launch_step_p<32, 2>(mode, fast, a, s) : launch_step_p<32, 1>(mode, fast, a, s);

@@ -84,12 +84,13 @@ def library():
         lib.gdn_decode_layer.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.gdn_sequence.argtypes = [S, I32] + [P] * 12 + [ctypes.c_size_t, P]
         lib.gdn_decode_layer_pooled.argtypes = [S, I32] + [P] * 13
+        lib.gdn_decode_layer_debug.argtypes = [S] + [P] * 17
         lib.gdn_decode_verify.argtypes = [S, I32] + [P] * 12 + [ctypes.c_size_t, P]
         lib.gdn_decode_commit.argtypes = [S, I32] + [P] * 5 + [ctypes.c_size_t, P]
         lib.gdn_in_proj.argtypes = [S, I32] + [P] * 10
         lib.gdn_out_proj.argtypes = [S, I32] + [P] * 4
         for f in (lib.gdn_conv_update, lib.gdn_recurrent_step, lib.gdn_decode_layer, lib.gdn_sequence,
-                  lib.gdn_decode_layer_pooled, lib.gdn_decode_verify, lib.gdn_decode_commit, lib.gdn_in_proj,
+                  lib.gdn_decode_layer_pooled, lib.gdn_decode_layer_debug, lib.gdn_decode_verify, lib.gdn_decode_commit, lib.gdn_in_proj,
                   lib.gdn_out_proj):
             f.restype = I32
         for f in (lib.gdn_sequence_workspace_bytes, lib.gdn_verify_trail_bytes):
@@ -188,6 +189,27 @@ def gdn_decode_layer(shape: GdnShape, conv1d_state, state, qkv, conv1d_weight, d
         _p(dt_bias, "dt_bias", torch.float32, Hv), _p(norm_weight, "norm_weight", torch.float32, dv),
         _p(out, "out", od, B * Hv * dv), _stream(stream))
     return _done(st, "gdn_decode_layer", check)
+
+
+def gdn_decode_layer_debug(shape: GdnShape, conv1d_state, state, qkv, conv1d_weight, dt_raw, b_raw, z, A_log,
+                           dt_bias, norm_weight, out, qkv_act=None, alpha=None, beta=None, y=None, y_norm=None,
+                           stream=None, check=True) -> int:
+    """gdn_decode_layer plus optional fp32 taps (each None or a GPU tensor): qkv_act
+    [B][C], alpha and beta [B][H_v], y and y_norm [B][H_v*d_v]."""
+    s = shape
+    act, od = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
+    B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
+    f32 = torch.float32
+    st = library().gdn_decode_layer_debug(
+        ctypes.byref(s), _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
+        _p(state, "state", f32, B * Hv * dk * dv), _p(qkv, "qkv", act, B * C),
+        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(dt_raw, "dt_raw", act, B * Hv),
+        _p(b_raw, "b_raw", act, B * Hv), _p(z, "z", act, B * Hv * dv), _p(A_log, "A_log", f32, Hv),
+        _p(dt_bias, "dt_bias", f32, Hv), _p(norm_weight, "norm_weight", f32, dv),
+        _p(out, "out", od, B * Hv * dv), _p(qkv_act, "qkv_act", f32, B * C), _p(alpha, "alpha", f32, B * Hv),
+        _p(beta, "beta", f32, B * Hv), _p(y, "y", f32, B * Hv * dv), _p(y_norm, "y_norm", f32, B * Hv * dv),
+        _stream(stream))
+    return _done(st, "gdn_decode_layer_debug", check)
 
 
 def gdn_decode_layer_pooled(shape: GdnShape, slots, conv1d_state_pool, state_pool, qkv, conv1d_weight, dt_raw,

@@ -120,6 +120,27 @@ gdn_status_t gdn_decode_layer(const gdn_shape_t* shape, void* conv1d_state, floa
                               const float* dt_bias, const float* norm_weight, void* out,
                               void* stream);
 
+/* gdn_decode_layer with intermediate taps, for staged debugging: the same step (states
+ * updated in place, out written), plus the intermediates that the page
+ * "linear_attention.rs" can dump after its optional stream synchronisation (the
+ * intra-layer dump at the end of forward_linear_attention: the smoothed qkv, the gates,
+ * y and y_norm). Every tap is optional (NULL: not written), fp32, device, and must not
+ * overlap another buffer:
+ *   qkv_act_tap [B][C]          q and k after the L2 norms, v after SiLU (step 3)
+ *   alpha_tap, beta_tap [B][H_v] the gates of steps 4-5
+ *   y_tap      [B][H_v][d_v]    the readout y = S q / sqrt(d_k) (step 7)
+ *   y_norm_tap [B][H_v][d_v]    y / sqrt(mean y^2 + rms_eps) * norm_weight (step 8,
+ *                               before the silu(z) gate of steps 9-11)
+ * y_tap and y_norm_tap must be 16-byte aligned, the others 4-byte. The step runs on the
+ * shape-generic kernel (slower than gdn_decode_layer; for tests and debugging), with
+ * the same validation and errors as gdn_decode_layer. */
+gdn_status_t gdn_decode_layer_debug(const gdn_shape_t* shape, void* conv1d_state, float* state,
+                                    const void* qkv, const void* conv1d_weight, const void* dt_raw,
+                                    const void* b_raw, const void* z, const float* A_log,
+                                    const float* dt_bias, const float* norm_weight, void* out,
+                                    float* qkv_act_tap, float* alpha_tap, float* beta_tap,
+                                    float* y_tap, float* y_norm_tap, void* stream);
+
 /* gdn_decode_layer for a batch whose states live in a pool (continuous batching).
  * For callers that keep one state slot per live sequence and run a changing subset
  * of them each step. Sequence b of the batch (its qkv, dt_raw, b_raw and z rows, and

@@ -304,3 +304,29 @@ def test_projection_validation():
     q = f()
     assert call_out_proj(s, 2048, gated=q, y=q) == ALIAS
     assert call_in_proj(qwen(batch=65535 * 32 + 1), 2048) == SHAPE
+
+
+def call_debug(shape, **override):
+    f = Fake()
+    names = ["conv1d_state", "state", "qkv", "conv1d_weight", "dt_raw", "b_raw", "z", "A_log", "dt_bias",
+             "norm_weight", "out", "qkv_act", "alpha", "beta", "y", "y_norm"]
+    args = {n: f() for n in names}
+    args.update(override)
+    return gdn.library().gdn_decode_layer_debug(ctypes.byref(shape), *[args[n] for n in names], None)
+
+
+def test_debug_taps_validation():
+    """gdn_decode_layer_debug: the decode step's checks, plus its optional taps: a null
+    tap is allowed, a misaligned y / y_norm tap or a tap overlapping another buffer is
+    rejected before any launch."""
+    s = qwen()
+    f = Fake()
+    assert call_debug(s, state=None) == NULL
+    assert call_debug(s, y=ctypes.c_void_p(f().value + 4)) == ALIGN
+    assert call_debug(s, y_norm=ctypes.c_void_p(f().value + 8)) == ALIGN
+    out = f()
+    assert call_debug(s, out=out, y=out) == ALIAS
+    assert call_debug(s, alpha=ctypes.c_void_p(f().value + 2)) == ALIGN
+    assert call_debug(qwen(batch=0), **{n: None for n in ["conv1d_state", "state", "qkv", "out", "y"]}) == OK
+    if NO_GPU:  # every tap null: validation passes and the (fake) launch fails
+        assert call_debug(s, qkv_act=None, alpha=None, beta=None, y=None, y_norm=None) == HIP
