@@ -865,16 +865,30 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
             for (int jt = 0; jt < 2; ++jt) oacc[lt][jt] = mfma32x3(ph, pl, dh[jt], dl[jt], oacc[lt][jt]);
           }
         }
-        // sums of O^2 over the wave's 32 columns, per row
+        // sums of O^2 over the wave's 32 columns, per row: the lane's 8 rows (i = 4 lt + r)
+        // are summed over the 16 lanes of its row group as one transposed reduction; each
+        // exchange halves the values a lane carries, and lane c16 ends with the total of
+        // row i = c16 >> 1
+        {
+          float v8[8];
 #pragma unroll
-        for (int lt = 0; lt < 2; ++lt)
+          for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float v = oacc[lt][0][r] * oacc[lt][0][r];
-            v = fmaf(oacc[lt][1][r], oacc[lt][1][r], v);
-            v = row16_sum(v);
-            if (c16 == 0) sm.rsum[16 * lt + 4 * q + r][w] = v;
-          }
+            for (int r = 0; r < 4; ++r)
+              v8[4 * lt + r] = fmaf(oacc[lt][1][r], oacc[lt][1][r], oacc[lt][0][r] * oacc[lt][0][r]);
+          const bool b3 = (c16 & 8) != 0, b2 = (c16 & 4) != 0, b1 = (c16 & 2) != 0;
+          float v4[4], v2[2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)  // lanes c16 and c16 ^ 8 (row rotate by 8)
+            v4[i] = (b3 ? v8[i + 4] : v8[i]) + dpp<0x128>(b3 ? v8[i] : v8[i + 4]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i)  // lanes c16 and 7 - c16 of each half row (half-row mirror)
+            v2[i] = (b2 ? v4[i + 2] : v4[i]) + dpp<0x141>(b2 ? v4[i] : v4[i + 2]);
+          float v1 = (b1 ? v2[1] : v2[0]) + dpp<0x4E>(b1 ? v2[0] : v2[1]);  // lanes c16 ^ 2
+          v1 += dpp<0xB1>(v1);                                                 // lanes c16 ^ 1
+          const int i = c16 >> 1;
+          if ((c16 & 1) == 0) sm.rsum[16 * (i >> 2) + 4 * q + (i & 3)][w] = v1;
+        }
         // H = gamma_C H + K^T diag(exp(g_C - g)) Delta
         {
           const float gamC = op.gam[kC - 1];
