@@ -7,17 +7,20 @@ the Qwen3.5-style layer (H_k = 16, H_v = 32, d_k = d_v = 128, K = 4, bf16 activa
 fp32 state) at B = 512: its 1 GiB of state exceeds the 256 MB Infinity Cache, so the
 bandwidth figure is a cold-HBM one. 32 distinct steps of inputs are drawn and reused
 cyclically; the state keeps evolving. B = 1 and B = 64 are reported in "sweep" (each
-step called from the host, and 64 steps captured in one HIP graph and replayed), the
-B = 8 x T = 4096 multi-token call in "sequence", speculative verification (B = 64,
-4 draft tokens) in "verify", the projections around the layer in "proj".
+step called from the host, 64 steps captured in one HIP graph and replayed, and for
+B = 64 single steps with the caches flushed), the B = 8 x T = 4096 multi-token call in
+"sequence", speculative verification (B = 64, 4 draft tokens) in "verify", the
+projections around the layer in "proj"; each leg carries a roofline block. The
+bandwidth reference is the benchmark's own streaming copy (libgdn_bench.so), and
+"cpu_baseline" times the fp64 oracle on the host cores beside each leg.
 
 Prints one JSON line. `value` = sequences x steps / second (seq-layer steps/s).
 The roofline figure uses algorithmic bytes (state read once and written once, every
 input read once, output written once) over the kernel's average duration, timed
 with HIP events on the stream the kernel is launched on.
 
-    python bench.py [--steps K] [--warmup W]
-    python bench.py --copy-calibration     # plain copy of known size (PMC scaling)
+    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
+    python bench.py --copy-calibration     # streaming copy of known size (PMC scaling)
     python bench.py --summarize DIR        # summarise rocprofv3 CSV output in DIR
 """
 
