@@ -441,7 +441,7 @@ gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_stat
   const bool chunked = gdn::chunked_supported(d, a.K) && T >= chunked_min_tokens(static_cast<long>(z.B) * z.Hv);
   (void)hipGetLastError();
   if (chunked) return launched(gdn::launch_chunked_sequence(a, s));
-  if (G <= 2 && a.K == 4) return launched(gdn::launch_sequence(d, G, a, s));
+  if (gdn::sequence_supported(G, a.K)) return launched(gdn::launch_sequence(d, G, a, s));
   // Shapes whose state or taps do not stay resident: one fused step launch per token.
   const size_t ea = z.ea, eo = z.eo;
   for (int32_t t = 0; t < T; ++t) {

@@ -56,8 +56,9 @@ enum Mode : int { kModeConv = 0, kModeRec = 1, kModeFused = 2 };
 // d: head dim (d_k == d_v); p: v-heads per pass (1 or 2). Grid = B * Hk workgroups.
 bool step_supported(int d, int p);
 hipError_t launch_step(int mode, int d, int p, const KernelArgs& a, hipStream_t stream);
-// Multi-token kernel that keeps the state on chip for all T tokens; needs G == p
-// and K == 4.
+// Multi-token kernel that keeps the state on chip for all T tokens, every v-head of a
+// k-head resident (p == G); sequence_supported(G, K): 1 <= G <= 4 and 2 <= K <= 5.
+bool sequence_supported(int G, int K);
 hipError_t launch_sequence(int d, int p, const KernelArgs& a, hipStream_t stream);
 // Chunked multi-token form on MFMA (gdn_chunked.hip): d == 128, K == 4, any G. One
 // workgroup per (sequence, v-head); enqueues the chunk kernel and the conv-state tail.

@@ -546,15 +546,35 @@ hipError_t launch_step_p(int mode, bool fast, const KernelArgs& a, hipStream_t s
   return a.act_bf16 ? launch_step_d<D, P, true>(mode, fast, a, s) : launch_step_d<D, P, false>(mode, fast, a, s);
 }
 
-template <int D, int P>
-hipError_t launch_seq_t(const KernelArgs& a, hipStream_t s) {
+template <int D, int P, int KT>
+void launch_seq_k(const KernelArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hk));
   const dim3 block(Layout<D, P>::NT);
   if (a.act_bf16)
-    gdn_seq_kernel<D, P, true, 4><<<grid, block, 0, s>>>(a);
+    gdn_seq_kernel<D, P, true, KT><<<grid, block, 0, s>>>(a);
   else
-    gdn_seq_kernel<D, P, false, 4><<<grid, block, 0, s>>>(a);
+    gdn_seq_kernel<D, P, false, KT><<<grid, block, 0, s>>>(a);
+}
+
+template <int D, int P>
+hipError_t launch_seq_t(const KernelArgs& a, hipStream_t s) {
+  switch (a.K) {
+    case 2: launch_seq_k<D, P, 2>(a, s); break;
+    case 3: launch_seq_k<D, P, 3>(a, s); break;
+    case 5: launch_seq_k<D, P, 5>(a, s); break;
+    default: launch_seq_k<D, P, 4>(a, s); break;
+  }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_seq_g(int p, const KernelArgs& a, hipStream_t s) {
+  switch (p) {
+    case 1: return launch_seq_t<D, 1>(a, s);
+    case 2: return launch_seq_t<D, 2>(a, s);
+    case 3: return launch_seq_t<D, 3>(a, s);
+    default: return launch_seq_t<D, 4>(a, s);
+  }
 }
 
 }  // namespace
@@ -570,10 +590,12 @@ hipError_t launch_step(int mode, int d, int p, const KernelArgs& a, hipStream_t 
   return p == 2 ? launch_step_p<32, 2>(mode, fast, a, s) : launch_step_p<32, 1>(mode, fast, a, s);
 }
 
+bool sequence_supported(int G, int K) { return G >= 1 && G <= 4 && K >= 2 && K <= 5; }
+
 hipError_t launch_sequence(int d, int p, const KernelArgs& a, hipStream_t s) {
-  if (d == 128) return p == 2 ? launch_seq_t<128, 2>(a, s) : launch_seq_t<128, 1>(a, s);
-  if (d == 64) return p == 2 ? launch_seq_t<64, 2>(a, s) : launch_seq_t<64, 1>(a, s);
-  return p == 2 ? launch_seq_t<32, 2>(a, s) : launch_seq_t<32, 1>(a, s);
+  if (d == 128) return launch_seq_g<128>(p, a, s);
+  if (d == 64) return launch_seq_g<64>(p, a, s);
+  return launch_seq_g<32>(p, a, s);
 }
 
 }  // namespace gdn

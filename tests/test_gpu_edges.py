@@ -41,6 +41,8 @@ SHAPES = [
     ("G1_d32_K5_f32", 2, 3, 3, 32, 5, "f32"),
     ("G2_d128_f32_acts", 2, 2, 4, 128, 4, "f32"),
     ("G2_d128_ragged_B17", 17, 2, 4, 128, 4, "bf16"),
+    # beyond the resident-state sequence kernel (G > 4, K > 5): one step launch per token
+    ("G8_d32_K6_f32", 2, 1, 8, 32, 6, "f32"),
 ]
 
 
