@@ -372,14 +372,12 @@ hipError_t launch_skinny_m(ProjArgs& p, long ntiles, int cus, hipStream_t st) {
 // ----------------------------------------------------------------------------------
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-// NI DMA instructions of a stage: 16 bytes per lane from src[i] + off into 1 KB blocks
-// of LDS at dst + 512 i elements (a device function: the builtin has no host form)
-template <int NI>
-__device__ __forceinline__ void pipe_issue(const uint16_t* const (&src)[NI], long off, uint16_t* dst) {
-#pragma unroll
-  for (int i = 0; i < NI; ++i) __builtin_amdgcn_global_load_lds(src[i] + off, dst + 512 * i, 16, 0, 0);
+// One DMA instruction: 16 bytes per lane from src into 1 KB of consecutive LDS at dst. A
+// plain device function: the builtin has no host form, and a kernel that names it
+// directly (or through a lambda or a function template) can lose its host launch stub.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
-
 template <int BM, int BN, int S, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) {
   constexpr int NW = WM * WN;           // waves
@@ -404,7 +402,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
   const ProjSeg s = p.seg[si];
   const long n0 = static_cast<long>(nt - s.tile0) * BN;
   const long m0 = static_cast<long>(k % nmb) * BM;
-  const int K = p.K;
+  const int K = p.K, nk = K / 64;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
   const int wm = w / WN, wn = w % WN;
 
@@ -424,11 +422,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nk = K / 64;
-  auto issue = [&](int j) { pipe_issue<NI>(src, 64L * j, ring0 + (j % S) * (R * 64)); };
+  // the NI DMA instructions of stage j: 16 bytes per lane from src[i] + 64 j into the
+  // 1 KB blocks of this wave in ring slot j % S
 #pragma unroll
-  for (int i = 0; i < S - 1; ++i)
-    if (i < nk) issue(i);
+  for (int j = 0; j < S - 1; ++j)
+    if (j < nk)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        dma16(src[i] + 64L * j, ring0 + j * (R * 64) + 512 * i);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's DMA of stage kt has landed once at most the S - 2 later stages are
     // outstanding (the memory counter drains in issue order)
@@ -437,7 +438,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
     else
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();
-    if (kt + S - 1 < nk) issue(kt + S - 1);
+    if (kt + S - 1 < nk) {
+      const int j = kt + S - 1;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        dma16(src[i] + 64L * j, ring0 + (j % S) * (R * 64) + 512 * i);
+    }
     const uint16_t* st = &ring[kt % S][0][0];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -559,9 +565,6 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
   // weight-streaming and tiled paths. At 48 and 64 rows the split gave no gain over the
   // tiled kernel (13.3-13.5 us either way).
   if (p.M >= 3 && p.M <= 32 && rows <= 4096 && p.K % 512 == 0) return launch_skinny_m<1, 8>(p, (rows + 15) / 16, 256, st);
-  // 33..64 rows and many columns (the in_proj shape): one 64-row tile, so the weights
-  // stream once (32-row tiles read them twice); 19.8 against 21.6 us at 64 rows.
-  if (p.M > 32 && p.M <= 64 && rows >= 8192 && p.K % 256 == 0) return launch_mfma<64, 64, 256, 2, 2>(p, st);
   // weight streaming for one or two rows, and for up to 8 rows when there are too few
   // output columns to give the MFMA tiles a full grid (X rows within the default LDS
   // allowance of 64 KB)
@@ -572,9 +575,9 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
     if (mt == 4) return launch_gemv<4>(p, st);
     return launch_gemv<8>(p, st);
   }
-  // MFMA: the largest tile that still gives every CU a workgroup (the weight stream and
-  // the LDS reads per MFMA both favour large tiles; a grid below 256 workgroups leaves
-  // CUs idle), else 32 x 32 tiles with 256-deep stages for more bytes in flight
+  // MFMA tiles: large tiles need fewer weight and LDS bytes per MFMA, small ones give
+  // more workgroups; measured at hidden = 2048 and 12352 / 2048 output columns (in_proj /
+  // out_proj), each rule below takes the fastest tile of its range
   auto tiles = [&](int bm, int bn) {
     long n = 0;
     for (int i = 0; i < p.nseg; ++i) n += (p.seg[i].n + bn - 1) / bn;
@@ -584,11 +587,19 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
   // of LDS, one workgroup of two waves per SIMD per CU): 61.0 / 118.4 -> 47.8 / 95.6 us at
   // 512 / 1024 rows
   if (tiles(256, 128) >= 128) return launch_pipe<256, 128, 3, 4, 2>(p, st);
-  if (tiles(128, 128) >= 256) return launch_mfma<128, 128, 64, 2, 2>(p, st);
-  // 64 x 64 tiles: the DMA-fed ring of 4 stages (64 KB of LDS, two workgroups per CU).
-  // out_proj at 512 / 1024 rows: 44.4 / 50.4 -> 25.7 / 31.1 us; in_proj at 128 rows:
-  // 28.4 -> 23.9 us. (A 128 x 128 ring needs 128 KB, one workgroup per CU, and lost to
-  // the register-staged kernel above.)
+  // 128 x 128 tiles of 4 waves on a 4-stage ring (128 KB) when they still give 192
+  // workgroups and their row blocks pad no more rows than 64-row blocks would: in_proj at
+  // 256 rows 28.9 -> 26.6 us (at 160 rows, half a block of padding, 25.2 -> 26.2)
+  if (tiles(128, 128) >= 192 && (p.M + 127) / 128 * 2 == (p.M + 63) / 64) return launch_pipe<128, 128, 4>(p, st);
+  // otherwise the largest of the 64 x 64, 32 x 64 and 32 x 32 rings (4 waves, 4 stages of
+  // 64 / 48 / 32 KB) that gives at least 384 workgroups, so that the CUs whose tiles come
+  // first are not the only ones streaming. in_proj at 4 / 16 / 64 rows: 12.2 / 12.2 /
+  // 17.6 -> 10.9 / 11.1 / 14.3 us; out_proj at 256 / 320 / 384 rows: 23.5 / 32.7 / 33.1
+  // -> 17.1 / 19.1 / 19.6 us (hidden = 2048)
+  if (tiles(64, 64) >= 384) return launch_pipe<64, 64, 4>(p, st);
+  if (tiles(32, 64) >= 384) return launch_pipe<32, 64, 4>(p, st);
+  if (tiles(32, 32) >= 384) return launch_pipe<32, 32, 4>(p, st);
+  // 64 x 64 ring with a full grid
   if (tiles(64, 64) >= 256) return launch_pipe<64, 64, 4>(p, st);
   // 32 x 32 tiles: 64-deep stages keep 8 workgroups per CU resident when the grid is
   // large; a small grid needs the deeper stages for bytes in flight

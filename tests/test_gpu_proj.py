@@ -10,13 +10,15 @@ Tolerance: the kernels accumulate in fp32 and round once to the output dtype.
   error of order sqrt(K) 2^-24, a few 1e-7.
 Shapes cover every kernel: weight streaming (B <= 8, or B <= 2), the skinny MFMA
 kernel (3..32 rows, few output columns: out_proj at B = 3 and 20, in_proj at hidden
-512), 64 x 64 tiles for 33..64 rows (in_proj at B = 40 and 64), 32 x 32 tiles (B = 100),
-the DMA-fed 64 x 64 ring (in_proj at B = 128, out_proj at B = 512, 600 and 1024, the
-600 with a ragged last row tile) and the 256 x 128 ring (in_proj at B = 512, 600 and
-1024); ragged row and column tiles (the H_v-wide a/b segments are narrower than a tile)
-and the Qwen3.5-style sizes. The ring kernels store their tiles in 16-byte pieces; a
-segment whose width is not a multiple of 8 bf16 values (the a/b segments of the H_v = 20
-layer at B = 1024) is stored element by element.
+512), the register-staged 32 x 32 tiles (out_proj at B = 9 to 128, in_proj at B = 100),
+and the DMA-fed rings: 32 x 32 (in_proj at B = 3 and 20, out_proj at B = 200), 32 x 64
+(in_proj at B = 40 and 64, out_proj at B = 512 and 600, the 40 and 600 with a ragged
+last row tile), 64 x 64 (in_proj at B = 128, out_proj at B = 1024), 128 x 128 (in_proj
+at B = 200, ragged) and 256 x 128 (in_proj at B = 512, 600 and 1024); ragged row and
+column tiles (the H_v-wide a/b segments are narrower than a tile) and the Qwen3.5-style
+sizes. The ring kernels store their tiles in 16-byte pieces; a segment whose width is
+not a multiple of 8 bf16 values (the a/b segments of the H_v = 20 layer at B = 1024) is
+stored element by element.
 """
 
 import numpy as np
@@ -69,11 +71,12 @@ CASES = [
     (64, 16, 32, 128, 2048, None),
     (100, 2, 6, 64, 256, None),
     (128, 16, 32, 128, 2048, [0, 1, 15, 63, 64, 100, 127]),
+    (200, 16, 32, 128, 2048, [0, 1, 127, 128, 150, 199]),
     (600, 16, 32, 128, 2048, [0, 63, 64, 511, 512, 575, 576, 599]),
     (512, 16, 32, 128, 2048, [0, 1, 63, 64, 255, 300, 511]),
     (1024, 4, 20, 128, 2048, [0, 1, 255, 256, 511, 767, 1000, 1023]),
     # contractions of 1, 2 and 3 stages through the 256 x 128 ring (in_proj, hidden 64 /
-    # 128 / 192) and of 1..4 stages through the 64 x 64 ring (out_proj, H_v d_v = 64 ..
+    # 128 / 192) and of 1..4 stages through the 32 x 64 ring (out_proj, H_v d_v = 64 ..
     # 256): the prologue issues fewer stages than the ring holds and every stage is a tail
     (512, 16, 32, 128, 64, [0, 255, 256, 511]),
     (512, 16, 32, 128, 128, [0, 300, 511]),
