@@ -288,27 +288,43 @@ __global__ __launch_bounds__(64 * KW) void gdn_proj_skinny(const ProjArgs p) {
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto mfma = [&](int sl) {
 #pragma unroll
-  for (int i = 0; i < D; ++i)
-    if (i < nkb) load(i, i);
-  // k-block kb sits in register slot kb % D; unrolled by D so that slots are constants
-  for (int kb0 = 0; kb0 < nkb; kb0 += D) {
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[sl][i][e]),
+                                                              __builtin_bit_cast(bf16x8, wb[sl][j][e]), acc[i][j], 0, 0, 0);
+  };
+  // the first D k-blocks (clamped to the last one when the slice is shorter, so that
+  // every slot is loaded and the memory counter is the same on every path into the loop)
+#pragma unroll
+  for (int i = 0; i < D; ++i) load(min(i, nkb - 1), i);
+  // k-block kb sits in register slot kb % D; unrolled by D so that slots are constants.
+  // The steady state reloads every slot unconditionally: a conditional load there makes
+  // the compiler rotate the slots through copies at the loop edge, which first waits for
+  // every load in flight.
+  int kb0 = 0;
+  for (; kb0 + 2 * D <= nkb; kb0 += D) {
 #pragma unroll
     for (int sl = 0; sl < D; ++sl) {
-      const int kb = kb0 + sl;
-      if (kb >= nkb) break;
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[sl][i][e]),
-                                                                __builtin_bit_cast(bf16x8, wb[sl][j][e]), acc[i][j], 0, 0,
-                                                                0);
-      if (kb + D < nkb) load(kb + D, sl);
+      mfma(sl);
+      load(kb0 + sl + D, sl);
     }
   }
+  // the last 2D - 1 or fewer k-blocks
+#pragma unroll
+  for (int sl = 0; sl < D; ++sl) {
+    if (kb0 + sl < nkb) {
+      mfma(sl);
+      if (kb0 + sl + D < nkb) load(kb0 + sl + D, sl);
+    }
+  }
+#pragma unroll
+  for (int sl = 0; sl < D; ++sl)
+    if (kb0 + D + sl < nkb) mfma(sl);
   // accumulator tile (i, j): lane holds rows 16 i + 4 q + r, column 16 j + c16
 #pragma unroll
   for (int i = 0; i < TI; ++i)
