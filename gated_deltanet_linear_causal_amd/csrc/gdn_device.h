@@ -245,11 +245,9 @@ struct Layout {
 // State pass of one v-head for a lane: m = H^T k, p = H^T q (reduced over the row
 // groups), delta = beta (v - alpha m), H <- alpha H + k delta^T (stored when STORE),
 // and returns o = H'^T q / sqrt(D) = (alpha p + (k.q) delta) / sqrt(D) for the lane's
-// 4 columns. FORM 0 is the decode kernels' step. FORM 1 and 2 write the readout out with
-// fmaf, so that both round it the same way, and FORM 2 leaves hreg as it is (a last
-// token whose state is not needed).
+// 4 columns.
 // ----------------------------------------------------------------------------------
-template <int D, int P, bool STORE, bool STREAM, int R, int FORM = 0>
+template <int D, int P, bool STORE, bool STREAM, int R>
 __device__ __forceinline__ float4 delta_rule(float4 (&hreg)[R], const float* kr, const float* qr, float4 v4,
                                              float alpha, float beta, float kq, __amdgpu_buffer_rsrc_t srs,
                                              uint32_t voff, uint32_t soff, float4* delta_out = nullptr) {
@@ -280,14 +278,6 @@ __device__ __forceinline__ float4 delta_rule(float4 (&hreg)[R], const float* kr,
   xor_round<32>(m, pq);
   const float4 delta = beta * (v4 - alpha * m);
   if (delta_out) *delta_out = delta;
-  float4 o = f4(0.0f);
-  if constexpr (FORM != 0) {
-    const float4 ap = alpha * pq;
-    o = (1.0f / sqrtf(static_cast<float>(D))) *
-        make_float4(fmaf(kq, delta.x, ap.x), fmaf(kq, delta.y, ap.y), fmaf(kq, delta.z, ap.z),
-                    fmaf(kq, delta.w, ap.w));
-  }
-  if constexpr (FORM == 2) return o;
   // keep k out of registers across the shuffles: re-read it from LDS
   __asm__ volatile("" ::: "memory");
 #pragma unroll
@@ -304,8 +294,7 @@ __device__ __forceinline__ float4 delta_rule(float4 (&hreg)[R], const float* kr,
       if constexpr (STORE) buf_store4<STREAM>(srs, voff, soff + (4 * k4 + e) * kRowBytes, h);
     }
   }
-  if constexpr (FORM == 0) return (1.0f / sqrtf(static_cast<float>(D))) * (alpha * pq + kq * delta);
-  return o;
+  return (1.0f / sqrtf(static_cast<float>(D))) * (alpha * pq + kq * delta);
 }
 
 // Step 8 for one head: 1/sqrt(mean o^2 + eps) over the head's D columns (lanes with

@@ -14,10 +14,19 @@ namespace {
 // would give after the previous draft tokens, and the trail of the token's update
 // H <- alpha H + k delta^T (delta, unit k, alpha), from which gdn_commit_kernel
 // rebuilds the state after any accepted prefix.
-// Only the delta rule depends on the previous token, so the kernel runs in three
-// phases: (A) conv, gates and L2 norms of all T tokens at once (one block reduction),
-// (B) the T delta-rule steps on the VGPR-resident state with no barrier between them,
-// (C) the per-head RMSNorm and the outputs of all T tokens (one block reduction).
+// The states are not written, so the state after each draft token is never formed:
+// with H0 the state before the draft and G(i, j) = alpha_i ... alpha_j (1 when i > j),
+// the rule H_t = alpha_t H_{t-1} + k_t delta_t^T unrolls to
+//   m_t = H_{t-1}^T k_t = G(0, t-1) H0^T k_t + sum_{s<t} G(s+1, t-1) (k_s . k_t) delta_s,
+//   delta_t = beta_t (v_t - alpha_t m_t),
+//   o_t = H_t^T q_t / sqrt(d) = (G(0, t) H0^T q_t + sum_{s<=t} G(s+1, t) (k_s . q_t) delta_s) / sqrt(d),
+// so one pass over H0 gives every token's H0^T k_t and H0^T q_t (two matrix-vector
+// products per token instead of two plus the rank-one update), and the rest is the
+// T x T products k_s . k_t, k_s . q_t and the decay products. Phases: (A) conv, gates
+// and L2 norms of all T tokens (one block reduction), then the T^2 token products;
+// (B) per token, H0^T k_t and H0^T q_t on the VGPR-resident state, reduced over the
+// row groups, then delta_t and o_t; (C) the per-head RMSNorm and the outputs of all T
+// tokens (one block reduction).
 // ----------------------------------------------------------------------------------
 // d = 128 uses 16 state rows per lane (4 waves per head, 64 state VGPRs): the per-token
 // work per lane halves and more workgroups stay resident.
@@ -33,15 +42,32 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   constexpr int kRows = kMaxConvTaps - 1 + kTM;
   constexpr uint32_t kRowBytes = D * 4;
   using raw_t = typename Act<BF>::raw_t;  // stored values, widened on use
-  __shared__ __attribute__((aligned(16))) raw_t s_x[kRows][NCH];  // K-1 conv-state rows, then T token rows
-  __shared__ __attribute__((aligned(16))) raw_t s_w[NCH * kMaxConvTaps];  // taps [NCH][K]
+  // The conv inputs and taps are dead once the conv has run; the reduced state products
+  // of phase B reuse their storage.
+  union Reused {
+    struct {
+      raw_t x[kRows][NCH];            // K-1 conv-state rows, then T token rows
+      raw_t w[NCH * kMaxConvTaps];    // taps [NCH][K]
+    } conv;
+    struct {
+      float hk[kTM][D];               // H0^T k_t, reduced
+      float hq[kTM][D];               // H0^T q_t, reduced
+    } prod;
+  };
+  __shared__ __attribute__((aligned(16))) Reused reused;
+  auto& s_x = reused.conv.x;
+  auto& s_w = reused.conv.w;
+  auto& s_hk = reused.prod.hk;
+  auto& s_hq = reused.prod.hq;
   __shared__ __attribute__((aligned(16))) float s_q[kTM][D];
   __shared__ __attribute__((aligned(16))) float s_k[kTM][D];
   __shared__ __attribute__((aligned(16))) float s_v[kTM][D];
   __shared__ __attribute__((aligned(16))) float s_o[kTM][D];  // readouts, for the RMSNorm of phase C
   __shared__ __attribute__((aligned(16))) raw_t s_z[kTM][D];  // z rows of the tokens, staged in phase A
-  __shared__ float s_gate[3][kTM];      // alpha, beta, k.q per token
-  __shared__ float red[NW][3 * kTM];    // per-wave partial sums
+  __shared__ float s_gate[2][kTM];      // alpha, beta per token
+  __shared__ float s_kk[kTM][kTM];      // [t][s]: k_s . k_t for s < t (unit vectors)
+  __shared__ float s_kq[kTM][kTM];      // [t][s]: k_s . q_t for s <= t
+  __shared__ float red[NW][2 * kTM];    // per-wave partial sums
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int bh = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x));  // (b, h), uniform
@@ -176,40 +202,37 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
     }
   }
   __syncthreads();
-  // L2 norms of q and k and their dot product, all tokens in one reduction
-  float s3[3 * kTM];
+  // L2 norms of q and k, all tokens in one reduction
+  float s2n[2 * kTM];
 #pragma unroll
-  for (int i = 0; i < 3 * kTM; ++i) s3[i] = 0.0f;
+  for (int i = 0; i < 2 * kTM; ++i) s2n[i] = 0.0f;
   for (int i = t; i < D; i += NT)
 #pragma unroll
     for (int tok = 0; tok < kTM; ++tok)
       if (tok < T) {
         const float q = s_q[tok][i], k = s_k[tok][i];
-        s3[3 * tok] = fmaf(q, q, s3[3 * tok]);
-        s3[3 * tok + 1] = fmaf(k, k, s3[3 * tok + 1]);
-        s3[3 * tok + 2] = fmaf(q, k, s3[3 * tok + 2]);
+        s2n[2 * tok] = fmaf(q, q, s2n[2 * tok]);
+        s2n[2 * tok + 1] = fmaf(k, k, s2n[2 * tok + 1]);
       }
   {
-    float s6[3 * kTM / 4];  // row r holds sum j + 6 (r & 1) + 12 (r >> 1) in register j
-    wave_sums_t<3 * kTM>(s3, s6);
+    float s4[2 * kTM / 4];  // row r holds sum j + 4 (r & 1) + 8 (r >> 1) in register j
+    wave_sums_t<2 * kTM>(s2n, s4);
     if ((lane & 15) == 0) {
       const int r = lane >> 4;
 #pragma unroll
-      for (int j = 0; j < 3 * kTM / 4; ++j) red[wv][j + (3 * kTM / 4) * (r & 1) + (3 * kTM / 2) * (r >> 1)] = s6[j];
+      for (int j = 0; j < 2 * kTM / 4; ++j) red[wv][j + (2 * kTM / 4) * (r & 1) + (2 * kTM / 2) * (r >> 1)] = s4[j];
     }
   }
   __syncthreads();
   const long bt0 = static_cast<long>(b) * T;
   for (int tok = 0; tok < T; ++tok) {
-    float sq = 0.0f, sk = 0.0f, sqk = 0.0f;
+    float sq = 0.0f, sk = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      sq += red[w][3 * tok];
-      sk += red[w][3 * tok + 1];
-      sqk += red[w][3 * tok + 2];
+      sq += red[w][2 * tok];
+      sk += red[w][2 * tok + 1];
     }
     const float rq = __builtin_amdgcn_rsqf(sq + a.l2_eps), rk = __builtin_amdgcn_rsqf(sk + a.l2_eps);
-    if (t == 0) s_gate[2][tok] = sqk * rq * rk;
     // elements 0..D-1 scale q, D..2D-1 scale k (and record it in the trail)
     for (int i = t; i < 2 * D; i += NT) {
       if (i < D) {
@@ -223,23 +246,103 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   }
   __syncthreads();
 
-  // ---- B. the T delta-rule steps (no barrier: each lane reads LDS written above). The
-  // state after the last token is not needed here (commit rebuilds it from the trail),
-  // so the last step only forms delta and the readout.
-  auto step = [&](int tok, auto form) {
-    const float alpha = s_gate[0][tok], beta = s_gate[1][tok];
-    const float4 v4 = *reinterpret_cast<const float4*>(&s_v[tok][4 * cg]);
-    float4 delta;
-    const float4 ot = delta_rule<D, 1, false, false, R, decltype(form)::value>(
-        hreg, &s_k[tok][rg * R], &s_q[tok][rg * R], v4, alpha, beta, s_gate[2][tok], srs, voff, 0, &delta);
-    if (rg == 0) {
-      *reinterpret_cast<float4*>(&s_o[tok][4 * cg]) = ot;
-      *reinterpret_cast<float4*>(a.trail_delta + ((bt0 + tok) * a.Hv + h) * D + 4 * cg) = delta;
+  // The T^2 products of the unit vectors: pair p = i T + j is k_j . k_i for j < i and
+  // k_i . q_j for j >= i. 16 pairs per wave and pass, 4 lanes per pair, each lane D / 4
+  // consecutive elements, then a sum over the 4 lanes.
+  {
+    constexpr int EPL = D / 4;
+    const int sub = lane >> 2, part = lane & 3;
+    for (int p0 = 0; p0 < T * T; p0 += 16 * NW) {
+      const int p = p0 + 16 * wv + sub;
+      const bool live = p < T * T;
+      const int pi = live ? p / T : 0, pj = live ? p - pi * T : 0;
+      const bool kk = pj < pi;
+      const float* x = &s_k[kk ? pj : pi][part * EPL];
+      const float* y = kk ? &s_k[pi][part * EPL] : &s_q[pj][part * EPL];
+      float acc = 0.0f;
+      // two pieces of each vector in flight: the state is live in registers here
+#pragma unroll 2
+      for (int e = 0; e < EPL; e += 4) {
+        const float4 xv = *reinterpret_cast<const float4*>(x + e), yv = *reinterpret_cast<const float4*>(y + e);
+        acc = fmaf(xv.x, yv.x, acc);
+        acc = fmaf(xv.y, yv.y, acc);
+        acc = fmaf(xv.z, yv.z, acc);
+        acc = fmaf(xv.w, yv.w, acc);
+      }
+      acc = xor_add<1>(acc);
+      acc = xor_add<2>(acc);
+      if (live && part == 0) {
+        if (kk)
+          s_kk[pi][pj] = acc;
+        else
+          s_kq[pj][pi] = acc;
+      }
     }
-    if (t == 0) a.trail_alpha[(bt0 + tok) * a.Hv + h] = alpha;
-  };
-  for (int tok = 0; tok + 1 < T; ++tok) step(tok, std::integral_constant<int, 1>{});
-  step(T - 1, std::integral_constant<int, 2>{});  // T >= 1
+  }
+  // (read in B2, after the barrier that ends B1)
+
+  // ---- B1. H0^T k_t and H0^T q_t of every token on the VGPR-resident state, reduced
+  // over the row groups (no barrier: each lane reads LDS written above)
+  for (int tok = 0; tok < T; ++tok) {
+    const float* kr = &s_k[tok][rg * R];
+    const float* qr = &s_q[tok][rg * R];
+    float4 m = f4(0.0f), pq = f4(0.0f);
+#pragma unroll
+    for (int k4 = 0; k4 < R / 4; ++k4) {
+      const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * k4);
+      const float4 qq = *reinterpret_cast<const float4*>(qr + 4 * k4);
+      m = fma4(hreg[4 * k4 + 0], kk.x, m);
+      m = fma4(hreg[4 * k4 + 1], kk.y, m);
+      m = fma4(hreg[4 * k4 + 2], kk.z, m);
+      m = fma4(hreg[4 * k4 + 3], kk.w, m);
+      pq = fma4(hreg[4 * k4 + 0], qq.x, pq);
+      pq = fma4(hreg[4 * k4 + 1], qq.y, pq);
+      pq = fma4(hreg[4 * k4 + 2], qq.z, pq);
+      pq = fma4(hreg[4 * k4 + 3], qq.w, pq);
+    }
+    // lanes l ^ CGL, l ^ 2 CGL, ... up to l ^ 32
+    if constexpr (CGL <= 1) xor_round<1>(m, pq);
+    if constexpr (CGL <= 2) xor_round<2>(m, pq);
+    if constexpr (CGL <= 4) xor_round<4>(m, pq);
+    if constexpr (CGL <= 8) xor_round<8>(m, pq);
+    if constexpr (CGL <= 16) xor_round<16>(m, pq);
+    xor_round<32>(m, pq);
+    if (rg == 0) {
+      *reinterpret_cast<float4*>(&s_hk[tok][4 * cg]) = m;
+      *reinterpret_cast<float4*>(&s_hq[tok][4 * cg]) = pq;
+    }
+  }
+  __syncthreads();
+
+  // ---- B2. delta_t and o_t, one thread per column c: dl holds the deltas so far,
+  // gs[s] = G(s+1, t-1) and g0 = G(0, t-1) before token t's gate is applied
+  if (t < D) {
+    const int c = t;
+    const float scale = 1.0f / sqrtf(static_cast<float>(D));
+    float dl[kTM], gs[kTM];
+    float g0 = 1.0f;
+#pragma unroll
+    for (int tok = 0; tok < kTM; ++tok) {
+      if (tok >= T) break;
+      const float alpha = s_gate[0][tok], beta = s_gate[1][tok];
+      float mt = g0 * s_hk[tok][c];
+#pragma unroll
+      for (int s = 0; s < tok; ++s) mt = fmaf(gs[s] * s_kk[tok][s], dl[s], mt);
+      const float delta = beta * (s_v[tok][c] - alpha * mt);
+      dl[tok] = delta;
+      g0 *= alpha;
+#pragma unroll
+      for (int s = 0; s < tok; ++s) gs[s] *= alpha;
+      gs[tok] = 1.0f;
+      float ot = g0 * s_hq[tok][c];
+#pragma unroll
+      for (int s = 0; s <= tok; ++s) ot = fmaf(gs[s] * s_kq[tok][s], dl[s], ot);
+      s_o[tok][c] = scale * ot;
+      a.trail_delta[((bt0 + tok) * a.Hv + h) * D + c] = delta;
+    }
+  }
+  if (t < T) a.trail_alpha[(bt0 + t) * a.Hv + h] = s_gate[0][t];
+  __syncthreads();
 
   // ---- C. per-head RMSNorm and gated outputs of all tokens
   float ss[kTM];
@@ -279,8 +382,8 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
 }
 
 // Commit of the accepted prefix: H <- alpha_t H + k_t delta_t^T for t < n = accepted[b]
-// (the expression delta_rule evaluates, so the result is bit-identical to the verify
-// kernel's state after n tokens). n outside [1, T] leaves the sequence untouched.
+// with the recorded deltas (those the verify kernel formed its outputs from). n
+// outside [1, T] leaves the sequence untouched.
 template <int D>
 __global__ __launch_bounds__((Layout<D, 1>::NT)) void gdn_commit_kernel(const KernelArgs a) {
   using L = Layout<D, 1>;

@@ -217,8 +217,9 @@ gdn_status_t gdn_decode_verify(const gdn_shape_t* shape, int32_t T, const void* 
 
 /* Advance each sequence b by its first n = accepted[b] draft tokens of the preceding
  * gdn_decode_verify call (same shape, T, qkv and trail): the state becomes the state
- * after those n tokens (bit-identical to the one the verify kernel computed) and the
- * conv state is rolled by n tokens (bit-exact copies of the draft's qkv rows).
+ * after those n tokens (the recorded updates H <- alpha_t H + k_t delta_t^T replayed in
+ * order, with the deltas verify formed its outputs from) and the conv state is rolled
+ * by n tokens (bit-exact copies of the draft's qkv rows).
  * accepted: [B] int32 (device). n = 0 leaves the sequence untouched, and so does a
  * value outside [0, T] (device data, not checked on the host). qkv and trail are read,
  * conv1d_state and state updated in place. */
