@@ -281,12 +281,14 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   }
   // (read in B2, after the barrier that ends B1)
 
-  // ---- B1. H0^T k_t and H0^T q_t of every token on the VGPR-resident state, reduced
-  // over the row groups (no barrier: each lane reads LDS written above)
-  for (int tok = 0; tok < T; ++tok) {
+  // ---- B1. H0^T k_t and H0^T q_t of every token on the VGPR-resident state, summed
+  // over the lane's rows (no barrier: each lane reads LDS written above), then over the
+  // row groups and stored to LDS
+  auto partial = [&](int tok, float4& m, float4& pq) {
     const float* kr = &s_k[tok][rg * R];
     const float* qr = &s_q[tok][rg * R];
-    float4 m = f4(0.0f), pq = f4(0.0f);
+    m = f4(0.0f);
+    pq = f4(0.0f);
 #pragma unroll
     for (int k4 = 0; k4 < R / 4; ++k4) {
       const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * k4);
@@ -300,7 +302,11 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
       pq = fma4(hreg[4 * k4 + 2], qq.z, pq);
       pq = fma4(hreg[4 * k4 + 3], qq.w, pq);
     }
-    // lanes l ^ CGL, l ^ 2 CGL, ... up to l ^ 32
+  };
+  // one token: each value summed over lanes l ^ CGL, l ^ 2 CGL, ... up to l ^ 32
+  auto single = [&](int tok) {
+    float4 m, pq;
+    partial(tok, m, pq);
     if constexpr (CGL <= 1) xor_round<1>(m, pq);
     if constexpr (CGL <= 2) xor_round<2>(m, pq);
     if constexpr (CGL <= 4) xor_round<4>(m, pq);
@@ -311,6 +317,43 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
       *reinterpret_cast<float4*>(&s_hk[tok][4 * cg]) = m;
       *reinterpret_cast<float4*>(&s_hq[tok][4 * cg]) = pq;
     }
+  };
+  if constexpr (CGL == 8) {
+    // Row groups are lane bits 3-5. Two tokens at a time, transposed: the 16 values
+    // (m, pq of token t0, then of t0 + 1) go through the 32-lane swaps (register i of
+    // the lower half-wave keeps value i, of the upper value i + 8), the 16-lane swaps
+    // (register j of row r holds value j + 4 (r & 1) + 8 (r >> 1)) and a DPP row_ror:8
+    // sum; lanes with bit 3 clear store their 4 values. An odd last token goes alone.
+    int t0 = 0;
+    for (; t0 + 1 < T; t0 += 2) {
+      float4 m0, p0, m1, p1;
+      partial(t0, m0, p0);
+      partial(t0 + 1, m1, p1);
+      float v[16] = {m0.x, m0.y, m0.z, m0.w, p0.x, p0.y, p0.z, p0.w, m1.x, m1.y, m1.z, m1.w, p1.x, p1.y, p1.z, p1.w};
+      float hh[8], qq[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float x0 = v[i], x1 = v[i + 8];
+        asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x0), "+v"(x1));
+        hh[i] = x0 + x1;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x0 = hh[j], x1 = hh[j + 4];
+        asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x0), "+v"(x1));
+        qq[j] = x0 + x1;
+        qq[j] += dpp_mov<0x128>(qq[j]);
+      }
+      const int r = lane >> 4, vb = 4 * (r & 1) + 8 * (r >> 1);  // value index of qq[0]
+      const int tok = vb < 8 ? t0 : t0 + 1;
+      if ((lane & 8) == 0) {
+        float* dst = (vb & 4) ? &s_hq[tok][4 * cg] : &s_hk[tok][4 * cg];
+        *reinterpret_cast<float4*>(dst) = make_float4(qq[0], qq[1], qq[2], qq[3]);
+      }
+    }
+    if (t0 < T) single(t0);
+  } else {
+    for (int tok = 0; tok < T; ++tok) single(tok);
   }
   __syncthreads();
 
