@@ -115,3 +115,46 @@ def sequence(H0, Q, K, V, la, beta, chunk, form="solve"):
         O, H = chunk_step(H, Q[t0:t1], K[t0:t1], V[t0:t1], la[t0:t1], beta[t0:t1], form)
         out[t0:t1] = O
     return out / np.sqrt(dk), H
+
+
+def decay_product(alpha, i, j):
+    """G(i, j) = alpha_i ... alpha_j, 1 when i > j."""
+    return float(np.prod(alpha[i:j + 1])) if i <= j else 1.0
+
+
+def draft_unrolled(H0, Q, K, V, alpha, beta, shift=1):
+    """T draft tokens of one head evaluated from the state before them, H0, without
+    forming any later state (the speculative verification's form). Unrolling
+    H_t = alpha_t H_{t-1} + k_t delta_t^T gives, with G the decay products,
+        m_t = H_{t-1}^T k_t = G(0, t-1) H0^T k_t + sum_{s<t} G(s+1, t-1) (k_s . k_t) delta_s
+        delta_t = beta_t (v_t - alpha_t m_t)
+        o_t = H_t^T q_t = G(0, t) H0^T q_t + sum_{s<=t} G(s+1, t) (k_s . q_t) delta_s.
+    alpha are the gates themselves (not their logs). `shift` is the first factor's
+    offset from s (1 is the rule; tests plant 0). Returns (delta [T][d_v],
+    o [T][d_v] / sqrt(d_k))."""
+    T, dk = Q.shape
+    a = K @ H0          # row t: H0^T k_t
+    b = Q @ H0          # row t: H0^T q_t
+    KK = K @ K.T        # [s][t] = k_s . k_t
+    KQ = K @ Q.T        # [s][t] = k_s . q_t
+    D = np.zeros((T, V.shape[1]))
+    O_ = np.zeros_like(D)
+    for t in range(T):
+        m = decay_product(alpha, 0, t - 1) * a[t]
+        for s in range(t):
+            m = m + decay_product(alpha, s + shift, t - 1) * KK[s, t] * D[s]
+        D[t] = beta[t] * (V[t] - alpha[t] * m)
+        o = decay_product(alpha, 0, t) * b[t]
+        for s in range(t + 1):
+            o = o + decay_product(alpha, s + shift, t) * KQ[s, t] * D[s]
+        O_[t] = o / np.sqrt(dk)
+    return D, O_
+
+
+def replay(H0, K, D, alpha, n):
+    """The state after the first n of the recorded updates H <- alpha_t H + k_t delta_t^T."""
+    H = np.array(H0, dtype=np.float64, copy=True)
+    for t in range(n):
+        H = alpha[t] * H + np.outer(K[t], D[t])
+    return H
+

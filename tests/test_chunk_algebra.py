@@ -2,7 +2,9 @@
 against the sequential fp64 oracle: T tokens in chunks of C in {1, 4, 32, 64} must give
 the oracle's per-token readouts and final state to 1e-12, with the last chunk ragged,
 for the three ways of solving for Delta, with k-heads shared by two v-heads, d_k != d_v,
-and gates whose running log sum falls far below the fp64 range inside a chunk.
+and gates whose running log sum falls far below the fp64 range inside a chunk. Likewise
+the unrolled form the speculative verification evaluates draft tokens in (deltas and
+readouts from the state before the draft), and the commit's replay of its updates.
 
 The pages give only the per-token rule (page "linear_attention.rs", step 7); the
 chunked regrouping is derived from it, so this is the check of that derivation that
@@ -34,9 +36,10 @@ def _case(T=100, dk=16, dv=24, seed=11, strong_decay=False):
     return cfg, data
 
 
-def _oracle_by_token(cfg, data):
+def _oracle_by_token(cfg, data, states=None):
     """Per-token q, k, v (after conv, SiLU and the L2 norms), alpha, beta and readout o
-    of every (sequence, v-head), and the final state, from the oracle's step functions."""
+    of every (sequence, v-head), and the final state, from the oracle's step functions.
+    `states`, a list, receives the state after each token."""
     s = O.shape_of(cfg)
     B, T, Hk, Hv, dk, dv = cfg.batch, cfg.steps, cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim
     G = Hv // Hk
@@ -57,6 +60,8 @@ def _oracle_by_token(cfg, data):
             v[:, h, t] = act[:, 2 * Hk * dk + h * dv:2 * Hk * dk + (h + 1) * dv]
         ot, at, bt = O.recurrent_step(s, st, act, data["a"][:, t], data["b"][:, t], data["A_log"], data["dt_bias"])
         o[:, :, t], alpha[:, :, t], beta[:, :, t] = ot, at, bt
+        if states is not None:
+            states.append(st.copy())
     return q, k, v, o, alpha, beta, st
 
 
@@ -135,3 +140,41 @@ def test_model_catches_a_planted_mistake():
     finally:
         M.chunk_step = saved
     assert np.abs(hm - st[0, 0]).max() > 1e-3
+
+
+@pytest.fixture(scope="module", params=[False, True], ids=["drawn_gates", "strong_decay"])
+def draft_case(request):
+    cfg, data = _case(T=8, strong_decay=request.param)
+    states = []
+    return cfg, data, _oracle_by_token(cfg, data, states), states
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 8])
+def test_draft_unrolled_equals_sequential(draft_case, T):
+    """The draft tokens' readouts from H0 alone equal the oracle's token-by-token ones,
+    and replaying the recorded deltas gives the oracle's state after every prefix."""
+    cfg, data, (q, k, v, o, alpha, beta, st), states = draft_case
+    H0 = data["state"].astype(np.float64)
+    worst_o = worst_h = 0.0
+    for b in range(cfg.batch):
+        for h in range(cfg.num_v_heads):
+            D, om = M.draft_unrolled(H0[b, h], q[b, h, :T], k[b, h, :T], v[b, h, :T], alpha[b, h, :T], beta[b, h, :T])
+            assert np.all(np.isfinite(om)) and np.all(np.isfinite(D))
+            worst_o = max(worst_o, float(np.abs(om - o[b, h, :T]).max() / max(1.0, np.abs(o[b, h, :T]).max())))
+            for n in range(T + 1):
+                ref = H0[b, h] if n == 0 else states[n - 1][b, h]
+                hm = M.replay(H0[b, h], k[b, h], D, alpha[b, h], n)
+                worst_h = max(worst_h, float(np.abs(hm - ref).max() / max(1.0, np.abs(ref).max())))
+    print("T=%d: readout %.2e, replayed states %.2e" % (T, worst_o, worst_h))
+    assert worst_o <= 1e-12 and worst_h <= 1e-12
+
+
+def test_draft_model_catches_a_planted_mistake(draft_case):
+    """An off-by-one in the decay products (G(s, t-1) for G(s+1, t-1)) is caught."""
+    cfg, data, (q, k, v, o, alpha, beta, st), _ = draft_case
+    H0 = data["state"].astype(np.float64)
+    _, om = M.draft_unrolled(H0[0, 0], q[0, 0], k[0, 0], v[0, 0], alpha[0, 0], beta[0, 0], shift=0)
+    err = float(np.abs(om - o[0, 0]).max() / max(1.0, np.abs(o[0, 0]).max()))
+    print("planted: readout %.2e" % err)
+    assert err > 1e-6
+
