@@ -33,12 +33,12 @@ namespace {
 template <int D>
 using VerifyLayout = Layout<D, 1, D == 128 ? 16 : 0>;
 
-template <int D, bool BF>
+template <int D, bool BF, int TM>
 __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const KernelArgs a) {
   using L = VerifyLayout<D>;
   constexpr int NT = L::NT, R = L::R, CGL = L::CGL, NW = L::NW;
   constexpr int NCH = 3 * D;
-  constexpr int kTM = kMaxVerifyTokens;
+  constexpr int kTM = TM;  // draft tokens the LDS and register arrays hold (T <= TM)
   constexpr int kRows = kMaxConvTaps - 1 + kTM;
   constexpr uint32_t kRowBytes = D * 4;
   using raw_t = typename Act<BF>::raw_t;  // stored values, widened on use
@@ -492,10 +492,18 @@ __global__ __launch_bounds__(256) void gdn_conv_commit(const KernelArgs a) {
 template <int D>
 hipError_t launch_verify_d(const KernelArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv));
-  if (a.act_bf16)
-    gdn_verify_kernel<D, true><<<grid, VerifyLayout<D>::NT, 0, s>>>(a);
-  else
-    gdn_verify_kernel<D, false><<<grid, VerifyLayout<D>::NT, 0, s>>>(a);
+  // up to 4 draft tokens: arrays for 4, half the LDS of the instance for 8
+  if (a.T <= 4) {
+    if (a.act_bf16)
+      gdn_verify_kernel<D, true, 4><<<grid, VerifyLayout<D>::NT, 0, s>>>(a);
+    else
+      gdn_verify_kernel<D, false, 4><<<grid, VerifyLayout<D>::NT, 0, s>>>(a);
+  } else {
+    if (a.act_bf16)
+      gdn_verify_kernel<D, true, kMaxVerifyTokens><<<grid, VerifyLayout<D>::NT, 0, s>>>(a);
+    else
+      gdn_verify_kernel<D, false, kMaxVerifyTokens><<<grid, VerifyLayout<D>::NT, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
