@@ -394,15 +394,18 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 __device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
-template <int BM, int BN, int S, int WM, int WN>
+template <int BM, int BN, int S, int WM, int WN, int KB = 64>
 __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) {
   constexpr int NW = WM * WN;           // waves
   constexpr int R = BM + BN;            // rows per stage
-  constexpr int NI = R / 8 / NW;        // DMA instructions per wave per stage
+  constexpr int CPR = KB / 8;           // 16-byte cells per row of a stage
+  constexpr int RPI = 64 / CPR;         // rows one DMA instruction fills (1 KB)
+  constexpr int NI = R / RPI / NW;      // DMA instructions per wave per stage
   constexpr int TI = BM / WM / 16, TJ = BN / WN / 16;
-  static_assert(R % (8 * NW) == 0 && TI >= 1 && TJ >= 1, "tile shape");
+  static_assert(KB % 64 == 0 && KB <= 512, "stage depth");
+  static_assert(R % (RPI * NW) == 0 && TI >= 1 && TJ >= 1, "tile shape");
   static_assert((S - 2) * NI < 64, "memory counter range");
-  __shared__ __attribute__((aligned(16))) uint16_t ring[S][R][64];
+  __shared__ __attribute__((aligned(16))) uint16_t ring[S][R][KB];
 
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by id, so XCD x takes
   // the column tiles nt = x, x + 8, ..., each with all its row blocks in a row. The
@@ -418,15 +421,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
   const ProjSeg s = p.seg[si];
   const long n0 = static_cast<long>(nt - s.tile0) * BN;
   const long m0 = static_cast<long>(k % nmb) * BM;
-  const int K = p.K, nk = K / 64;
+  const int K = p.K, nk = K / KB;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
   const int wm = w / WN, wn = w % WN;
 
-  // this lane's DMA sources: instruction i of wave w fills rows 8 (NI w + i) .. + 7
+  // this lane's DMA sources: instruction i of wave w fills rows RPI (NI w + i) .. + RPI - 1,
+  // lane l position l % CPR of row l / CPR, with the global cell whose swizzled place that is
   const uint16_t* src[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int r = 8 * (NI * w + i) + (l >> 3), cell = (l & 7) ^ (l >> 3);
+    const int r = RPI * (NI * w + i) + l / CPR, cell = (l % CPR) ^ (r & 7);
     src[i] = r < BM ? p.x + min(m0 + r, static_cast<long>(p.M) - 1) * K + 8 * cell
                     : s.w + min(n0 + (r - BM), s.n - 1) * K + 8 * cell;
   }
@@ -438,14 +442,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // the NI DMA instructions of stage j: 16 bytes per lane from src[i] + 64 j into the
+  // the NI DMA instructions of stage j: 16 bytes per lane from src[i] + KB j into the
   // 1 KB blocks of this wave in ring slot j % S
 #pragma unroll
   for (int j = 0; j < S - 1; ++j)
     if (j < nk)
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        dma16(src[i] + 64L * j, ring0 + j * (R * 64) + 512 * i);
+        dma16(src[i] + static_cast<long>(KB) * j, ring0 + j * (R * KB) + 512 * i);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's DMA of stage kt has landed once at most the S - 2 later stages are
     // outstanding (the memory counter drains in issue order)
@@ -458,21 +462,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
       const int j = kt + S - 1;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        dma16(src[i] + 64L * j, ring0 + (j % S) * (R * 64) + 512 * i);
+        dma16(src[i] + static_cast<long>(KB) * j, ring0 + (j % S) * (R * KB) + 512 * i);
     }
     const uint16_t* st = &ring[kt % S][0][0];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KB / 32; ++kk) {
       bf16x8 a[TI], bb[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         const int r = wm * (BM / WM) + 16 * i + c16;
-        a[i] = *reinterpret_cast<const bf16x8*>(st + 64 * r + 8 * ((4 * kk + q) ^ (r & 7)));
+        a[i] = *reinterpret_cast<const bf16x8*>(st + KB * r + 8 * ((4 * kk + q) ^ (r & 7)));
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int r = BM + wn * (BN / WN) + 16 * j + c16;
-        bb[j] = *reinterpret_cast<const bf16x8*>(st + 64 * r + 8 * ((4 * kk + q) ^ (r & 7)));
+        bb[j] = *reinterpret_cast<const bf16x8*>(st + KB * r + 8 * ((4 * kk + q) ^ (r & 7)));
       }
 #pragma unroll
       for (int i = 0; i < TI; ++i)
@@ -486,7 +490,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
   __syncthreads();
   float* const tile = reinterpret_cast<float*>(&ring[0][0][0]);
   constexpr int TS = BN + 4;  // row stride in floats
-  static_assert(BM * TS * 4 <= S * R * 128, "output tile fits the ring");
+  static_assert(BM * TS * 4 <= S * R * KB * 2, "output tile fits the ring");
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
   }
 }
 
-template <int BM, int BN, int S, int WM = 2, int WN = 2>
+template <int BM, int BN, int S, int WM = 2, int WN = 2, int KB = 64>
 hipError_t launch_pipe(ProjArgs& p, hipStream_t st) {
   int tiles = 0;
   for (int i = 0; i < p.nseg; ++i) {
@@ -534,7 +538,7 @@ hipError_t launch_pipe(ProjArgs& p, hipStream_t st) {
   p.mblocks = static_cast<int>((p.M + BM - 1) / BM);
   // one workgroup per (column tile, row block), column tiles rounded up to a multiple of 8
   const dim3 grid(static_cast<unsigned>(((tiles + 7) / 8) * 8 * p.mblocks));
-  gdn_proj_pipe<BM, BN, S, WM, WN><<<grid, 64 * WM * WN, 0, st>>>(p);
+  gdn_proj_pipe<BM, BN, S, WM, WN, KB><<<grid, 64 * WM * WN, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -614,7 +618,20 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
   // -> 17.1 / 19.1 / 19.6 us (hidden = 2048)
   if (tiles(64, 64) >= 384) return launch_pipe<64, 64, 4>(p, st);
   if (tiles(32, 64) >= 384) return launch_pipe<32, 64, 4>(p, st);
+  // A long contraction (the out_proj shape, K = H_v d_v = 4096) over few output columns
+  // (at most 4096) takes deeper stages: 128 or 256 k per stage halve or quarter the
+  // barriers and make each DMA instruction fetch 256 / 512 contiguous bytes of 4 / 2
+  // rows. A 256-deep ring of 4 stages needs 128 KB (one workgroup per CU), so it is used
+  // while the grid fits one round of the CUs. out_proj (hidden = 2048) at 48 / 64 / 96 /
+  // 128 / 160 / 192 / 256 rows: 13.8 / 13.9 / 14.1 / 14.1 / 18.8 / 17.0 / 17.2 ->
+  // 11.4 / 11.5 / 12.6 / 12.8 / 15.2 / 15.8 / 16.2 us (in_proj's 2048-long contraction
+  // gained nothing from them).
+  const bool deep = p.K >= 4096 && p.K % 256 == 0 && rows <= 4096;
+  if (deep && tiles(32, 32) >= 384) return launch_pipe<32, 32, 4, 2, 2, 128>(p, st);
   if (tiles(32, 32) >= 384) return launch_pipe<32, 32, 4>(p, st);
+  if (deep && tiles(32, 16) <= 256) return launch_pipe<32, 16, 4, 2, 1, 256>(p, st);
+  if (deep && tiles(32, 32) <= 256) return launch_pipe<32, 32, 4, 2, 2, 256>(p, st);
+  if (deep) return launch_pipe<32, 16, 4, 2, 1, 128>(p, st);
   // 64 x 64 ring with a full grid
   if (tiles(64, 64) >= 256) return launch_pipe<64, 64, 4>(p, st);
   // 32 x 32 tiles: 64-deep stages keep 8 workgroups per CU resident when the grid is

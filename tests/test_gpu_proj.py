@@ -10,13 +10,16 @@ Tolerance: the kernels accumulate in fp32 and round once to the output dtype.
   error of order sqrt(K) 2^-24, a few 1e-7.
 Shapes cover every kernel: weight streaming (B <= 8, or B <= 2), the skinny MFMA
 kernel (3..32 rows, few output columns: out_proj at B = 3 and 20, in_proj at hidden
-512), the register-staged 32 x 32 tiles (out_proj at B = 9 to 128, in_proj at B = 100),
-and the DMA-fed rings: 32 x 32 (in_proj at B = 3 and 20, out_proj at B = 200), 32 x 64
-(in_proj at B = 40 and 64, out_proj at B = 512 and 600, the 40 and 600 with a ragged
-last row tile), 64 x 64 (in_proj at B = 128, out_proj at B = 1024), 128 x 128 (in_proj
-at B = 200, ragged) and 256 x 128 (in_proj at B = 512, 600 and 1024); ragged row and
-column tiles (the H_v-wide a/b segments are narrower than a tile) and the Qwen3.5-style
-sizes. The ring kernels store their tiles in 16-byte pieces; a segment whose width is
+512), the register-staged 32 x 32 tiles (out_proj of the small layers at B = 9 and 100,
+in_proj at B = 100), and the DMA-fed rings with 64-deep stages: 32 x 32 (in_proj at
+B = 3 and 20), 32 x 64 (in_proj at B = 33, 40 and 64, out_proj at B = 512 and 600, the
+33, 40 and 600 with a ragged last row tile), 64 x 64 (in_proj at B = 128 and 150,
+out_proj at B = 1024), 128 x 128 (in_proj at B = 200, ragged) and 256 x 128 (in_proj at
+B = 512, 600 and 1024); and with the deeper stages of out_proj's 4096-long contraction:
+32 x 16 by 256 (B = 33, 40, 64, and the narrow outputs of hidden 64..192), 32 x 32 by
+256 (B = 128), 32 x 16 by 128 (B = 150, ragged) and 32 x 32 by 128 (B = 200, ragged);
+ragged row and column tiles (the H_v-wide a/b segments are narrower than a tile) and
+the Qwen3.5-style sizes. The ring kernels store their tiles in 16-byte pieces; a segment whose width is
 not a multiple of 8 bf16 values (the a/b segments of the H_v = 20 layer at B = 1024) is
 stored element by element.
 """
@@ -67,10 +70,12 @@ CASES = [
     (8, 2, 4, 64, 512, None),
     (9, 2, 4, 64, 512, None),
     (20, 16, 32, 128, 2048, None),
+    (33, 16, 32, 128, 2048, None),
     (40, 16, 32, 128, 2048, None),
     (64, 16, 32, 128, 2048, None),
     (100, 2, 6, 64, 256, None),
     (128, 16, 32, 128, 2048, [0, 1, 15, 63, 64, 100, 127]),
+    (150, 16, 32, 128, 2048, [0, 31, 32, 127, 128, 149]),
     (200, 16, 32, 128, 2048, [0, 1, 127, 128, 150, 199]),
     (600, 16, 32, 128, 2048, [0, 63, 64, 511, 512, 575, 576, 599]),
     (512, 16, 32, 128, 2048, [0, 1, 63, 64, 255, 300, 511]),
