@@ -66,6 +66,7 @@ def cfg_of(B, Hk=16, Hv=32, d=128):
 CASES = [
     # B, Hk, Hv, d, hidden, rows checked (None: all)
     (1, 16, 32, 128, 2048, None),
+    (2, 16, 32, 128, 2048, None),
     (3, 16, 32, 128, 2048, None),
     (8, 2, 4, 64, 512, None),
     (9, 2, 4, 64, 512, None),
