@@ -7,7 +7,10 @@ missing library raises at first use.
 
 Before passing pointers, each tensor is checked to be a contiguous tensor on the GPU
 with the dtype and at least the number of elements the shape implies, so that the
-library never reads or writes past a tensor it was given.
+library never reads or writes past a tensor it was given. These checks cost about half
+a microsecond per tensor; a caller that has checked its buffers once (a serving loop
+over fixed buffers) may pass validate=False to skip them, and the library's own checks
+(null pointers, alignment, aliasing, the shape) still run.
 """
 
 from __future__ import annotations
@@ -139,6 +142,13 @@ def _p(t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] = 
     return t.data_ptr()  # an int: the c_void_p argtypes convert it
 
 
+def _ptr(t: Optional[torch.Tensor], name: str = "", dtype=None, numel: Optional[int] = None):
+    """The pointer alone, for validate=False: a caller that has checked its buffers once
+    (device, contiguity, dtype, size) skips the per-call checks; the library still checks
+    null pointers, alignment, aliasing and the shape."""
+    return None if t is None else t.data_ptr()
+
+
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -153,160 +163,173 @@ def _done(st: int, where: str, check: bool) -> int:
     return st
 
 
-def gdn_conv_update(shape: GdnShape, conv1d_state, qkv, conv1d_weight, qkv_act, stream=None, check=True) -> int:
+def gdn_conv_update(shape: GdnShape, conv1d_state, qkv, conv1d_weight, qkv_act, stream=None, check=True,
+                    validate=True) -> int:
+    P = _p if validate else _ptr
     s = shape
     act = _ACT.get(s.act_dtype)
     B, C, K = s.batch, s.channels, s.conv_kernel
     st = library().gdn_conv_update(
-        ctypes.byref(s), _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C), _p(qkv, "qkv", act, B * C),
-        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(qkv_act, "qkv_act", torch.float32, B * C), _stream(stream))
+        ctypes.byref(s), P(conv1d_state, "conv1d_state", act, B * (K - 1) * C), P(qkv, "qkv", act, B * C),
+        P(conv1d_weight, "conv1d_weight", act, C * K), P(qkv_act, "qkv_act", torch.float32, B * C), _stream(stream))
     return _done(st, "gdn_conv_update", check)
 
 
 def gdn_recurrent_step(shape: GdnShape, state, qkv_act, dt_raw, b_raw, A_log, dt_bias, y, stream=None,
-                       check=True) -> int:
+                       check=True, validate=True) -> int:
+    P = _p if validate else _ptr
     s = shape
     act, out = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
     B, C, Hv, dk, dv = s.batch, s.channels, s.num_v_heads, s.head_k_dim, s.head_v_dim
     st = library().gdn_recurrent_step(
-        ctypes.byref(s), _p(state, "state", torch.float32, B * Hv * dk * dv),
-        _p(qkv_act, "qkv_act", torch.float32, B * C), _p(dt_raw, "dt_raw", act, B * Hv),
-        _p(b_raw, "b_raw", act, B * Hv), _p(A_log, "A_log", torch.float32, Hv),
-        _p(dt_bias, "dt_bias", torch.float32, Hv), _p(y, "y", out, B * Hv * dv), _stream(stream))
+        ctypes.byref(s), P(state, "state", torch.float32, B * Hv * dk * dv),
+        P(qkv_act, "qkv_act", torch.float32, B * C), P(dt_raw, "dt_raw", act, B * Hv),
+        P(b_raw, "b_raw", act, B * Hv), P(A_log, "A_log", torch.float32, Hv),
+        P(dt_bias, "dt_bias", torch.float32, Hv), P(y, "y", out, B * Hv * dv), _stream(stream))
     return _done(st, "gdn_recurrent_step", check)
 
 
 def gdn_decode_layer(shape: GdnShape, conv1d_state, state, qkv, conv1d_weight, dt_raw, b_raw, z, A_log,
-                     dt_bias, norm_weight, out, stream=None, check=True) -> int:
+                     dt_bias, norm_weight, out, stream=None, check=True, validate=True) -> int:
+    P = _p if validate else _ptr
     s = shape
     act, od = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
     B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
     st = library().gdn_decode_layer(
-        ctypes.byref(s), _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
-        _p(state, "state", torch.float32, B * Hv * dk * dv), _p(qkv, "qkv", act, B * C),
-        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(dt_raw, "dt_raw", act, B * Hv),
-        _p(b_raw, "b_raw", act, B * Hv), _p(z, "z", act, B * Hv * dv), _p(A_log, "A_log", torch.float32, Hv),
-        _p(dt_bias, "dt_bias", torch.float32, Hv), _p(norm_weight, "norm_weight", torch.float32, dv),
-        _p(out, "out", od, B * Hv * dv), _stream(stream))
+        ctypes.byref(s), P(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
+        P(state, "state", torch.float32, B * Hv * dk * dv), P(qkv, "qkv", act, B * C),
+        P(conv1d_weight, "conv1d_weight", act, C * K), P(dt_raw, "dt_raw", act, B * Hv),
+        P(b_raw, "b_raw", act, B * Hv), P(z, "z", act, B * Hv * dv), P(A_log, "A_log", torch.float32, Hv),
+        P(dt_bias, "dt_bias", torch.float32, Hv), P(norm_weight, "norm_weight", torch.float32, dv),
+        P(out, "out", od, B * Hv * dv), _stream(stream))
     return _done(st, "gdn_decode_layer", check)
 
 
 def gdn_decode_layer_debug(shape: GdnShape, conv1d_state, state, qkv, conv1d_weight, dt_raw, b_raw, z, A_log,
                            dt_bias, norm_weight, out, qkv_act=None, alpha=None, beta=None, y=None, y_norm=None,
-                           stream=None, check=True) -> int:
+                           stream=None, check=True, validate=True) -> int:
     """gdn_decode_layer plus optional fp32 taps (each None or a GPU tensor): qkv_act
     [B][C], alpha and beta [B][H_v], y and y_norm [B][H_v*d_v]."""
+    P = _p if validate else _ptr
     s = shape
     act, od = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
     B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
     f32 = torch.float32
     st = library().gdn_decode_layer_debug(
-        ctypes.byref(s), _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
-        _p(state, "state", f32, B * Hv * dk * dv), _p(qkv, "qkv", act, B * C),
-        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(dt_raw, "dt_raw", act, B * Hv),
-        _p(b_raw, "b_raw", act, B * Hv), _p(z, "z", act, B * Hv * dv), _p(A_log, "A_log", f32, Hv),
-        _p(dt_bias, "dt_bias", f32, Hv), _p(norm_weight, "norm_weight", f32, dv),
-        _p(out, "out", od, B * Hv * dv), _p(qkv_act, "qkv_act", f32, B * C), _p(alpha, "alpha", f32, B * Hv),
-        _p(beta, "beta", f32, B * Hv), _p(y, "y", f32, B * Hv * dv), _p(y_norm, "y_norm", f32, B * Hv * dv),
+        ctypes.byref(s), P(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
+        P(state, "state", f32, B * Hv * dk * dv), P(qkv, "qkv", act, B * C),
+        P(conv1d_weight, "conv1d_weight", act, C * K), P(dt_raw, "dt_raw", act, B * Hv),
+        P(b_raw, "b_raw", act, B * Hv), P(z, "z", act, B * Hv * dv), P(A_log, "A_log", f32, Hv),
+        P(dt_bias, "dt_bias", f32, Hv), P(norm_weight, "norm_weight", f32, dv),
+        P(out, "out", od, B * Hv * dv), P(qkv_act, "qkv_act", f32, B * C), P(alpha, "alpha", f32, B * Hv),
+        P(beta, "beta", f32, B * Hv), P(y, "y", f32, B * Hv * dv), P(y_norm, "y_norm", f32, B * Hv * dv),
         _stream(stream))
     return _done(st, "gdn_decode_layer_debug", check)
 
 
 def gdn_decode_layer_pooled(shape: GdnShape, slots, conv1d_state_pool, state_pool, qkv, conv1d_weight, dt_raw,
-                            b_raw, z, A_log, dt_bias, norm_weight, out, stream=None, check=True) -> int:
+                            b_raw, z, A_log, dt_bias, norm_weight, out, stream=None, check=True,
+                            validate=True) -> int:
     """gdn_decode_layer with the states in a pool: sequence b uses slot slots[b]
     (int32 GPU tensor [B]; a slot outside the pool skips the sequence). The pool size
     is taken from state_pool's first dimension."""
+    P = _p if validate else _ptr
     s = shape
     act, od = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
     B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
     pool = int(state_pool.shape[0]) if isinstance(state_pool, torch.Tensor) else 0
     st = library().gdn_decode_layer_pooled(
-        ctypes.byref(s), pool, _p(slots, "slots", torch.int32, B),
-        _p(conv1d_state_pool, "conv1d_state_pool", act, pool * (K - 1) * C),
-        _p(state_pool, "state_pool", torch.float32, pool * Hv * dk * dv), _p(qkv, "qkv", act, B * C),
-        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(dt_raw, "dt_raw", act, B * Hv),
-        _p(b_raw, "b_raw", act, B * Hv), _p(z, "z", act, B * Hv * dv), _p(A_log, "A_log", torch.float32, Hv),
-        _p(dt_bias, "dt_bias", torch.float32, Hv), _p(norm_weight, "norm_weight", torch.float32, dv),
-        _p(out, "out", od, B * Hv * dv), _stream(stream))
+        ctypes.byref(s), pool, P(slots, "slots", torch.int32, B),
+        P(conv1d_state_pool, "conv1d_state_pool", act, pool * (K - 1) * C),
+        P(state_pool, "state_pool", torch.float32, pool * Hv * dk * dv), P(qkv, "qkv", act, B * C),
+        P(conv1d_weight, "conv1d_weight", act, C * K), P(dt_raw, "dt_raw", act, B * Hv),
+        P(b_raw, "b_raw", act, B * Hv), P(z, "z", act, B * Hv * dv), P(A_log, "A_log", torch.float32, Hv),
+        P(dt_bias, "dt_bias", torch.float32, Hv), P(norm_weight, "norm_weight", torch.float32, dv),
+        P(out, "out", od, B * Hv * dv), _stream(stream))
     return _done(st, "gdn_decode_layer_pooled", check)
 
 
 def gdn_sequence(shape: GdnShape, T: int, conv1d_state, state, qkv, conv1d_weight, dt_raw, b_raw, z, A_log,
-                 dt_bias, norm_weight, out, workspace=None, stream=None, check=True) -> int:
+                 dt_bias, norm_weight, out, workspace=None, stream=None, check=True, validate=True) -> int:
+    P = _p if validate else _ptr
     s = shape
     act, od = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
     B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
     T = int(T)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = library().gdn_sequence(
-        ctypes.byref(s), T, _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
-        _p(state, "state", torch.float32, B * Hv * dk * dv), _p(qkv, "qkv", act, B * T * C),
-        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(dt_raw, "dt_raw", act, B * T * Hv),
-        _p(b_raw, "b_raw", act, B * T * Hv), _p(z, "z", act, B * T * Hv * dv),
-        _p(A_log, "A_log", torch.float32, Hv), _p(dt_bias, "dt_bias", torch.float32, Hv),
-        _p(norm_weight, "norm_weight", torch.float32, dv), _p(out, "out", od, B * T * Hv * dv),
-        _p(workspace, "workspace"), ctypes.c_size_t(ws_bytes), _stream(stream))
+        ctypes.byref(s), T, P(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
+        P(state, "state", torch.float32, B * Hv * dk * dv), P(qkv, "qkv", act, B * T * C),
+        P(conv1d_weight, "conv1d_weight", act, C * K), P(dt_raw, "dt_raw", act, B * T * Hv),
+        P(b_raw, "b_raw", act, B * T * Hv), P(z, "z", act, B * T * Hv * dv),
+        P(A_log, "A_log", torch.float32, Hv), P(dt_bias, "dt_bias", torch.float32, Hv),
+        P(norm_weight, "norm_weight", torch.float32, dv), P(out, "out", od, B * T * Hv * dv),
+        P(workspace, "workspace"), ctypes.c_size_t(ws_bytes), _stream(stream))
     return _done(st, "gdn_sequence", check)
 
 
 def gdn_decode_verify(shape: GdnShape, T: int, conv1d_state, state, qkv, conv1d_weight, dt_raw, b_raw, z, A_log,
-                      dt_bias, norm_weight, out, trail, stream=None, check=True) -> int:
+                      dt_bias, norm_weight, out, trail, stream=None, check=True, validate=True) -> int:
     """Outputs of T draft tokens from the current states, which are only read; the
     per-token updates go to `trail` (a GPU tensor of gdn_verify_trail_bytes bytes)."""
+    P = _p if validate else _ptr
     s = shape
     act, od = _ACT.get(s.act_dtype), _ACT.get(s.out_dtype)
     B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
     T = int(T)
     tr_bytes = 0 if trail is None else trail.numel() * trail.element_size()
     st = library().gdn_decode_verify(
-        ctypes.byref(s), T, _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
-        _p(state, "state", torch.float32, B * Hv * dk * dv), _p(qkv, "qkv", act, B * T * C),
-        _p(conv1d_weight, "conv1d_weight", act, C * K), _p(dt_raw, "dt_raw", act, B * T * Hv),
-        _p(b_raw, "b_raw", act, B * T * Hv), _p(z, "z", act, B * T * Hv * dv),
-        _p(A_log, "A_log", torch.float32, Hv), _p(dt_bias, "dt_bias", torch.float32, Hv),
-        _p(norm_weight, "norm_weight", torch.float32, dv), _p(out, "out", od, B * T * Hv * dv),
-        _p(trail, "trail"), ctypes.c_size_t(tr_bytes), _stream(stream))
+        ctypes.byref(s), T, P(conv1d_state, "conv1d_state", act, B * (K - 1) * C),
+        P(state, "state", torch.float32, B * Hv * dk * dv), P(qkv, "qkv", act, B * T * C),
+        P(conv1d_weight, "conv1d_weight", act, C * K), P(dt_raw, "dt_raw", act, B * T * Hv),
+        P(b_raw, "b_raw", act, B * T * Hv), P(z, "z", act, B * T * Hv * dv),
+        P(A_log, "A_log", torch.float32, Hv), P(dt_bias, "dt_bias", torch.float32, Hv),
+        P(norm_weight, "norm_weight", torch.float32, dv), P(out, "out", od, B * T * Hv * dv),
+        P(trail, "trail"), ctypes.c_size_t(tr_bytes), _stream(stream))
     return _done(st, "gdn_decode_verify", check)
 
 
 def gdn_decode_commit(shape: GdnShape, T: int, accepted, conv1d_state, state, qkv, trail, stream=None,
-                      check=True) -> int:
+                      check=True, validate=True) -> int:
     """Advance sequence b by its first accepted[b] draft tokens (int32 GPU tensor [B])
     of the preceding gdn_decode_verify call with the same T, qkv and trail."""
+    P = _p if validate else _ptr
     s = shape
     act = _ACT.get(s.act_dtype)
     B, C, K, Hv, dk, dv = s.batch, s.channels, s.conv_kernel, s.num_v_heads, s.head_k_dim, s.head_v_dim
     T = int(T)
     tr_bytes = 0 if trail is None else trail.numel() * trail.element_size()
     st = library().gdn_decode_commit(
-        ctypes.byref(s), T, _p(accepted, "accepted", torch.int32, B),
-        _p(conv1d_state, "conv1d_state", act, B * (K - 1) * C), _p(state, "state", torch.float32, B * Hv * dk * dv),
-        _p(qkv, "qkv", act, B * T * C), _p(trail, "trail"), ctypes.c_size_t(tr_bytes), _stream(stream))
+        ctypes.byref(s), T, P(accepted, "accepted", torch.int32, B),
+        P(conv1d_state, "conv1d_state", act, B * (K - 1) * C), P(state, "state", torch.float32, B * Hv * dk * dv),
+        P(qkv, "qkv", act, B * T * C), P(trail, "trail"), ctypes.c_size_t(tr_bytes), _stream(stream))
     return _done(st, "gdn_decode_commit", check)
 
 
 def gdn_in_proj(shape: GdnShape, hidden: int, x_norm, w_qkv, w_z, w_a, w_b, qkv, z, dt_raw, b_raw, stream=None,
-                check=True) -> int:
+                check=True, validate=True) -> int:
     """x_norm [B, hidden] -> qkv, z, dt_raw, b_raw (bf16), weights [outputs, hidden] bf16."""
+    P = _p if validate else _ptr
     s = shape
     bf = torch.bfloat16
     B, C, Hv, dv, H = s.batch, s.channels, s.num_v_heads, s.head_v_dim, int(hidden)
     st = library().gdn_in_proj(
-        ctypes.byref(s), H, _p(x_norm, "x_norm", bf, B * H), _p(w_qkv, "w_qkv", bf, C * H),
-        _p(w_z, "w_z", bf, Hv * dv * H), _p(w_a, "w_a", bf, Hv * H), _p(w_b, "w_b", bf, Hv * H),
-        _p(qkv, "qkv", bf, B * C), _p(z, "z", bf, B * Hv * dv), _p(dt_raw, "dt_raw", bf, B * Hv),
-        _p(b_raw, "b_raw", bf, B * Hv), _stream(stream))
+        ctypes.byref(s), H, P(x_norm, "x_norm", bf, B * H), P(w_qkv, "w_qkv", bf, C * H),
+        P(w_z, "w_z", bf, Hv * dv * H), P(w_a, "w_a", bf, Hv * H), P(w_b, "w_b", bf, Hv * H),
+        P(qkv, "qkv", bf, B * C), P(z, "z", bf, B * Hv * dv), P(dt_raw, "dt_raw", bf, B * Hv),
+        P(b_raw, "b_raw", bf, B * Hv), _stream(stream))
     return _done(st, "gdn_in_proj", check)
 
 
-def gdn_out_proj(shape: GdnShape, hidden: int, gated, w_out, y, stream=None, check=True) -> int:
+def gdn_out_proj(shape: GdnShape, hidden: int, gated, w_out, y, stream=None, check=True,
+                 validate=True) -> int:
     """gated [B, H_v*d_v] bf16 -> y [B, hidden] (out dtype), w_out [hidden, H_v*d_v] bf16."""
+    P = _p if validate else _ptr
     s = shape
     bf = torch.bfloat16
     od = _ACT.get(s.out_dtype)
     B, Hv, dv, H = s.batch, s.num_v_heads, s.head_v_dim, int(hidden)
     st = library().gdn_out_proj(
-        ctypes.byref(s), H, _p(gated, "gated", bf, B * Hv * dv), _p(w_out, "w_out", bf, H * Hv * dv),
-        _p(y, "y", od, B * H), _stream(stream))
+        ctypes.byref(s), H, P(gated, "gated", bf, B * Hv * dv), P(w_out, "w_out", bf, H * Hv * dv),
+        P(y, "y", od, B * H), _stream(stream))
     return _done(st, "gdn_out_proj", check)

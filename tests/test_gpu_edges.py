@@ -139,22 +139,23 @@ def test_empty_batch_and_zero_tokens_are_noops():
 
 
 def test_deterministic_and_poison_overwritten():
-    """Two runs from the same inputs agree bit for bit, and outputs poisoned with NaN
-    are fully overwritten."""
+    """Two runs from the same inputs agree bit for bit (the second with the binding's
+    per-call tensor checks off, validate=False), and outputs poisoned with NaN are fully
+    overwritten."""
     cfg = I.config(2).with_(batch=8)
     data = I.generate(cfg, steps=2)
     runs = []
-    for _ in range(2):
+    for validate in (True, False):
         dv = GC.DeviceInputs(cfg, data)
         s = GC.shape_for(cfg)
         out = torch.full((2, cfg.batch, cfg.z_dim), float("nan"), device="cuda")
         for t in range(2):
             gdn.gdn_decode_layer(s, dv.conv_state, dv.state, dv.qkv[t], dv.conv_w, dv.a[t], dv.b[t], dv.z[t],
-                                 dv.A_log, dv.dt_bias, dv.norm_w, out[t])
+                                 dv.A_log, dv.dt_bias, dv.norm_w, out[t], validate=validate)
         act = torch.full((cfg.batch, cfg.channels), float("nan"), device="cuda")
         y = torch.full((cfg.batch, cfg.num_v_heads, cfg.head_v_dim), float("nan"), device="cuda")
-        gdn.gdn_conv_update(s, dv.conv_state, dv.qkv[0], dv.conv_w, act)
-        gdn.gdn_recurrent_step(s, dv.state, act, dv.a[0], dv.b[0], dv.A_log, dv.dt_bias, y)
+        gdn.gdn_conv_update(s, dv.conv_state, dv.qkv[0], dv.conv_w, act, validate=validate)
+        gdn.gdn_recurrent_step(s, dv.state, act, dv.a[0], dv.b[0], dv.A_log, dv.dt_bias, y, validate=validate)
         torch.cuda.synchronize()
         for tns in (out, act, y):
             assert torch.isfinite(tns).all()
