@@ -156,7 +156,7 @@ struct TrailLayout {
 
 extern "C" {
 
-int32_t gdn_abi_version(void) { return (1 << 16) | 2; }
+int32_t gdn_abi_version(void) { return (1 << 16) | 3; }
 
 const char* gdn_status_string(int32_t st) {
   switch (st) {
@@ -560,7 +560,9 @@ gdn_status_t check_proj(const gdn_shape_t* shape, int32_t hidden, int64_t K) {
   if (st != GDN_OK) return st;
   if (hidden < 1) return GDN_ERR_SHAPE;
   if (shape->act_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
-  if (hidden % 64 != 0 || K % 64 != 0) return GDN_ERR_UNSUPPORTED;
+  // the contraction (hidden for in_proj, H_v d_v for out_proj) goes in 64-deep stages;
+  // any number of output columns is fine (ragged tiles are stored element by element)
+  if (K % 64 != 0) return GDN_ERR_UNSUPPORTED;
   if ((static_cast<int64_t>(shape->batch) + 31) / 32 > 65535) return GDN_ERR_SHAPE;  // grid rows
   return GDN_OK;
 }

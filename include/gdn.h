@@ -234,7 +234,8 @@ gdn_status_t gdn_decode_commit(const gdn_shape_t* shape, int32_t T, const int32_
  * Y[b][n] = sum_k X[b][k] W[n][k] with bf16 X and W, fp32 accumulation and one final
  * rounding to the output dtype (round to nearest even for bf16). One launch each.
  * Requirements: act_dtype == GDN_BF16 and the contraction length (hidden for
- * gdn_in_proj, H_v*d_v for gdn_out_proj) a multiple of 64, else GDN_ERR_UNSUPPORTED;
+ * gdn_in_proj, H_v*d_v for gdn_out_proj) a multiple of 64, else GDN_ERR_UNSUPPORTED
+ * (gdn_out_proj's hidden, its number of outputs, may be any value >= 1 since ABI 1.3);
  * hidden < 1 -> GDN_ERR_SHAPE. Alignment: 16 bytes for every buffer except dt_raw and
  * b_raw (2). Weights are row-major [outputs][inputs] (K contiguous). */
 

@@ -287,8 +287,7 @@ def test_projection_validation():
     s = qwen()
     assert call_in_proj(s, 0) == SHAPE
     assert call_out_proj(s, -64) == SHAPE
-    assert call_in_proj(s, 2000) == UNSUPPORTED      # hidden not a multiple of 64
-    assert call_out_proj(s, 100) == UNSUPPORTED
+    assert call_in_proj(s, 2000) == UNSUPPORTED      # in_proj contracts over hidden: a multiple of 64
     assert call_in_proj(qwen(act_dtype="f32"), 2048) == UNSUPPORTED
     assert call_out_proj(qwen(act_dtype="f32"), 2048) == UNSUPPORTED
     # out_proj contracts over H_v * d_v, which must also be a multiple of 64

@@ -155,3 +155,27 @@ def test_projection_then_decode_layer():
     ref = O.decode_step(so, cs, st, bf(bits(qkv)), I.widen(data["conv_w"], "bf16"), bf(bits(a)), bf(bits(b)),
                         bf(bits(z)), data["A_log"], data["dt_bias"], data["norm_w"])
     compare("in_proj -> decode_layer", host_f64(out), ref, "bf16", TOL["bf16"])
+
+
+@pytest.mark.parametrize("B", [64, 150, 300, 400])
+def test_out_proj_deep_stages_ragged_columns(B):
+    """out_proj's 4096-long contraction onto 1000 output columns, whose last column tile
+    is ragged, through each deep-stage ring: 32 x 16 by 256 (B = 64), 32 x 32 by 256
+    (150), 32 x 16 by 128 (300) and 32 x 32 by 128 (400)."""
+    hidden = 1000
+    cfg = cfg_of(B)
+    zd = cfg.z_dim
+    rng = np.random.default_rng(B + 7)
+    g = I.f32_to_bf16_bits(rng.standard_normal((B, zd), dtype=np.float32))
+    w = I.f32_to_bf16_bits((rng.standard_normal((hidden, zd)) / np.sqrt(zd)).astype(np.float32))
+    gd, wd = dev(g, "bf16"), dev(w, "bf16")
+    y32 = torch.full((B, hidden), float("nan"), dtype=torch.float32, device="cuda")
+    y16 = torch.full((B, hidden), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_out_proj(shape_for(cfg), hidden, gd, wd, y32)
+    gdn.gdn_out_proj(shape_for(cfg, out_dtype="bf16"), hidden, gd, wd, y16)
+    torch.cuda.synchronize()
+    idx = np.unique(np.array([0, 1, 31, 32, B // 2, B - 2, B - 1]))
+    ref = O.linear(bf(g[idx]), bf(w))
+    sel = torch.as_tensor(idx, device="cuda")
+    check_f32("out_proj h1000 B=%d f32" % B, y32[sel], ref)
+    check_bf16("out_proj h1000 B=%d bf16" % B, y16[sel], ref)
