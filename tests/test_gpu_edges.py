@@ -557,3 +557,43 @@ def test_sequence_verify_commit_replayed_from_a_hip_graph():
         for name, x, e in zip(("out", "verify out", "trail", "state", "conv state"),
                               (out, vout, trail, d.state, d.conv_state), eager):
             assert torch.equal(x, e), "replay %d: %s differs from the eager calls" % (rep, name)
+
+
+def test_projections_replayed_from_a_hip_graph():
+    """in_proj and out_proj at B = 1, 20 and 64 (GEMV, skinny, 32 x 32 and 32 x 64 rings
+    with 64-deep stages, the 32 x 16 ring with 256-deep ones) captured in one HIP graph
+    and replayed three times with the outputs poisoned in between: every replay
+    reproduces the eager calls bit for bit."""
+    hidden = I.HIDDEN
+    calls, outs = [], []
+    for B in (1, 20, 64):
+        cfg = I.config(2).with_(batch=B)
+        s = GC.shape_for(cfg, out_dtype="bf16")
+        P = I.generate_projections(cfg, hidden)
+        x = GC.dev(P["x_norm"], "bf16")
+        w = {k: GC.dev(P[k], "bf16") for k in ("w_qkv", "w_z", "w_a", "w_b", "w_out")}
+        g = torch.randn((B, cfg.z_dim), device="cuda").to(torch.bfloat16)
+        o = [torch.empty((B, n), dtype=torch.bfloat16, device="cuda")
+             for n in (cfg.channels, cfg.z_dim, cfg.num_v_heads, cfg.num_v_heads, hidden)]
+
+        def call(st=None, s=s, x=x, w=w, g=g, o=o):
+            gdn.gdn_in_proj(s, hidden, x, w["w_qkv"], w["w_z"], w["w_a"], w["w_b"], o[0], o[1], o[2], o[3], stream=st)
+            gdn.gdn_out_proj(s, hidden, g, w["w_out"], o[4], stream=st)
+        calls.append(call)
+        outs.extend(o)
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c in calls:
+            c(torch.cuda.current_stream())
+    for rep in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (t, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(t, e), "replay %d: output %d differs from the eager calls" % (rep, i)
