@@ -623,7 +623,7 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
   // (at most 4096) takes deeper stages: 128 or 256 k per stage halve or quarter the
   // barriers and make each DMA instruction fetch 256 / 512 contiguous bytes of 4 / 2
   // rows. A 256-deep ring of 4 stages needs 128 KB (one workgroup per CU), so it is used
-  // while the grid fits one round of the CUs. out_proj (hidden = 2048) at 48 / 64 / 96 /
+  // while the whole grid is resident at once. out_proj (hidden = 2048) at 48 / 64 / 96 /
   // 128 / 160 / 192 / 256 rows: 13.8 / 13.9 / 14.1 / 14.1 / 18.8 / 17.0 / 17.2 ->
   // 11.4 / 11.5 / 12.6 / 12.8 / 15.2 / 15.8 / 16.2 us (in_proj's 2048-long contraction
   // gained nothing from them).
