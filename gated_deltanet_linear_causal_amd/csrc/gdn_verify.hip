@@ -62,7 +62,6 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   __shared__ __attribute__((aligned(16))) float s_q[kTM][D];
   __shared__ __attribute__((aligned(16))) float s_k[kTM][D];
   __shared__ __attribute__((aligned(16))) float s_v[kTM][D];
-  __shared__ __attribute__((aligned(16))) float s_o[kTM][D];  // readouts, for the RMSNorm of phase C
   __shared__ __attribute__((aligned(16))) raw_t s_z[kTM][D];  // z rows of the tokens, staged in phase A
   __shared__ float s_gate[2][kTM];      // alpha, beta per token
   __shared__ float s_kk[kTM][kTM];      // [t][s]: k_s . k_t for s < t (unit vectors)
@@ -358,7 +357,11 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   __syncthreads();
 
   // ---- B2. delta_t and o_t, one thread per column c: dl holds the deltas so far,
-  // gs[s] = G(s+1, t-1) and g0 = G(0, t-1) before token t's gate is applied
+  // gs[s] = G(s+1, t-1) and g0 = G(0, t-1) before token t's gate is applied; the
+  // readouts stay in registers for phase C
+  float ov[kTM];
+#pragma unroll
+  for (int tok = 0; tok < kTM; ++tok) ov[tok] = 0.0f;
   if (t < D) {
     const int c = t;
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
@@ -380,26 +383,19 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
       float ot = g0 * s_hq[tok][c];
 #pragma unroll
       for (int s = 0; s <= tok; ++s) ot = fmaf(gs[s] * s_kq[tok][s], dl[s], ot);
-      s_o[tok][c] = scale * ot;
+      ov[tok] = scale * ot;
       a.trail_delta[((bt0 + tok) * a.Hv + h) * D + c] = delta;
     }
   }
   if (t < T) a.trail_alpha[(bt0 + t) * a.Hv + h] = s_gate[0][t];
-  __syncthreads();
 
-  // ---- C. per-head RMSNorm and gated outputs of all tokens
+  // ---- C. per-head RMSNorm: each token's squares summed over the D column threads (one
+  // transposed reduction for all tokens), then the gated outputs, one column per thread
   float ss[kTM];
 #pragma unroll
-  for (int tok = 0; tok < kTM; ++tok) {
-    float v = 0.0f;
-    if (rg == 0 && tok < T) {
-      const float4 o = *reinterpret_cast<const float4*>(&s_o[tok][4 * cg]);
-      v = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
-    }
-    ss[tok] = v;
-  }
+  for (int tok = 0; tok < kTM; ++tok) ss[tok] = (t < D && tok < T) ? ov[tok] * ov[tok] : 0.0f;
   {
-    float s2[kTM / 4];  // row r holds token j + 2 (r & 1) + 4 (r >> 1) in register j
+    float s2[kTM / 4];  // row r holds token j + (kTM / 4) (r & 1) + (kTM / 2) (r >> 1) in register j
     wave_sums_t<kTM>(ss, s2);
     if ((lane & 15) == 0) {
       const int r = lane >> 4;
@@ -408,21 +404,27 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
     }
   }
   __syncthreads();
-  if (rg == 0) {
-    const float4 w4 = *reinterpret_cast<const float4*>(a.norm_w + 4 * cg);
+  if (t < D) {
+    const int c = t;
+    const float w = a.norm_w[c];
     const bool obf = a.out_bf16 != 0;
-    for (int tok = 0; tok < T; ++tok) {
+#pragma unroll
+    for (int tok = 0; tok < kTM; ++tok) {
+      if (tok >= T) break;
       float tot = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) tot += red[w][tok];
+      for (int ww = 0; ww < NW; ++ww) tot += red[ww][tok];
       const float r = __builtin_amdgcn_rsqf(tot / static_cast<float>(D) + a.rms_eps);
-      const float4 z4 = Act<BF>::load4(&s_z[tok][0], 4 * cg);
-      const float4 o = *reinterpret_cast<const float4*>(&s_o[tok][4 * cg]);
-      store_out4(a.out, b * a.out_bs + tok * a.out_ts + static_cast<long>(h) * D + 4 * cg, gated<true>(o, r, w4, z4),
-                 obf);
+      const float y = ov[tok] * r * w * silu_rcp(Act<BF>::f(s_z[tok][c]));
+      const long at = b * a.out_bs + tok * a.out_ts + static_cast<long>(h) * D + c;
+      if (obf)
+        static_cast<uint16_t*>(a.out)[at] = static_cast<uint16_t>(f32_to_bf16(y));
+      else
+        static_cast<float*>(a.out)[at] = y;
     }
   }
 }
+
 
 // Commit of the accepted prefix: H <- alpha_t H + k_t delta_t^T for t < n = accepted[b]
 // with the recorded deltas (those the verify kernel formed its outputs from). n
