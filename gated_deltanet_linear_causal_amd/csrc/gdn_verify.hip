@@ -23,10 +23,11 @@ namespace {
 // so one pass over H0 gives every token's H0^T k_t and H0^T q_t (two matrix-vector
 // products per token instead of two plus the rank-one update), and the rest is the
 // T x T products k_s . k_t, k_s . q_t and the decay products. Phases: (A) conv, gates
-// and L2 norms of all T tokens (one block reduction), then the T^2 token products;
+// and the L2 norms of all T tokens (one block reduction), then the T^2 token products;
 // (B) per token, H0^T k_t and H0^T q_t on the VGPR-resident state, reduced over the
-// row groups, then delta_t and o_t; (C) the per-head RMSNorm and the outputs of all T
-// tokens (one block reduction).
+// row groups, then delta_t and o_t, one thread per column (the L2 norms enter as
+// factors of those products, q and k are never rescaled in place); (C) the per-head
+// RMSNorm and the outputs of all T tokens on the same threads (one block reduction).
 // ----------------------------------------------------------------------------------
 // d = 128 uses 16 state rows per lane (4 waves per head, 64 state VGPRs): the per-token
 // work per lane halves and more workgroups stay resident.
@@ -50,8 +51,8 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
       raw_t w[NCH * kMaxConvTaps];    // taps [NCH][K]
     } conv;
     struct {
-      float hk[kTM][D];               // H0^T k_t, reduced
-      float hq[kTM][D];               // H0^T q_t, reduced
+      float hk[kTM][D];               // H0^T k_t, reduced (k before its L2 norm)
+      float hq[kTM][D];               // H0^T q_t, reduced (q before its L2 norm)
     } prod;
   };
   __shared__ __attribute__((aligned(16))) Reused reused;
@@ -64,8 +65,8 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   __shared__ __attribute__((aligned(16))) float s_v[kTM][D];
   __shared__ __attribute__((aligned(16))) raw_t s_z[kTM][D];  // z rows of the tokens, staged in phase A
   __shared__ float s_gate[2][kTM];      // alpha, beta per token
-  __shared__ float s_kk[kTM][kTM];      // [t][s]: k_s . k_t for s < t (unit vectors)
-  __shared__ float s_kq[kTM][kTM];      // [t][s]: k_s . q_t for s <= t
+  __shared__ float s_kk[kTM][kTM];      // [t][s]: k_s . k_t for s < t (before the L2 norms)
+  __shared__ float s_kq[kTM][kTM];      // [t][s]: k_s . q_t for s <= t (before the L2 norms)
   __shared__ float red[NW][2 * kTM];    // per-wave partial sums
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -224,30 +225,35 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   }
   __syncthreads();
   const long bt0 = static_cast<long>(b) * T;
-  for (int tok = 0; tok < T; ++tok) {
-    float sq = 0.0f, sk = 0.0f;
+  // 1 / |q_t| and 1 / |k_t| of every token, in every thread: q and k stay as the conv
+  // left them, and the factors are applied where their products are used (B2)
+  float rq[kTM], rk[kTM];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      sq += red[w][2 * tok];
-      sk += red[w][2 * tok + 1];
-    }
-    const float rq = __builtin_amdgcn_rsqf(sq + a.l2_eps), rk = __builtin_amdgcn_rsqf(sk + a.l2_eps);
-    // elements 0..D-1 scale q, D..2D-1 scale k (and record it in the trail)
-    for (int i = t; i < 2 * D; i += NT) {
-      if (i < D) {
-        s_q[tok][i] *= rq;
-      } else {
-        const float kn = s_k[tok][i - D] * rk;
-        s_k[tok][i - D] = kn;
-        if (h % a.G == 0) a.trail_k[((bt0 + tok) * a.Hk + g) * D + (i - D)] = kn;
+  for (int tok = 0; tok < kTM; ++tok) {
+    float sq = 0.0f, sk = 0.0f;
+    if (tok < T) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        sq += red[w][2 * tok];
+        sk += red[w][2 * tok + 1];
       }
     }
+    rq[tok] = __builtin_amdgcn_rsqf(sq + a.l2_eps);
+    rk[tok] = __builtin_amdgcn_rsqf(sk + a.l2_eps);
   }
-  __syncthreads();
+  // the trail's unit k
+  if (h % a.G == 0) {
+#pragma unroll
+    for (int tok = 0; tok < kTM; ++tok) {
+      if (tok >= T) break;
+      for (int i = t; i < D; i += NT) a.trail_k[((bt0 + tok) * a.Hk + g) * D + i] = s_k[tok][i] * rk[tok];
+    }
+  }
 
-  // The T^2 products of the unit vectors: pair p = i T + j is k_j . k_i for j < i and
-  // k_i . q_j for j >= i. 16 pairs per wave and pass, 4 lanes per pair, each lane D / 4
-  // consecutive elements, then a sum over the 4 lanes.
+  // The T^2 products of q and k (as the conv left them; B2 scales them to unit vectors):
+  // pair p = i T + j is k_j . k_i for j < i and k_i . q_j for j >= i. 16 pairs per wave
+  // and pass, 4 lanes per pair, each lane D / 4 consecutive elements, then a sum over
+  // the 4 lanes.
   {
     constexpr int EPL = D / 4;
     const int sub = lane >> 2, part = lane & 3;
@@ -280,7 +286,8 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
   }
   // (read in B2, after the barrier that ends B1)
 
-  // ---- B1. H0^T k_t and H0^T q_t of every token on the VGPR-resident state, summed
+  // ---- B1. H0^T k_t and H0^T q_t of every token (k and q not yet scaled to unit length)
+  // on the VGPR-resident state, summed
   // over the lane's rows (no barrier: each lane reads LDS written above), then over the
   // row groups and stored to LDS
   auto partial = [&](int tok, float4& m, float4& pq) {
@@ -371,18 +378,18 @@ __global__ __launch_bounds__((VerifyLayout<D>::NT)) void gdn_verify_kernel(const
     for (int tok = 0; tok < kTM; ++tok) {
       if (tok >= T) break;
       const float alpha = s_gate[0][tok], beta = s_gate[1][tok];
-      float mt = g0 * s_hk[tok][c];
+      float mt = g0 * (s_hk[tok][c] * rk[tok]);
 #pragma unroll
-      for (int s = 0; s < tok; ++s) mt = fmaf(gs[s] * s_kk[tok][s], dl[s], mt);
+      for (int s = 0; s < tok; ++s) mt = fmaf(gs[s] * (s_kk[tok][s] * (rk[s] * rk[tok])), dl[s], mt);
       const float delta = beta * (s_v[tok][c] - alpha * mt);
       dl[tok] = delta;
       g0 *= alpha;
 #pragma unroll
       for (int s = 0; s < tok; ++s) gs[s] *= alpha;
       gs[tok] = 1.0f;
-      float ot = g0 * s_hq[tok][c];
+      float ot = g0 * (s_hq[tok][c] * rq[tok]);
 #pragma unroll
-      for (int s = 0; s <= tok; ++s) ot = fmaf(gs[s] * s_kq[tok][s], dl[s], ot);
+      for (int s = 0; s <= tok; ++s) ot = fmaf(gs[s] * (s_kq[tok][s] * (rk[s] * rq[tok])), dl[s], ot);
       ov[tok] = scale * ot;
       a.trail_delta[((bt0 + tok) * a.Hv + h) * D + c] = delta;
     }
