@@ -88,6 +88,7 @@ struct ProjArgs {
   int nseg;
   long rows;          // sum of the segments' n (set by launch_proj)
   int ntiles, mblocks;  // column tiles and row blocks of a tiled launch (set by its launcher)
+  int krot;            // 1: the DMA-ring workgroups start their contraction at staggered stages
   ProjSeg seg[kMaxProjSegs];
 };
 hipError_t launch_proj(ProjArgs p, hipStream_t stream);

@@ -394,7 +394,7 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 __device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
-template <int BM, int BN, int S, int WM, int WN, int KB = 64>
+template <int BM, int BN, int S, int WM, int WN, int KB, bool ROT>
 __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) {
   constexpr int NW = WM * WN;           // waves
   constexpr int R = BM + BN;            // rows per stage
@@ -422,6 +422,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
   const long n0 = static_cast<long>(nt - s.tile0) * BN;
   const long m0 = static_cast<long>(k % nmb) * BM;
   const int K = p.K, nk = K / KB;
+  // ROT: workgroup k takes the stages in the order k mod nk, ..., nk - 1, 0, ... (a
+  // template flag: the wrap costs the short loop of the small tiles a few instructions)
+  const int rot = ROT ? static_cast<int>(static_cast<unsigned>(k) % static_cast<unsigned>(nk)) : 0;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, q = l >> 4, c16 = l & 15;
   const int wm = w / WN, wn = w % WN;
 
@@ -449,7 +452,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
     if (j < nk)
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        dma16(src[i] + static_cast<long>(KB) * j, ring0 + j * (R * KB) + 512 * i);
+        dma16(src[i] + static_cast<long>(KB) * (j + rot < nk ? j + rot : j + rot - nk), ring0 + j * (R * KB) + 512 * i);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's DMA of stage kt has landed once at most the S - 2 later stages are
     // outstanding (the memory counter drains in issue order)
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
       const int j = kt + S - 1;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        dma16(src[i] + static_cast<long>(KB) * j, ring0 + (j % S) * (R * KB) + 512 * i);
+        dma16(src[i] + static_cast<long>(KB) * (j + rot < nk ? j + rot : j + rot - nk), ring0 + (j % S) * (R * KB) + 512 * i);
     }
     const uint16_t* st = &ring[kt % S][0][0];
 #pragma unroll
@@ -538,7 +541,10 @@ hipError_t launch_pipe(ProjArgs& p, hipStream_t st) {
   p.mblocks = static_cast<int>((p.M + BM - 1) / BM);
   // one workgroup per (column tile, row block), column tiles rounded up to a multiple of 8
   const dim3 grid(static_cast<unsigned>(((tiles + 7) / 8) * 8 * p.mblocks));
-  gdn_proj_pipe<BM, BN, S, WM, WN, KB><<<grid, 64 * WM * WN, 0, st>>>(p);
+  if (p.krot)
+    gdn_proj_pipe<BM, BN, S, WM, WN, KB, true><<<grid, 64 * WM * WN, 0, st>>>(p);
+  else
+    gdn_proj_pipe<BM, BN, S, WM, WN, KB, false><<<grid, 64 * WM * WN, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -604,13 +610,34 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
     for (int i = 0; i < p.nseg; ++i) n += (p.seg[i].n + bn - 1) / bn;
     return n * ((p.M + bm - 1) / bm);
   };
+  // The DMA-ring workgroups stream their stages in staggered orders while the activations
+  // are small (at most 2 MB), so that the workgroups running at once read different
+  // slices of the weights: in_proj at 64 rows 14.2 -> 13.3 us, out_proj at 96 / 128 rows
+  // 12.1 / 12.4 -> 11.7 / 12.0 us. Larger activations keep the common order, in which the
+  // workgroups of an XCD read each activation slice together from its L2 (in_proj /
+  // out_proj at 1024 rows: 70.6 / 27.8 us, staggered 73.7 / 39.2 us).
+  p.krot = static_cast<long>(p.M) * p.K * 2 <= (2L << 20) ? 1 : 0;
+  // A long contraction (the out_proj shape, K = H_v d_v = 4096) over few output columns
+  // (at most 4096) takes deeper stages (below).
+  const bool deep = p.K >= 4096 && p.K % 256 == 0 && rows <= 4096;
+  // Otherwise 64-row blocks on 3-stage rings of 72 or 48 KB (two or three workgroups per
+  // CU): 64 x 128 tiles while they make 257..448 workgroups, else 64 x 64 tiles where
+  // 256-row blocks would pad two or more 64-row blocks and would still make 128 or more
+  // workgroups. in_proj (hidden 2048) at 160 / 256 / 320 / 384 / 576 rows: 25.2 / 26.2 /
+  // 36.3 / 36.8 / 66.6 -> 22.0 / 23.1 / 30.1 / 33.2 / 47.5 us (at 448 rows, one block
+  // of padding, 64 x 64 measured 37.9 against 36.9 us).
+  if (!deep) {
+    const long t64 = tiles(64, 128);
+    if (t64 > 256 && t64 <= 448) return launch_pipe<64, 128, 3>(p, st);
+    if (tiles(256, 128) >= 128 && (p.M + 255) / 256 * 4 >= (p.M + 63) / 64 + 2) return launch_pipe<64, 64, 3>(p, st);
+  }
   // many rows (in_proj at 512+): 256 x 128 tiles of 8 waves on a 3-stage DMA ring (144 KB
   // of LDS, one workgroup of two waves per SIMD per CU): 61.0 / 118.4 -> 47.8 / 95.6 us at
   // 512 / 1024 rows
   if (tiles(256, 128) >= 128) return launch_pipe<256, 128, 3, 4, 2>(p, st);
   // 128 x 128 tiles of 4 waves on a 4-stage ring (128 KB) when they still give 192
-  // workgroups and their row blocks pad no more rows than 64-row blocks would: in_proj at
-  // 256 rows 28.9 -> 26.6 us (at 160 rows, half a block of padding, 25.2 -> 26.2)
+  // workgroups and their row blocks pad no more rows than 64-row blocks would (in_proj at
+  // 256 rows, before the 64-row rings above: 28.9 -> 26.6 us)
   if (tiles(128, 128) >= 192 && (p.M + 127) / 128 * 2 == (p.M + 63) / 64) return launch_pipe<128, 128, 4>(p, st);
   // otherwise the largest of the 64 x 64, 32 x 64 and 32 x 32 rings (4 waves, 4 stages of
   // 64 / 48 / 32 KB) that gives at least 384 workgroups, so that the CUs whose tiles come
@@ -619,15 +646,13 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
   // -> 17.1 / 19.1 / 19.6 us (hidden = 2048)
   if (tiles(64, 64) >= 384) return launch_pipe<64, 64, 4>(p, st);
   if (tiles(32, 64) >= 384) return launch_pipe<32, 64, 4>(p, st);
-  // A long contraction (the out_proj shape, K = H_v d_v = 4096) over few output columns
-  // (at most 4096) takes deeper stages: 128 or 256 k per stage halve or quarter the
-  // barriers and make each DMA instruction fetch 256 / 512 contiguous bytes of 4 / 2
-  // rows. A 256-deep ring of 4 stages needs 128 KB (one workgroup per CU), so it is used
+  // The long contraction over few output columns (deep): 128 or 256 k per stage halve or
+  // quarter the barriers and make each DMA instruction fetch 256 / 512 contiguous bytes
+  // of 4 / 2 rows. A 256-deep ring of 4 stages needs 128 KB (one workgroup per CU), so it is used
   // while the whole grid is resident at once. out_proj (hidden = 2048) at 48 / 64 / 96 /
   // 128 / 160 / 192 / 256 rows: 13.8 / 13.9 / 14.1 / 14.1 / 18.8 / 17.0 / 17.2 ->
   // 11.4 / 11.5 / 12.6 / 12.8 / 15.2 / 15.8 / 16.2 us (in_proj's 2048-long contraction
   // gained nothing from them).
-  const bool deep = p.K >= 4096 && p.K % 256 == 0 && rows <= 4096;
   if (deep && tiles(32, 32) >= 384) return launch_pipe<32, 32, 4, 2, 2, 128>(p, st);
   if (tiles(32, 32) >= 384) return launch_pipe<32, 32, 4>(p, st);
   if (deep && tiles(32, 16) <= 256) return launch_pipe<32, 16, 4, 2, 1, 256>(p, st);

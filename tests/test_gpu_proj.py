@@ -8,20 +8,24 @@ Tolerance: the kernels accumulate in fp32 and round once to the output dtype.
 * fp32 outputs: 1e-5 absolute + 1e-5 relative. The weights are scaled by
   1/sqrt(fan_in), so outputs are O(1) and the fp32 sum of K <= 4096 products has an
   error of order sqrt(K) 2^-24, a few 1e-7.
-Shapes cover every kernel: weight streaming (B <= 8, or B <= 2), the skinny MFMA
-kernel (3..32 rows, few output columns: out_proj at B = 3 and 20, in_proj at hidden
-512), the register-staged 32 x 32 tiles (out_proj of the small layers at B = 9 and 100,
-in_proj at B = 100), and the DMA-fed rings with 64-deep stages: 32 x 32 (in_proj at
-B = 3 and 20), 32 x 64 (in_proj at B = 33, 40 and 64, out_proj at B = 512 and 600, the
-33, 40 and 600 with a ragged last row tile), 64 x 64 (in_proj at B = 128 and 150,
-out_proj at B = 1024), 128 x 128 (in_proj at B = 200, ragged) and 256 x 128 (in_proj at
-B = 512, 600 and 1024); and with the deeper stages of out_proj's 4096-long contraction:
-32 x 16 by 256 (B = 33, 40, 64, and the narrow outputs of hidden 64..192), 32 x 32 by
-256 (B = 128), 32 x 16 by 128 (B = 150, ragged) and 32 x 32 by 128 (B = 200, ragged);
-ragged row and column tiles (the H_v-wide a/b segments are narrower than a tile) and
-the Qwen3.5-style sizes. The ring kernels store their tiles in 16-byte pieces; a segment whose width is
-not a multiple of 8 bf16 values (the a/b segments of the H_v = 20 layer at B = 1024) is
-stored element by element.
+Shapes cover every kernel: weight streaming (B <= 8, or B <= 2), the skinny MFMA kernel
+(3..32 rows, few output columns: out_proj at B = 3 and 20, in_proj at hidden 512), the
+register-staged 32 x 32 tiles (out_proj of the small layers at B = 9 and 100, in_proj at
+B = 100), and the DMA-fed rings with 64-deep stages: 32 x 32 (in_proj at B = 3 and 20),
+32 x 64 (in_proj at B = 33, 40 and 64, out_proj at B = 512 and 600, the 33, 40 and 600
+with a ragged last row tile), 64 x 64 by 4 stages (in_proj at B = 128, out_proj at B =
+1024), 64 x 128 by 3 stages (in_proj at B = 150 and 200, ragged), 64 x 64 by 3 stages
+(in_proj at B = 300 and 600, ragged), 128 x 128 (in_proj of an H_k = 20, H_v = 40 layer
+at B = 256) and 256 x 128 (in_proj at B = 512 and 1024); and with the deeper stages of
+out_proj's 4096-long contraction: 32 x 16 by 256 (B = 33, 40, 64, and the narrow outputs
+of hidden 64..192), 32 x 32 by 256 (B = 128), 32 x 16 by 128 (B = 150, ragged) and 32 x
+32 by 128 (B = 200, ragged); ragged row and column tiles (the H_v-wide a/b segments are
+narrower than a tile) and the Qwen3.5-style sizes. The rings take their stages in a
+staggered order per workgroup while the activations are at most 2 MB (most cases here)
+and in the common order above that (in_proj at B = 600 and 1024, out_proj at B = 300,
+512, 600, 1024). The ring kernels store their tiles in 16-byte pieces; a segment whose
+width is not a multiple of 8 bf16 values (the a/b segments of the H_v = 20 layer at B =
+1024) is stored element by element.
 """
 
 import numpy as np
@@ -78,6 +82,8 @@ CASES = [
     (128, 16, 32, 128, 2048, [0, 1, 15, 63, 64, 100, 127]),
     (150, 16, 32, 128, 2048, [0, 31, 32, 127, 128, 149]),
     (200, 16, 32, 128, 2048, [0, 1, 127, 128, 150, 199]),
+    (300, 16, 32, 128, 2048, [0, 63, 64, 255, 256, 299]),
+    (256, 20, 40, 128, 2048, [0, 1, 127, 128, 255]),
     (600, 16, 32, 128, 2048, [0, 63, 64, 511, 512, 575, 576, 599]),
     (512, 16, 32, 128, 2048, [0, 1, 63, 64, 255, 300, 511]),
     (1024, 4, 20, 128, 2048, [0, 1, 255, 256, 511, 767, 1000, 1023]),
