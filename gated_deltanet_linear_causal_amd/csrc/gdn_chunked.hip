@@ -20,11 +20,14 @@
 // K K^T, Q K^T, the two 16 x 16 block inverses, A21 and P. Waves w and w + 4 share a
 // SIMD, so each SIMD runs one matrix-heavy and one vector-heavy wave. Two barriers per
 // chunk:
-//   phase 1  consumers: K H0, Q H0, R, Delta, O = gamma Q H0 + P Delta, row sums of O^2
+//   phase 1  consumers: K H0, Q H0, R, Delta, O = gamma Q H0 + P Delta, row sums of O^2,
+//                       then H = gamma_C H + K^T diag(exp(g_C - g)) Delta
 //            producers: conv / norms / gates of chunk c+1 into the other operand buffer,
 //                       z rows of chunk c; then the loads of chunk c+2
-//   phase 2  consumers: H = gamma_C H + K^T diag(exp(g_C - g)) Delta, outputs of chunk c
-//            producers: K K^T, Q K^T of chunk c+1 -> T11, T22, A21, P
+//   phase 2  consumers: outputs of chunk c; Q K^T (1, 0), (1, 1) of chunk c+1 -> P
+//                       (waves 0, 1); conv + SiLU of chunk c+1's v rows (waves 2, 3)
+//            producers: K K^T (0, 0) -> T11, (1, 1) -> T22, (1, 0) -> A21, and
+//                       Q K^T (0, 0) -> P of chunk c+1, one tile per wave
 // The per-chunk buffers written in phase 1 (q, k planes, v, gates) are double-buffered;
 // those written in phase 2 (T, A21, P) are read by the consumers only in phase 1.
 // The A operand of the state update (K^T) is read from the [t][i] plane of k with the
