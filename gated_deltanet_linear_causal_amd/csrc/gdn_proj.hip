@@ -646,17 +646,21 @@ hipError_t launch_proj(ProjArgs p, hipStream_t st) {
   // -> 17.1 / 19.1 / 19.6 us (hidden = 2048)
   if (tiles(64, 64) >= 384) return launch_pipe<64, 64, 4>(p, st);
   if (tiles(32, 64) >= 384) return launch_pipe<32, 64, 4>(p, st);
-  // The long contraction over few output columns (deep): 128 or 256 k per stage halve or
-  // quarter the barriers and make each DMA instruction fetch 256 / 512 contiguous bytes
-  // of 4 / 2 rows. A 256-deep ring of 4 stages needs 128 KB (one workgroup per CU), so it is used
-  // while the whole grid is resident at once. out_proj (hidden = 2048) at 48 / 64 / 96 /
-  // 128 / 160 / 192 / 256 rows: 13.8 / 13.9 / 14.1 / 14.1 / 18.8 / 17.0 / 17.2 ->
-  // 11.4 / 11.5 / 12.6 / 12.8 / 15.2 / 15.8 / 16.2 us (in_proj's 2048-long contraction
-  // gained nothing from them).
+  // The long contraction over few output columns (deep): 128-deep stages halve the
+  // barriers and make each DMA instruction fetch 256 contiguous bytes of 4 rows. out_proj
+  // (hidden = 2048) at 160 / 192 / 256 rows: 18.8 / 17.0 / 17.2 -> 15.2 / 15.8 / 16.2 us
+  // against 64-deep stages (in_proj's 2048-long contraction gained nothing from them).
   if (deep && tiles(32, 32) >= 384) return launch_pipe<32, 32, 4, 2, 2, 128>(p, st);
   if (tiles(32, 32) >= 384) return launch_pipe<32, 32, 4>(p, st);
-  if (deep && tiles(32, 16) <= 256) return launch_pipe<32, 16, 4, 2, 1, 256>(p, st);
-  if (deep && tiles(32, 32) <= 256) return launch_pipe<32, 32, 4, 2, 2, 256>(p, st);
+  // Up to 128 rows, 16 x 16 tiles of one wave on a ring of four 128-deep stages (32 KB,
+  // up to five workgroups per CU): out_proj (hidden 2048) at 33 / 48 / 64 / 96 / 128 rows
+  // 11.4 / 11.4 / 11.4 / 11.7 / 12.1 -> 10.1 / 10.1 / 10.1 / 11.0 / 11.7 us. Up to 64 rows
+  // the stages keep the common order (staggered: 10.7 us at 33..64 rows, where each
+  // column tile's four row blocks then stop sharing its weight rows in L2).
+  if (deep && p.M <= 128) {
+    if (p.M <= 64) p.krot = 0;
+    return launch_pipe<16, 16, 4, 1, 1, 128>(p, st);
+  }
   if (deep) return launch_pipe<32, 16, 4, 2, 1, 128>(p, st);
   // 64 x 64 ring with a full grid
   if (tiles(64, 64) >= 256) return launch_pipe<64, 64, 4>(p, st);

@@ -16,16 +16,16 @@ B = 100), and the DMA-fed rings with 64-deep stages: 32 x 32 (in_proj at B = 3 a
 with a ragged last row tile), 64 x 64 by 4 stages (in_proj at B = 128, out_proj at B =
 1024), 64 x 128 by 3 stages (in_proj at B = 150 and 200, ragged), 64 x 64 by 3 stages
 (in_proj at B = 300 and 600, ragged), 128 x 128 (in_proj of an H_k = 20, H_v = 40 layer
-at B = 256) and 256 x 128 (in_proj at B = 512 and 1024); and with the deeper stages of
-out_proj's 4096-long contraction: 32 x 16 by 256 (B = 33, 40, 64, and the narrow outputs
-of hidden 64..192), 32 x 32 by 256 (B = 128), 32 x 16 by 128 (B = 150, ragged) and 32 x
-32 by 128 (B = 200, ragged); ragged row and column tiles (the H_v-wide a/b segments are
-narrower than a tile) and the Qwen3.5-style sizes. The rings take their stages in a
-staggered order per workgroup while the activations are at most 2 MB (most cases here)
-and in the common order above that (in_proj at B = 600 and 1024, out_proj at B = 300,
-512, 600, 1024). The ring kernels store their tiles in 16-byte pieces; a segment whose
-width is not a multiple of 8 bf16 values (the a/b segments of the H_v = 20 layer at B =
-1024) is stored element by element.
+at B = 256) and 256 x 128 (in_proj at B = 512 and 1024); and with the 128-deep stages of
+out_proj's 4096-long contraction: 16 x 16 tiles of one wave (B = 33, 40, 64 and 128), 32
+x 16 (B = 150, ragged, and the narrow outputs of hidden 64..192) and 32 x 32 (B = 200
+and 300, ragged); ragged row and column tiles (the H_v-wide a/b segments are narrower
+than a tile) and the Qwen3.5-style sizes. The rings take their stages in a staggered
+order per workgroup while the activations are at most 2 MB (most cases here) and in the
+common order above that (in_proj at B = 600 and 1024, out_proj at B = 300, 512, 600,
+1024). The ring kernels store their tiles in 16-byte pieces; a segment whose width is
+not a multiple of 8 bf16 values (the a/b segments of the H_v = 20 layer at B = 1024) is
+stored element by element.
 """
 
 import numpy as np
@@ -163,11 +163,12 @@ def test_projection_then_decode_layer():
     compare("in_proj -> decode_layer", host_f64(out), ref, "bf16", TOL["bf16"])
 
 
-@pytest.mark.parametrize("B", [64, 150, 300, 400])
+@pytest.mark.parametrize("B", [64, 100, 150, 300, 400])
 def test_out_proj_deep_stages_ragged_columns(B):
     """out_proj's 4096-long contraction onto 1000 output columns, whose last column tile
-    is ragged, through each deep-stage ring: 32 x 16 by 256 (B = 64), 32 x 32 by 256
-    (150), 32 x 16 by 128 (300) and 32 x 32 by 128 (400)."""
+    is ragged, through each 128-deep ring: 16 x 16 (B = 64 in the common stage order,
+    100 in the staggered one, ragged rows), 32 x 16 (150 staggered, 300 common) and
+    32 x 32 (400)."""
     hidden = 1000
     cfg = cfg_of(B)
     zd = cfg.z_dim
