@@ -22,14 +22,18 @@
 // chunk:
 //   phase 1  consumers: K H0, Q H0, R, Delta, O = gamma Q H0 + P Delta, row sums of O^2,
 //                       then H = gamma_C H + K^T diag(exp(g_C - g)) Delta
-//            producers: conv / norms / gates of chunk c+1 into the other operand buffer,
-//                       z rows of chunk c; then the loads of chunk c+2
+//            producers: conv / norms of chunk c+1 into the other operand buffer, z rows
+//                       of chunk c; then the loads of chunk c+2
 //   phase 2  consumers: outputs of chunk c; Q K^T (1, 0), (1, 1) of chunk c+1 -> P
 //                       (waves 0, 1); conv + SiLU of chunk c+1's v rows (waves 2, 3)
 //            producers: K K^T (0, 0) -> T11, (1, 1) -> T22, (1, 0) -> A21, and
-//                       Q K^T (0, 0) -> P of chunk c+1, one tile per wave
-// The per-chunk buffers written in phase 1 (q, k planes, v, gates) are double-buffered;
-// those written in phase 2 (T, A21, P) are read by the consumers only in phase 1.
+//                       Q K^T (0, 0) -> P of chunk c+1, one tile per wave; the last of
+//                       them then the gates of chunk c+2 (bf16 inputs; with fp32 inputs
+//                       the gates of chunk c+1 come in phase 1)
+// The per-chunk buffers written in phase 1 (q, k planes, v) and the gates are
+// double-buffered; those written in phase 2 (T, A21, P) are read by the consumers only
+// in phase 1. The gates of chunk c+2 go into the buffer of chunk c, whose gates the
+// consumers last read in phase 1.
 // The A operand of the state update (K^T) is read from the [t][i] plane of k with the
 // LDS transpose load (ds_read_b64_tr_b16): in each group of 16 lanes, lane i receives
 // element i % 4 of the 8-byte slots addressed by lanes 4k + i / 4, k = 0..3.
@@ -68,7 +72,8 @@ constexpr int kD = 128;       // head dim (d_k = d_v)
 constexpr int kC = 32;        // tokens per chunk
 constexpr int kNT = 512;      // 8 waves: 4 consumers, 4 producers
 constexpr int kTaps = 4;      // conv taps (K)
-constexpr int kGateWave = 1;  // the producer wave that loads the gate inputs and scans the gates
+constexpr int kGateWave = 3;  // the producer wave that loads the gate inputs and scans the gates
+                              // (bf16: in phase 2, after the lightest of the four tiles)
 constexpr int kRows = 8 + kTaps - 1;  // conv input rows of a producer wave (8 tokens + history)
 constexpr int kQKLd = kD + 4;  // halves per row of the [t][i] planes (66 dwords: the 16 rows of a
                                // fragment read start in 16 different even banks)
@@ -933,7 +938,10 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
           if (c >= 0) stage_z(sm, a, b, h, c, p, l);
           stage_inputs(sm, a, b, g, h, n, p, l, 2);
           if (p == kGateWave && n + 1 < nchunks) load_gate_inputs<BF>(a, b, h, n + 1, l, gdt, gbr);
-          if (p == kGateWave) chunk_gates(T - n * kC, l, dt, br, A_exp, dt_bias, sm.op[n & 1]);
+          // the gates of chunk n come from phase 2 of the pass before (chunk 0: here)
+          if constexpr (kFirst) {
+            if (p == kGateWave) chunk_gates(T - n * kC, l, dt, br, A_exp, dt_bias, sm.op[n & 1]);
+          }
           produce_conv<BF, 2>(
               sm, a, n, p, l,
               [&](int sg, float(&x0)[kRows], float(&x1)[kRows]) {
@@ -1035,6 +1043,12 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(const KernelArgs a) {
       }
     } else if (n < nchunks) {
       produce_factors<BF>(sm, n, p, l, one);
+      // gates of chunk n + 1 (inputs loaded in phase 1) into the buffer of chunk c
+      if constexpr (BF) {
+        if (p == kGateWave && n + 1 < nchunks)
+          chunk_gates(T - (n + 1) * kC, l, gate_input<BF>(gdt), gate_input<BF>(gbr), A_exp, dt_bias,
+                      sm.op[(n + 1) & 1]);
+      }
     }
     lds_barrier();
   };
