@@ -382,7 +382,8 @@ hipError_t launch_skinny_m(ProjArgs& p, long ntiles, int cus, hipStream_t st) {
 // Per stage: wait until this wave's DMA of the stage has landed (the memory counter,
 // S - 2 later stages may still be in flight), an LDS-only barrier, then the DMA of
 // stage + S - 1 into the slot every wave finished reading before the barrier, then the
-// products. No LDS store is issued in the loop, so nothing there waits for the DMA.
+// products (with the 256-row tiles, the DMA instructions go out between the products).
+// No LDS store is issued in the loop, so nothing there waits for the DMA.
 // Rows past M or the segment end are clamped to valid rows; they feed only outputs
 // that are not stored.
 // ----------------------------------------------------------------------------------
@@ -394,7 +395,7 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 __device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
-template <int BM, int BN, int S, int WM, int WN, int KB, bool ROT>
+template <int BM, int BN, int S, int WM, int WN, int KB, bool ROT, bool IL>
 __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) {
   constexpr int NW = WM * WN;           // waves
   constexpr int R = BM + BN;            // rows per stage
@@ -461,11 +462,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
     else
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();
-    if (kt + S - 1 < nk) {
-      const int j = kt + S - 1;
+    // the DMA of stage kt + S - 1 into the slot every wave finished reading before the
+    // barrier: issued at once, or (IL) one instruction after every GAP products of this
+    // stage, so that a wave does not stall on the memory pipe with its products unissued
+    const bool more = kt + S - 1 < nk;
+    const int jn = kt + S - 1;
+    const long joff = static_cast<long>(KB) * (jn + rot < nk ? jn + rot : jn + rot - nk);
+    uint16_t* const jdst = ring0 + (jn % S) * (R * KB);
+    constexpr int NM = (KB / 32) * TI * TJ, GAP = NM / NI > 0 ? NM / NI : 1;
+    if (!IL && more) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        dma16(src[i] + static_cast<long>(KB) * (j + rot < nk ? j + rot : j + rot - nk), ring0 + (j % S) * (R * KB) + 512 * i);
+      for (int i = 0; i < NI; ++i) dma16(src[i] + joff, jdst + 512 * i);
     }
     const uint16_t* st = &ring[kt % S][0][0];
 #pragma unroll
@@ -484,7 +491,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gdn_proj_pipe(const ProjArgs p) 
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TJ; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+          const int idx = (kk * TI + i) * TJ + j;
+          if (IL && idx % GAP == 0 && idx / GAP < NI && more) dma16(src[idx / GAP] + joff, jdst + 512 * (idx / GAP));
+        }
+    }
+    if (IL && more) {  // instructions left over when there are more of them than products
+#pragma unroll
+      for (int i = NM; i < NI; ++i) dma16(src[i] + joff, jdst + 512 * i);
     }
   }
   // The tile leaves through LDS: the ring is free once every wave is past its last
@@ -541,10 +556,15 @@ hipError_t launch_pipe(ProjArgs& p, hipStream_t st) {
   p.mblocks = static_cast<int>((p.M + BM - 1) / BM);
   // one workgroup per (column tile, row block), column tiles rounded up to a multiple of 8
   const dim3 grid(static_cast<unsigned>(((tiles + 7) / 8) * 8 * p.mblocks));
+  // the 256-row tiles spread their DMA over the products (in_proj, hidden = 2048, at 512 /
+  // 1024 rows: 41.0 / 80.8 -> 38.3 / 73.7 us); the smaller tiles, whose waves each issue
+  // few products per stage, issue it at once (spread: in_proj at 64 / 256 rows 13.3 /
+  // 25.1 -> 14.5 / 28.8 us)
+  constexpr bool IL = BM >= 256;
   if (p.krot)
-    gdn_proj_pipe<BM, BN, S, WM, WN, KB, true><<<grid, 64 * WM * WN, 0, st>>>(p);
+    gdn_proj_pipe<BM, BN, S, WM, WN, KB, true, IL><<<grid, 64 * WM * WN, 0, st>>>(p);
   else
-    gdn_proj_pipe<BM, BN, S, WM, WN, KB, false><<<grid, 64 * WM * WN, 0, st>>>(p);
+    gdn_proj_pipe<BM, BN, S, WM, WN, KB, false, IL><<<grid, 64 * WM * WN, 0, st>>>(p);
   return hipGetLastError();
 }
 
