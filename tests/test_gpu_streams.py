@@ -1,0 +1,110 @@
+"""Independent calls on two streams at once.
+
+The library keeps no state between calls and uses no memory of its own (include/gdn.h,
+"Pointers"), so calls on different streams that touch different buffers may run
+concurrently. Here two streams interleave a chunked gdn_sequence, a verify and commit of
+draft tokens, decode steps and both projections (the 256 x 128 and 32 x 64 rings at
+B = 512), each stream's calls in order; every result equals, bit for bit, the same calls
+run one after another on one stream (every kernel on these paths is deterministic), and
+the chunked sequence and decode outputs also meet the oracle's tolerance.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_causal_amd import gdn
+from gated_deltanet_linear_causal_amd import inputs as I
+
+import gdn_cases as GC
+
+pytestmark = pytest.mark.gpu
+
+
+def _work():
+    """Two lists of call closures (one per stream) over independent buffers, the
+    buffers they write, and a reset of the states they update."""
+    # stream 1: chunked sequence (B = 3, T = 70), then verify of 4 draft tokens and a
+    # commit of 4 / 1 / 0 of them on other states
+    sc = I.config(1).with_(batch=3, steps=70, mode="sequence", seed=4101)
+    dsq = I.generate(sc)
+    d1 = GC.DeviceInputs(sc, dsq)
+    s1 = GC.shape_for(sc)
+    out1 = torch.full((sc.batch, sc.steps, sc.z_dim), float("nan"), dtype=torch.float32, device="cuda")
+    vc = I.config(1).with_(batch=3, steps=4, mode="sequence", seed=4102)
+    dv = GC.DeviceInputs(vc, I.generate(vc))
+    sv = GC.shape_for(vc)
+    vout = torch.full((vc.batch, vc.steps, vc.z_dim), float("nan"), dtype=torch.float32, device="cuda")
+    trail = torch.zeros(gdn.gdn_verify_trail_bytes(sv, vc.steps), dtype=torch.uint8, device="cuda")
+    acc = torch.tensor([4, 1, 0], dtype=torch.int32, device="cuda")
+    # stream 2: 4 decode steps (B = 5), then in_proj and out_proj at B = 512
+    dc = I.config(1).with_(batch=5, seed=4103)
+    ddec = I.generate(dc, steps=4)
+    d2 = GC.DeviceInputs(dc, ddec)
+    s2 = GC.shape_for(dc)
+    out2 = torch.full((4, dc.batch, dc.z_dim), float("nan"), dtype=torch.float32, device="cuda")
+    pc = I.config(3)
+    P = I.generate_projections(pc)
+    sp = GC.shape_for(pc)
+    w = {k: GC.dev(P[k], "bf16") for k in ("x_norm", "w_qkv", "w_z", "w_a", "w_b", "w_out")}
+    g = GC.dev(I.f32_to_bf16_bits(np.random.default_rng(6).standard_normal((pc.batch, pc.z_dim), dtype=np.float32)),
+               "bf16")
+    po = [torch.empty((pc.batch, n), dtype=torch.bfloat16, device="cuda")
+          for n in (pc.channels, pc.z_dim, pc.num_v_heads, pc.num_v_heads)]
+    y = torch.empty((pc.batch, I.HIDDEN), dtype=torch.float32, device="cuda")  # out_dtype f32
+
+    first = [(t, t.clone()) for t in (d1.state, d1.conv_state, dv.state, dv.conv_state, d2.state, d2.conv_state)]
+
+    def reset():
+        for t, t0 in first:
+            t.copy_(t0)
+        for t in (out1, vout, out2, y, *po):
+            t.fill_(float("nan"))
+        trail.zero_()
+
+    a_calls = [
+        lambda st: gdn.gdn_sequence(s1, sc.steps, d1.conv_state, d1.state, d1.qkv, d1.conv_w, d1.a, d1.b, d1.z,
+                                    d1.A_log, d1.dt_bias, d1.norm_w, out1, stream=st),
+        lambda st: gdn.gdn_decode_verify(sv, vc.steps, dv.conv_state, dv.state, dv.qkv, dv.conv_w, dv.a, dv.b, dv.z,
+                                         dv.A_log, dv.dt_bias, dv.norm_w, vout, trail, stream=st),
+        lambda st: gdn.gdn_decode_commit(sv, vc.steps, acc, dv.conv_state, dv.state, dv.qkv, trail, stream=st),
+    ]
+    b_calls = [
+        (lambda st, t=t: gdn.gdn_decode_layer(s2, d2.conv_state, d2.state, d2.qkv[t], d2.conv_w, d2.a[t], d2.b[t],
+                                              d2.z[t], d2.A_log, d2.dt_bias, d2.norm_w, out2[t], stream=st))
+        for t in range(4)
+    ] + [
+        lambda st: gdn.gdn_in_proj(sp, I.HIDDEN, w["x_norm"], w["w_qkv"], w["w_z"], w["w_a"], w["w_b"], *po, stream=st),
+        lambda st: gdn.gdn_out_proj(sp, I.HIDDEN, g, w["w_out"], y, stream=st),
+    ]
+    written = [out1, vout, trail, out2, y, *po] + [t for t, _ in first]
+    checks = (sc, dsq, out1, dc, ddec, out2)
+    return a_calls, b_calls, written, reset, checks
+
+
+def test_two_streams_match_one_stream():
+    a_calls, b_calls, written, reset, checks = _work()
+    cur = torch.cuda.current_stream()
+    for c in a_calls + b_calls:
+        c(cur)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in written]
+    sc, dsq, out1, dc, ddec, out2 = checks
+    r_seq, _, _ = GC.oracle_sequence(sc, dsq)
+    GC.compare("one stream: chunked sequence out", GC.host_f64(out1), r_seq, "bf16")
+    r_dec, _, _ = GC.oracle_decode(dc, ddec, 4)
+    GC.compare("one stream: decode out", GC.host_f64(out2), r_dec, "bf16")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    for rep in range(3):
+        reset()
+        sa.wait_stream(cur)
+        sb.wait_stream(cur)
+        # interleave the two streams' launches from the host; each stream keeps its order
+        for i in range(max(len(a_calls), len(b_calls))):
+            if i < len(b_calls):
+                b_calls[i](sb)
+            if i < len(a_calls):
+                a_calls[i](sa)
+        torch.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(written, ref)):
+            assert torch.equal(t, r), "two streams, pass %d: buffer %d differs from the one-stream run" % (rep, i)
