@@ -4,6 +4,7 @@
 
 #include "gdn.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -156,7 +157,7 @@ struct TrailLayout {
 
 extern "C" {
 
-int32_t gdn_abi_version(void) { return (1 << 16) | 3; }
+int32_t gdn_abi_version(void) { return (1 << 16) | 4; }
 
 const char* gdn_status_string(int32_t st) {
   switch (st) {
@@ -380,8 +381,18 @@ gdn_status_t gdn_decode_layer_pooled(const gdn_shape_t* shape, int32_t pool_size
                                    static_cast<hipStream_t>(stream)));
 }
 
+// A T-token call moves B x T rows of qkv, z and out; every buffer size computed from
+// the shape stays below 2^62 bytes (so none of them wraps in 64 bits) when B x T times
+// the largest of those rows does. Evaluated in 128 bits: B, T < 2^31, a row < 2^34 bytes.
+bool sequence_fits(const gdn_shape_t* s, int32_t T) {
+  const Sizes z(s);
+  const size_t row = std::max(z.C * z.ea, z.Hv * z.d * std::max(z.ea, z.eo));
+  const unsigned __int128 bytes = static_cast<unsigned __int128>(z.B) * static_cast<uint64_t>(T) * row;
+  return bytes <= (static_cast<unsigned __int128>(1) << 62);
+}
+
 size_t gdn_sequence_workspace_bytes(const gdn_shape_t* shape, int32_t T) {
-  if (check_shape(shape) != GDN_OK || T < 0) return SIZE_MAX;
+  if (check_shape(shape) != GDN_OK || T < 0 || !sequence_fits(shape, T)) return SIZE_MAX;
   return 0;
 }
 
@@ -392,7 +403,7 @@ gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_stat
                           void* workspace, size_t workspace_bytes, void* stream) {
   gdn_status_t st = check_shape(shape);
   if (st != GDN_OK) return st;
-  if (T < 0) return GDN_ERR_SHAPE;
+  if (T < 0 || !sequence_fits(shape, T)) return GDN_ERR_SHAPE;
   const Sizes z(shape);
   if (z.B == 0 || T == 0) return GDN_OK;
   const size_t need = gdn_sequence_workspace_bytes(shape, T);

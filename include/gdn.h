@@ -37,7 +37,8 @@
  *   error the call returns a negative gdn_status_t and writes nothing.
  *   - NULL buffer pointers -> GDN_ERR_NULL (allowed only when batch, or T, is 0)
  *   - batch < 0, heads < 1, H_v % H_k != 0, K outside [2, 8], eps < 0 or not finite,
- *     T < 0, grid too large -> GDN_ERR_SHAPE
+ *     T < 0, grid too large, or (gdn_sequence, since ABI 1.4) B x T times the largest
+ *     token row of qkv, z or out above 2^62 bytes -> GDN_ERR_SHAPE
  *   - act_dtype / out_dtype not a gdn_dtype_t -> GDN_ERR_DTYPE
  *   - qkv, conv1d_state, state, conv1d_weight, z, qkv_act, y, out not 16-byte aligned,
  *     or another buffer not aligned to its element size -> GDN_ERR_ALIGN
@@ -184,7 +185,7 @@ gdn_status_t gdn_sequence(const gdn_shape_t* shape, int32_t T, void* conv1d_stat
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes gdn_sequence needs for this shape and T (0 if none; SIZE_MAX if the
- * shape is invalid). Host-only, no HIP call. */
+ * shape or T is invalid, the 2^62-byte bound included). Host-only, no HIP call. */
 size_t gdn_sequence_workspace_bytes(const gdn_shape_t* shape, int32_t T);
 
 /* Speculative decoding: verify T draft tokens, then commit the accepted prefix.

@@ -7,6 +7,8 @@ import os
 import re
 
 import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 from gated_deltanet_linear_causal_amd import gdn
 
@@ -173,6 +175,45 @@ def test_sequence_validation():
     assert gdn.gdn_sequence_workspace_bytes(s, -1) == ctypes.c_size_t(-1).value
     f = Fake()
     assert call_sequence(s, 3, out=ctypes.c_void_p(f().value + 8)) == ALIGN
+
+
+def _row_bytes(s):
+    C = 2 * s.num_k_heads * s.head_k_dim + s.num_v_heads * s.head_v_dim
+    ea = 2 if s.act_dtype == 1 else 4
+    eo = 2 if s.out_dtype == 1 else 4
+    return max(C * ea, s.num_v_heads * s.head_v_dim * max(ea, eo))
+
+
+def test_sequence_rejects_buffers_past_2_62_bytes():
+    """B x T times a token's largest row (qkv, z or out) above 2^62 bytes is a shape
+    error (no buffer size may wrap in 64 bits); at exactly 2^62 the shape passes and the
+    call goes on to the buffer checks (here: the fake buffers overlap)."""
+    SIZE_MAX = ctypes.c_size_t(-1).value
+    big = qwen(batch=1 << 18)                     # row = 16 KiB (fp32 out)
+    assert _row_bytes(big) == 1 << 14
+    T = (1 << 30) + 1                             # 2^18 x T x 2^14 > 2^62
+    assert gdn.gdn_sequence_workspace_bytes(big, T) == SIZE_MAX
+    assert call_sequence(big, T) == SHAPE
+    edge = qwen(batch=1 << 17)
+    T = (1 << 31) - 1                             # 2^17 x T x 2^14 < 2^62
+    assert gdn.gdn_sequence_workspace_bytes(edge, T) == 0
+    assert call_sequence(edge, T) == ALIAS
+    huge = qwen(batch=(1 << 27) - 1, num_k_heads=16)  # B x H_k just below 2^31
+    assert gdn.gdn_sequence_workspace_bytes(huge, (1 << 31) - 1) == SIZE_MAX
+    assert call_sequence(huge, (1 << 31) - 1) == SHAPE
+
+
+@settings(max_examples=300, deadline=None)
+@given(batch=st.integers(0, (1 << 31) - 1), hk=st.integers(1, 64), g=st.sampled_from([1, 2, 4]),
+       d=st.sampled_from([32, 64, 128]), T=st.integers(0, (1 << 31) - 1), act=st.sampled_from([0, 1]),
+       out=st.sampled_from([0, 1]))
+def test_sequence_size_rule_matches_the_definition(batch, hk, g, d, T, act, out):
+    """The workspace query (host-only, never launches) accepts exactly the shapes whose
+    grid fits and whose B x T x largest token row is at most 2^62 bytes."""
+    s = gdn.make_shape(batch, hk, hk * g, d, d, 4, 1e-6, 1e-6, act, out)
+    grid_ok = batch * hk <= (1 << 31) - 1
+    ok = grid_ok and batch * T * _row_bytes(s) <= 1 << 62
+    assert (gdn.gdn_sequence_workspace_bytes(s, T) == 0) == ok
 
 
 def test_header_mentions_every_status():
