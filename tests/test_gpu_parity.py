@@ -124,6 +124,13 @@ def test_qwen35_B512_32_steps_sampled():
     np.testing.assert_array_equal(GC.host_bits(d.conv_state), np.swapaxes(data["qkv"][29:32], 0, 1))
 
 
+def test_qwen35_B512_one_step_every_sequence():
+    """One decode step of the B = 512 workload (the benchmark's launch: 8192 workgroups
+    over the 1 GiB state) with every sequence recomputed by the oracle: all outputs and
+    the whole final state within tolerance, every conv state bit for bit."""
+    _check_decode(I.config(3), 1)
+
+
 def test_qwen35_sequence_B8_T4096():
     cfg = I.config(4)
     data = I.generate(cfg)
