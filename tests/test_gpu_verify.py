@@ -51,6 +51,8 @@ CASES = [
     ("G3_d128_K2_T5_f32", 2, 1, 3, 128, 2, "f32", 5, [2, 5]),
     ("G2_d32_K6_T3", 5, 2, 4, 32, 6, "bf16", 3, [1, 3, 0, 2, 3]),
     ("T1_B2", 2, 16, 32, 128, 4, "bf16", 1, [1, 0]),
+    # the benchmark's verify workload: B = 64, 4 draft tokens, every count 0..4
+    ("qwen35_B64_T4", 64, 16, 32, 128, 4, "bf16", 4, [i % 5 for i in range(64)]),
 ]
 
 
